@@ -1,0 +1,145 @@
+"""Float64 CPU oracle of the gated delta-net recurrence (forward and backward).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py``; never by the product package. It shares no code
+with the HIP path. The arithmetic lives in ``gdn_oracle.c`` (plain C, float64, no
+contraction, one thread per (sequence, key head) group); this module builds it with
+gcc and marshals numpy arrays through ctypes.
+
+Pins (tests/test_oracle.py) tie it to things other than itself: central finite
+differences of its own forward, a second formulation of the recurrence
+(S_t = g_t (I - beta_t k k^T) S_{t-1} + beta_t k v^T) differentiated by torch
+autograd, closed forms (beta = 0, T = 1, g = beta = 1 with orthonormal keys),
+the v_repeat / replication identity, linearity, zero upstream gradient and split
+resume. No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "gdn_oracle.c")
+LIB = os.path.join(_HERE, "libgdn_oracle.so")
+
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC", "-pthread"]
+
+
+def build(out: str = LIB, plant: Optional[int] = None) -> str:
+    """Compile the oracle with gcc. ``plant`` builds a deliberately broken
+    variant (used only by the falsification test)."""
+    cmd = ["gcc", *_CFLAGS, SRC, "-o", out]
+    if plant is not None:
+        cmd.insert(1, f"-DORACLE_PLANT={int(plant)}")
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_libs = {}
+
+
+def _load(path: str = LIB):
+    if path not in _libs:
+        if path == LIB and not os.path.exists(LIB):
+            build()
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.oracle_gdn_fwd.argtypes = [I, P, I, I, I, I, ctypes.c_double] + [P] * 8 + [I]
+        lib.oracle_gdn_fwd.restype = I
+        lib.oracle_gdn_bwd.argtypes = [I, P, I, I, I, I, ctypes.c_double] + [P] * 14 + [I]
+        lib.oracle_gdn_bwd.restype = I
+        _libs[path] = lib
+    return _libs[path]
+
+
+def _c(a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def gdn_fwd(cu, q, k, v, g, beta, S0=None, scale=None, nthreads=None, lib=None):
+    """Forward. q, k [T, Hk, Dk]; v [T, Hv, Dv]; g, beta [T, Hv]; S0 [N, Hv, Dk, Dv] or None.
+    Returns (o [T, Hv, Dv], S_T [N, Hv, Dk, Dv])."""
+    cu = np.ascontiguousarray(cu, dtype=np.int64)
+    q, k, v, g, beta, S0 = map(_c, (q, k, v, g, beta, S0))
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N = len(cu) - 1
+    assert cu[-1] == T and k.shape == q.shape and v.shape[0] == T and g.shape == (T, Hv)
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dk)
+    o = np.zeros((T, Hv, Dv))
+    ST = np.zeros((N, Hv, Dk, Dv))
+    L = _load(lib or LIB)
+    rc = L.oracle_gdn_fwd(N, _p(cu), Hk, Hv, Dk, Dv, float(scale), _p(q), _p(k), _p(v), _p(g),
+                          _p(beta), _p(S0), _p(o), _p(ST), int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdn_fwd failed ({rc})")
+    return o, ST
+
+
+def gdn_bwd(cu, q, k, v, g, beta, S0, dO, dST, scale=None, nthreads=None, lib=None):
+    """Backward. Returns dict dq, dk [T, Hk, Dk], dv [T, Hv, Dv], dg, dbeta [T, Hv],
+    dS0 [N, Hv, Dk, Dv]."""
+    cu = np.ascontiguousarray(cu, dtype=np.int64)
+    q, k, v, g, beta, S0, dO, dST = map(_c, (q, k, v, g, beta, S0, dO, dST))
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N = len(cu) - 1
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dk)
+    out = dict(
+        dq=np.zeros((T, Hk, Dk)), dk=np.zeros((T, Hk, Dk)), dv=np.zeros((T, Hv, Dv)),
+        dg=np.zeros((T, Hv)), dbeta=np.zeros((T, Hv)), dS0=np.zeros((N, Hv, Dk, Dv)),
+    )
+    L = _load(lib or LIB)
+    rc = L.oracle_gdn_bwd(N, _p(cu), Hk, Hv, Dk, Dv, float(scale), _p(q), _p(k), _p(v), _p(g),
+                          _p(beta), _p(S0), _p(dO), _p(dST), _p(out["dq"]), _p(out["dk"]),
+                          _p(out["dv"]), _p(out["dg"]), _p(out["dbeta"]), _p(out["dS0"]),
+                          int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdn_bwd failed ({rc})")
+    return out
+
+
+def run_case(case, backward=True, nthreads=None, lib=None, seqs=None, key_heads=None):
+    """Run the oracle on a ``synth.GdnCase``. ``seqs`` / ``key_heads`` restrict it to a
+    subset of sequences and key-head groups (each group is independent of the others,
+    so the restriction is exact). Returns dict with o, S_T and, if backward, the
+    gradients, indexed like the restricted problem, plus the index maps used."""
+    r = case.Hv // case.Hk
+    seqs = list(range(case.N)) if seqs is None else list(seqs)
+    key_heads = list(range(case.Hk)) if key_heads is None else list(key_heads)
+    vheads = [kh * r + j for kh in key_heads for j in range(r)]
+    cu_full = case.cu_seqlens
+    rows = np.concatenate([np.arange(cu_full[n], cu_full[n + 1]) for n in seqs]) if seqs else np.zeros(0, np.int64)
+    lens = [int(cu_full[n + 1] - cu_full[n]) for n in seqs]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    sel = lambda a, heads: a[rows][:, heads]
+    q, k = sel(case.q, key_heads), sel(case.k, key_heads)
+    v, g, beta, dO = sel(case.v, vheads), sel(case.g, vheads), sel(case.beta, vheads), sel(case.dO, vheads)
+    S0 = None if case.S0 is None else case.S0[seqs][:, vheads]
+    dST = None if case.dST is None else case.dST[seqs][:, vheads]
+    o, ST = gdn_fwd(cu, q, k, v, g, beta, S0, case.scale, nthreads, lib)
+    res = dict(o=o, S_T=ST, rows=rows, vheads=vheads, key_heads=key_heads, seqs=seqs)
+    if backward:
+        res.update(gdn_bwd(cu, q, k, v, g, beta, S0, dO, dST, case.scale, nthreads, lib))
+    return res

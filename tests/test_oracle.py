@@ -1,0 +1,338 @@
+"""Pins of the float64 oracle to things other than itself (CPU only).
+
+Each test ties the oracle to a fact fixed by the mathematics of the recurrence
+(lattice-inference 0.6.0, src/attention/gdn_backward.rs, "Forward recap" and
+gdn_backward steps 4a-4d), chosen so a plausible slip -- a dropped term, a wrong
+sign or index, a transposed operand, a wrong head map -- fails at least one:
+
+* central finite differences of the oracle's own forward for every gradient
+  (the check the dormouse KDA log uses: f64 loss, derived step size, the smaller
+  of the errors at h and h/10, normwise max|a-b|/max|b|);
+* a second formulation of the recurrence (the Householder form
+  S_t = g (I - beta k k^T) S_{t-1} + beta k v^T) in torch float64, with gradients by
+  autograd, not by the oracle's hand-derived backward;
+* closed forms: beta = 0 (pure decay of S0), T = 1, and g = beta = 1 with orthonormal
+  keys (the delta rule writes v exactly);
+* v_repeat = r equals explicit replication of q/k with dq/dk summed over the group
+  (the asymmetric-heads source-parity idea of the lattice-inference tests);
+* zero upstream gradient gives exactly zero gradients (same page's gradcheck tests);
+* linearity in V and in S0, split-sequence resume, zero-length sequences;
+* falsification: builds of the oracle with a planted mistake must fail a pin.
+"""
+import os
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_case
+
+
+def normwise(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.max(np.abs(b)) if b.size else 0.0
+    num = np.max(np.abs(a - b)) if a.size else 0.0
+    return num / den if den > 0 else num
+
+
+def small_case(seed, lens, Hk, Hv, D, s0=True, dst=True, gate="raw"):
+    return make_case(seed, lens, Hk, Hv, D, dtype="f32", chunk=16, gate=gate,
+                     with_S0=s0, with_dST=dst)
+
+
+def loss_of(case, lib=None, **over):
+    arrs = dict(q=case.q, k=case.k, v=case.v, g=case.g, beta=case.beta, S0=case.S0)
+    arrs.update(over)
+    o, ST = oracle.gdn_fwd(case.cu_seqlens, arrs["q"], arrs["k"], arrs["v"], arrs["g"],
+                           arrs["beta"], arrs["S0"], case.scale, nthreads=1, lib=lib)
+    L = float(np.sum(case.dO * o))
+    if case.dST is not None:
+        L += float(np.sum(case.dST * ST))
+    return L
+
+
+def fd_check(case, lib=None, max_coords=48, seed=0):
+    """Return {tensor: normwise error} of the oracle backward vs central differences."""
+    grads = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                           case.dO, case.dST, case.scale, nthreads=1, lib=lib)
+    L0 = loss_of(case, lib)
+    eps = np.finfo(np.float64).eps
+    rng = np.random.default_rng(seed)
+    errs = {}
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta")]
+    if case.S0 is not None:
+        names.append(("S0", "dS0"))
+    for name, gname in names:
+        x = getattr(case, name)
+        an = grads[gname]
+        gmax = max(np.max(np.abs(an)), 1e-30)
+        h0 = (3.0 * eps * max(abs(L0), 1.0) / gmax) ** (1.0 / 3.0)
+        idx = np.arange(x.size)
+        if x.size > max_coords:
+            idx = rng.choice(x.size, size=max_coords, replace=False)
+        best = np.inf
+        for h in (h0, h0 / 10):
+            fd = np.empty(len(idx))
+            for c, i in enumerate(idx):
+                xp = x.copy().reshape(-1)
+                xm = x.copy().reshape(-1)
+                xp[i] += h
+                xm[i] -= h
+                fd[c] = (loss_of(case, lib, **{name: xp.reshape(x.shape)})
+                         - loss_of(case, lib, **{name: xm.reshape(x.shape)})) / (2 * h)
+            best = min(best, normwise(an.reshape(-1)[idx], fd))
+        errs[gname] = best
+    return errs
+
+
+FD_SHAPES = [
+    # (lens, Hk, Hv, D)
+    ([9], 1, 1, 4),
+    ([7, 12], 1, 2, 4),
+    ([16], 2, 6, 8),
+    ([5, 0, 11], 2, 4, 8),
+    ([24], 1, 3, 16),
+]
+
+
+@pytest.mark.parametrize("shape", FD_SHAPES, ids=lambda s: f"lens{s[0]}_Hk{s[1]}_Hv{s[2]}_D{s[3]}")
+def test_fd_all_gradients(oracle_lib, shape):
+    lens, Hk, Hv, D = shape
+    case = small_case(7 + sum(lens), lens, Hk, Hv, D)
+    errs = fd_check(case)
+    for name, e in errs.items():
+        assert e < 1e-6, f"{name}: FD normwise error {e:.3e}"
+
+
+def householder_torch(case):
+    """Second formulation, torch float64 autograd: S_t = g (S - beta k (k^T S)) + beta k v^T."""
+    import torch
+
+    t = lambda a: None if a is None else torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    q, k, v, g, beta = map(t, (case.q, case.k, case.v, case.g, case.beta))
+    S0 = t(case.S0)
+    r = case.Hv // case.Hk
+    heads = torch.arange(case.Hv) // r
+    cu = case.cu_seqlens
+    outs, finals = [], []
+    for n in range(case.N):
+        if S0 is not None:
+            S = S0[n]
+        else:
+            S = torch.zeros(case.Hv, case.Dk, case.Dv, dtype=torch.float64)
+        for tt in range(cu[n], cu[n + 1]):
+            kt = k[tt][heads]  # [Hv, Dk]
+            qt = q[tt][heads]
+            bt = beta[tt][:, None, None]
+            gt = g[tt][:, None, None]
+            kS = torch.einsum("hi,hij->hj", kt, S)
+            S = gt * (S - bt * kt[:, :, None] * kS[:, None, :]) + bt * kt[:, :, None] * v[tt][:, None, :]
+            outs.append(case.scale * torch.einsum("hij,hi->hj", S, qt))
+        finals.append(S)
+    o = torch.stack(outs) if outs else torch.zeros(0, case.Hv, case.Dv, dtype=torch.float64)
+    ST = torch.stack(finals)
+    L = (o * torch.tensor(case.dO)).sum()
+    if case.dST is not None:
+        L = L + (ST * torch.tensor(case.dST)).sum()
+    L.backward()
+    grads = dict(dq=q.grad, dk=k.grad, dv=v.grad, dg=g.grad, dbeta=beta.grad,
+                 dS0=None if S0 is None else S0.grad)
+    return o.detach().numpy(), ST.detach().numpy(), {a: None if b is None else b.numpy() for a, b in grads.items()}
+
+
+@pytest.mark.parametrize("shape", [([20], 2, 4, 8), ([6, 17], 1, 3, 4), ([33], 2, 2, 16)],
+                         ids=["r2", "r3_two_seqs", "r1"])
+@pytest.mark.parametrize("s0", [False, True])
+def test_householder_form_and_autograd(oracle_lib, shape, s0):
+    lens, Hk, Hv, D = shape
+    case = small_case(11 + D, lens, Hk, Hv, D, s0=s0, dst=s0)
+    o_ref, ST_ref, g_ref = householder_torch(case)
+    o, ST = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0, case.scale)
+    assert normwise(o, o_ref) < 1e-13
+    assert normwise(ST, ST_ref) < 1e-13
+    gr = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                        case.dO, case.dST, case.scale)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert normwise(gr[name], g_ref[name]) < 1e-12, name
+    if s0:
+        assert normwise(gr["dS0"], g_ref["dS0"]) < 1e-12
+
+
+def test_beta_zero_is_pure_decay(oracle_lib):
+    case = small_case(3, [13, 5], 2, 4, 8, s0=True, dst=True)
+    case.beta[:] = 0.0
+    o, ST = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0, case.scale)
+    r = case.Hv // case.Hk
+    cu = case.cu_seqlens
+    for n in range(case.N):
+        decay = np.ones(case.Hv)
+        for t in range(cu[n], cu[n + 1]):
+            decay = decay * case.g[t]
+            for h in range(case.Hv):
+                expect = case.scale * decay[h] * case.S0[n, h].T @ case.q[t, h // r]
+                np.testing.assert_allclose(o[t, h], expect, rtol=1e-13, atol=1e-15)
+        for h in range(case.Hv):
+            np.testing.assert_allclose(ST[n, h], decay[h] * case.S0[n, h], rtol=1e-13, atol=1e-16)
+    gr = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                        case.dO, case.dST, case.scale)
+    assert np.all(gr["dv"] == 0.0)
+
+
+@pytest.mark.parametrize("s0", [False, True])
+def test_unit_gate_orthonormal_keys_write_v(oracle_lib, s0):
+    """g = beta = 1 and orthonormal keys: S_T^T k_r = v_r for every written key, and with
+    q_t = k_t the output is scale * v_t exactly (the delta rule overwrites the slot)."""
+    D, T = 8, 8
+    rng = np.random.default_rng(5)
+    Qm, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    case = small_case(5, [T], 1, 2, D, s0=s0, dst=False)
+    case.k[:, 0, :] = Qm.T[:T]
+    case.q[:, 0, :] = Qm.T[:T]
+    case.g[:] = 1.0
+    case.beta[:] = 1.0
+    o, ST = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0, case.scale)
+    for h in range(case.Hv):
+        for t in range(T):
+            np.testing.assert_allclose(ST[0, h].T @ case.k[t, 0], case.v[t, h], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(o[t, h], case.scale * case.v[t, h], rtol=0, atol=1e-13)
+
+
+def test_single_token_closed_form(oracle_lib):
+    case = small_case(17, [1], 1, 1, 8, s0=True, dst=True)
+    q, k, v = case.q[0, 0], case.k[0, 0], case.v[0, 0]
+    g, b = case.g[0, 0], case.beta[0, 0]
+    S0, dST, dO, sc = case.S0[0, 0], case.dST[0, 0], case.dO[0, 0], case.scale
+    delta = b * (v - g * (S0.T @ k))
+    S1 = g * S0 + np.outer(k, delta)
+    o_ref = sc * S1.T @ q
+    o, ST = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0, sc)
+    np.testing.assert_allclose(o[0, 0], o_ref, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(ST[0, 0], S1, rtol=1e-14, atol=1e-16)
+    # hand derivation of L = <dO, o> + <dS_T, S_1>
+    dS1 = dST + sc * np.outer(q, dO)
+    dq = sc * S1 @ dO
+    dd = dS1.T @ k
+    dk = dS1 @ delta - g * b * (S0 @ dd)
+    dv = b * dd
+    dbeta = (v - g * (S0.T @ k)) @ dd
+    dg = np.sum(S0 * dS1) - b * (S0.T @ k) @ dd
+    dS0 = g * dS1 - g * b * np.outer(k, dd)
+    gr = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                        case.dO, case.dST, sc)
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv), ("dS0", dS0)):
+        np.testing.assert_allclose(gr[name].reshape(ref.shape), ref, rtol=1e-12, atol=1e-14, err_msg=name)
+    np.testing.assert_allclose(gr["dbeta"][0, 0], dbeta, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gr["dg"][0, 0], dg, rtol=1e-12, atol=1e-14)
+
+
+def test_vrepeat_equals_replication(oracle_lib):
+    case = small_case(23, [10, 19], 2, 6, 8, s0=True, dst=True)
+    r = case.Hv // case.Hk
+    heads = np.arange(case.Hv) // r
+    o, ST = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0, case.scale)
+    qr, kr = case.q[:, heads], case.k[:, heads]
+    o2, ST2 = oracle.gdn_fwd(case.cu_seqlens, qr, kr, case.v, case.g, case.beta, case.S0, case.scale)
+    assert np.array_equal(o, o2) and np.array_equal(ST, ST2)
+    g1 = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                        case.dO, case.dST, case.scale)
+    g2 = oracle.gdn_bwd(case.cu_seqlens, qr, kr, case.v, case.g, case.beta, case.S0,
+                        case.dO, case.dST, case.scale)
+    for name in ("dv", "dg", "dbeta", "dS0"):
+        assert np.array_equal(g1[name], g2[name]), name
+    for name in ("dq", "dk"):
+        folded = np.zeros_like(g1[name])
+        for h in range(case.Hv):  # ascending head order, as the fold adds them
+            folded[:, h // r] += g2[name][:, h]
+        assert np.array_equal(g1[name], folded), name
+
+
+def test_zero_upstream_gives_zero_gradients(oracle_lib):
+    case = small_case(29, [14, 3], 2, 4, 8, s0=True, dst=False)
+    case.dO[:] = 0.0
+    gr = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                        case.dO, None, case.scale)
+    for name, a in gr.items():
+        assert np.all(a == 0.0), name
+
+
+def test_linearity_in_v_and_s0(oracle_lib):
+    case = small_case(31, [21], 1, 2, 8, s0=True, dst=False)
+    o1, S1 = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, None, case.scale)
+    o2, S2 = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, 0.37 * case.v, case.g, case.beta, None, case.scale)
+    np.testing.assert_allclose(o2, 0.37 * o1, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(S2, 0.37 * S1, rtol=1e-12, atol=1e-15)
+    zero_v = np.zeros_like(case.v)
+    oa, _ = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, zero_v, case.g, case.beta, case.S0, case.scale)
+    ob, _ = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, zero_v, case.g, case.beta, -2.5 * case.S0, case.scale)
+    np.testing.assert_allclose(ob, -2.5 * oa, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("m", [1, 37, 64, 70])
+def test_split_resume(oracle_lib, m):
+    T = 100
+    case = small_case(37, [T], 1, 2, 8, s0=True, dst=True)
+    full_o, full_ST = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0, case.scale)
+    full = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                          case.dO, case.dST, case.scale)
+    a, b = slice(0, m), slice(m, T)
+    cu_a, cu_b = np.array([0, m]), np.array([0, T - m])
+    oa, Sm = oracle.gdn_fwd(cu_a, case.q[a], case.k[a], case.v[a], case.g[a], case.beta[a], case.S0, case.scale)
+    ob, ST = oracle.gdn_fwd(cu_b, case.q[b], case.k[b], case.v[b], case.g[b], case.beta[b], Sm, case.scale)
+    assert np.array_equal(np.concatenate([oa, ob]), full_o)
+    assert np.array_equal(ST, full_ST)
+    gb = oracle.gdn_bwd(cu_b, case.q[b], case.k[b], case.v[b], case.g[b], case.beta[b], Sm,
+                        case.dO[b], case.dST, case.scale)
+    ga = oracle.gdn_bwd(cu_a, case.q[a], case.k[a], case.v[a], case.g[a], case.beta[a], case.S0,
+                        case.dO[a], gb["dS0"], case.scale)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        np.testing.assert_allclose(np.concatenate([ga[name], gb[name]]), full[name], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ga["dS0"], full["dS0"], rtol=1e-12, atol=1e-14)
+
+
+def test_zero_length_sequences(oracle_lib):
+    case = small_case(41, [0, 6, 0], 1, 2, 4, s0=True, dst=True)
+    o, ST = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0, case.scale)
+    assert np.array_equal(ST[0], case.S0[0]) and np.array_equal(ST[2], case.S0[2])
+    gr = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                        case.dO, case.dST, case.scale)
+    assert np.array_equal(gr["dS0"][0], case.dST[0]) and np.array_equal(gr["dS0"][2], case.dST[2])
+
+
+def test_threads_do_not_change_results(oracle_lib):
+    case = small_case(43, [40, 25, 33], 2, 6, 8, s0=True, dst=True)
+    a = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                       case.dO, case.dST, case.scale, nthreads=1)
+    b = oracle.gdn_bwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                       case.dO, case.dST, case.scale, nthreads=5)
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
+
+
+def _pins_fail(lib):
+    """Run a cheap subset of the pins against an oracle build; return names that failed."""
+    failed = []
+    case = small_case(101, [12], 2, 4, 4, s0=True, dst=True)
+    errs = fd_check(case, lib=lib, max_coords=16)
+    if any(e > 1e-6 for e in errs.values()):
+        failed.append("fd")
+    o_ref, _, g_ref = householder_torch(case)
+    o, _ = oracle.gdn_fwd(case.cu_seqlens, case.q, case.k, case.v, case.g, case.beta, case.S0,
+                          case.scale, lib=lib)
+    if normwise(o, o_ref) > 1e-12:
+        failed.append("householder")
+    return failed
+
+
+@pytest.mark.parametrize("plant", [1, 2, 3, 4],
+                         ids=["modulo_head_map", "drop_dk_retrieval_term", "dg_sign", "dq_no_scale"])
+def test_planted_mistake_is_caught(oracle_lib, plant):
+    with tempfile.TemporaryDirectory() as d:
+        lib = oracle.build(os.path.join(d, f"liboracle_plant{plant}.so"), plant=plant)
+        failed = _pins_fail(lib)
+    assert failed, f"planted mistake {plant} passed every pin"
+
+
+def test_unplanted_passes_the_same_pins(oracle_lib):
+    assert _pins_fail(oracle.LIB) == []
