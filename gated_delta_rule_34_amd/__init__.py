@@ -1,0 +1,197 @@
+"""gated_delta_rule_34_amd -- gated delta-net forward/backward on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``include/gdn.h`` (``libgdn.so``, built in-tree
+by ``gated_delta_rule_34_amd.build``). Functions keep the C names; this layer only
+marshals arguments: PyTorch provides device memory and the current HIP stream, every
+step of the computation runs in the library's HIP kernels. There is no CPU fallback:
+importing fails loudly when the library has not been built.
+
+Convenience wrappers ``forward`` / ``backward`` allocate outputs, the saved chunk
+states and the workspace with torch and call ``gdn_fwd`` / ``gdn_bwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4, -5
+GDN_F32, GDN_BF16 = 0, 1
+
+EXPORTED = ("gdn_fwd", "gdn_bwd", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
+            "gdn_chunk_state_bytes", "gdn_strerror")
+
+
+class gdn_problem(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("T_total", ctypes.c_int64),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("Hk", ctypes.c_int32),
+        ("Hv", ctypes.c_int32),
+        ("Dk", ctypes.c_int32),
+        ("Dv", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m gated_delta_rule_34_amd.build, or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    prob = ctypes.POINTER(gdn_problem)
+    for name in ("gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_chunk_state_bytes"):
+        fn = getattr(lib, name)
+        fn.argtypes = [prob]
+        fn.restype = SZ
+    lib.gdn_fwd.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, P, I64, P, P, P, SZ, P]
+    lib.gdn_fwd.restype = ctypes.c_int
+    lib.gdn_bwd.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, P, P, I64, P,
+                            P, I64, P, I64, P, I64, P, P, P, P, SZ, P]
+    lib.gdn_bwd.restype = ctypes.c_int
+    lib.gdn_strerror.argtypes = [ctypes.c_int]
+    lib.gdn_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def gdn_strerror(status: int) -> str:
+    return _lib.gdn_strerror(int(status)).decode()
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {gdn_strerror(status)} ({status})")
+        self.status = status
+
+
+def make_problem(N, T_total, Hk, Hv, D, *, T=None, cu_seqlens=None, chunk=64, scale=None, dtype="bf16"):
+    """Build a gdn_problem. ``cu_seqlens``: device int32 tensor [N + 1] or None."""
+    p = gdn_problem()
+    p.N = int(N)
+    p.T_total = int(T_total)
+    p.T = int(T if T is not None else (T_total // N if (cu_seqlens is None and N) else 0))
+    p.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
+    p.Hk, p.Hv, p.Dk, p.Dv = int(Hk), int(Hv), int(D), int(D)
+    p.chunk = int(chunk)
+    p.scale = float(scale if scale is not None else D ** -0.5)
+    p.dtype = {"f32": GDN_F32, "bf16": GDN_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    return p
+
+
+def gdn_fwd_workspace_bytes(p: gdn_problem) -> int:
+    return int(_lib.gdn_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def gdn_bwd_workspace_bytes(p: gdn_problem) -> int:
+    return int(_lib.gdn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def gdn_chunk_state_bytes(p: gdn_problem) -> int:
+    return int(_lib.gdn_chunk_state_bytes(ctypes.byref(p)))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rs(t, width):
+    """Row stride (elements) of a [rows, width] or [rows, heads, D] view whose rows hold
+    contiguous heads; the ABI requires exactly that inner layout."""
+    if t is None:
+        return 0
+    if t.dim() == 3:
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError("inner head layout must be contiguous")
+    elif t.dim() == 2:
+        if t.stride(1) != 1 or t.shape[1] != width:
+            raise ValueError("rows must be contiguous")
+    else:
+        raise ValueError("expected a 2-D or 3-D row view")
+    return t.stride(0)
+
+
+def _stream(stream):
+    import torch
+
+    return stream if stream is not None else torch.cuda.current_stream().cuda_stream
+
+
+def gdn_fwd(p, q, k, v, g, beta, S0, o, S_T, chunk_states, workspace, stream=None):
+    """Call gdn_fwd on torch tensors (views). Raises GdnError on a non-OK status."""
+    qk, vw = p.Hk * p.Dk, p.Hv * p.Dv
+    st = _lib.gdn_fwd(ctypes.byref(p), _ptr(q), _rs(q, qk), _ptr(k), _rs(k, qk), _ptr(v), _rs(v, vw),
+                      _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _rs(o, vw), _ptr(S_T), _ptr(chunk_states),
+                      _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                      _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_fwd")
+
+
+def gdn_bwd(p, q, k, v, g, beta, S0, chunk_states, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
+            stream=None):
+    qk, vw = p.Hk * p.Dk, p.Hv * p.Dv
+    st = _lib.gdn_bwd(ctypes.byref(p), _ptr(q), _rs(q, qk), _ptr(k), _rs(k, qk), _ptr(v), _rs(v, vw),
+                      _ptr(g), _ptr(beta), _ptr(S0), _ptr(chunk_states), _ptr(dO), _rs(dO, vw), _ptr(dS_T),
+                      _ptr(dq), _rs(dq, qk), _ptr(dk), _rs(dk, qk), _ptr(dv), _rs(dv, vw),
+                      _ptr(dg), _ptr(dbeta), _ptr(dS0),
+                      _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                      _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_bwd")
+
+
+def _empty_bytes(n, device):
+    import torch
+
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def forward(p, q, k, v, g, beta, S0=None, o=None, want_final=True, workspace=None, stream=None):
+    """Allocate o, S_T and the saved chunk states, run gdn_fwd; returns (o, S_T, states)."""
+    import torch
+
+    dev = v.device
+    T = p.T_total
+    if o is None:
+        o = torch.empty(T, p.Hv, p.Dv, dtype=v.dtype, device=dev)
+    S_T = torch.empty(p.N, p.Hv, p.Dk, p.Dv, dtype=torch.float32, device=dev) if want_final else None
+    states = _empty_bytes(gdn_chunk_state_bytes(p), dev)
+    if workspace is None:
+        workspace = _empty_bytes(gdn_fwd_workspace_bytes(p), dev)
+    gdn_fwd(p, q, k, v, g, beta, S0, o, S_T, states, workspace, stream)
+    return o, S_T, states
+
+
+def backward(p, q, k, v, g, beta, S0, states, dO, dS_T=None, grads=None, want_dS0=True, workspace=None,
+             stream=None):
+    """Allocate gradients, run gdn_bwd; returns dict dq, dk, dv, dg, dbeta, dS0."""
+    import torch
+
+    dev = v.device
+    T = p.T_total
+    if grads is None:
+        grads = dict(
+            dq=torch.empty(T, p.Hk, p.Dk, dtype=v.dtype, device=dev),
+            dk=torch.empty(T, p.Hk, p.Dk, dtype=v.dtype, device=dev),
+            dv=torch.empty(T, p.Hv, p.Dv, dtype=v.dtype, device=dev),
+            dg=torch.empty(T, p.Hv, dtype=torch.float32, device=dev),
+            dbeta=torch.empty(T, p.Hv, dtype=torch.float32, device=dev),
+            dS0=torch.empty(p.N, p.Hv, p.Dk, p.Dv, dtype=torch.float32, device=dev) if want_dS0 else None,
+        )
+    if workspace is None:
+        workspace = _empty_bytes(gdn_bwd_workspace_bytes(p), dev)
+    gdn_bwd(p, q, k, v, g, beta, S0, states, dO, dS_T, grads["dq"], grads["dk"], grads["dv"], grads["dg"],
+            grads["dbeta"], grads["dS0"], workspace, stream)
+    return grads

@@ -1,0 +1,257 @@
+// gdn_abi.cpp -- host side of the C ABI declared in include/gdn.h: argument checks,
+// workspace layout and kernel launch sequencing. No allocation, no synchronisation.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "gdn_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Shape {
+  int64_t nc_max;
+  int C, D;
+};
+
+// Upper bound on the number of chunks: sum_n ceil(len_n / C).
+int64_t chunk_bound(const gdn_problem* p) {
+  const int64_t C = p->chunk;
+  if (p->cu_seqlens) return (p->T_total + (int64_t)p->N * (C - 1)) / C;
+  return (int64_t)p->N * (((int64_t)p->T + C - 1) / C);
+}
+
+gdn_status check_problem(const gdn_problem* p) {
+  if (!p) return GDN_EINVAL;
+  if (p->N < 0 || p->T_total < 0 || p->Hk <= 0 || p->Hv <= 0 || p->Hv % p->Hk) return GDN_EINVAL;
+  if (p->Dk <= 0 || p->Dv <= 0) return GDN_EINVAL;
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16) return GDN_EUNSUPPORTED;
+  if (p->Dk != p->Dv) return GDN_EUNSUPPORTED;
+  if (p->Dk != 16 && p->Dk != 32 && p->Dk != 64 && p->Dk != 128) return GDN_EUNSUPPORTED;
+  if (p->chunk != 16 && p->chunk != 64) return GDN_EUNSUPPORTED;
+  if (!std::isfinite(p->scale)) return GDN_EINVAL;
+  if (!p->cu_seqlens) {
+    if (p->T < 0 || (int64_t)p->N * p->T != p->T_total) return GDN_EINVAL;
+  } else if (p->N == 0 && p->T_total != 0) {
+    return GDN_EINVAL;
+  }
+  if (p->T_total > INT32_MAX - 64) return GDN_EINVAL;
+  const int64_t nc = chunk_bound(p);
+  if (nc > INT32_MAX / 64) return GDN_EINVAL;
+  return GDN_OK;
+}
+
+// Region sizes in bytes, in the order they are carved out of the workspace.
+struct Regions {
+  size_t chunks, seq_chunk, cvec, ccmat, cdmat, ddmat, scal;
+};
+
+Regions regions(const gdn_problem* p) {
+  const size_t nc = (size_t)chunk_bound(p), Hv = (size_t)p->Hv, C = (size_t)p->chunk, D = (size_t)p->Dk;
+  Regions r;
+  r.chunks = align_up(nc * sizeof(gdn::ChunkInfo));
+  r.seq_chunk = align_up(((size_t)p->N + 1) * sizeof(int));
+  r.cvec = align_up(nc * Hv * C * sizeof(float));
+  r.ccmat = align_up(nc * Hv * C * C * sizeof(float));
+  r.cdmat = align_up(nc * Hv * C * D * sizeof(float));
+  r.ddmat = align_up(nc * Hv * D * D * sizeof(float));
+  r.scal = align_up(nc * Hv * sizeof(float));
+  return r;
+}
+
+size_t fwd_ws(const gdn_problem* p) {
+  const Regions r = regions(p);
+  return r.chunks + r.seq_chunk + r.cvec + r.ccmat + 2 * r.cdmat;
+}
+
+size_t bwd_ws(const gdn_problem* p) {
+  const Regions r = regions(p);
+  // table, gam, Tm, W, U, dDi, dDel, dstates, XQ, XW, XK, Pb, dT, ebar, rq, rho, db1, sdot,
+  // dKbb, dqh, dkh
+  return r.chunks + r.seq_chunk + 5 * r.cvec + 3 * r.ccmat + 10 * r.cdmat + r.ddmat + r.scal;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+gdn_status check_view(const void* ptr, int64_t rs, int64_t width, int esize, int64_t T_total) {
+  if (T_total == 0) return GDN_OK;
+  if (!ptr) return GDN_EINVAL;
+  if (rs < width) return GDN_EINVAL;
+  if (!aligned(ptr, 16) || ((size_t)rs * esize) % 16) return GDN_EALIGN;
+  return GDN_OK;
+}
+
+gdn_status check_f32(const void* ptr, bool required) {
+  if (!ptr) return required ? GDN_EINVAL : GDN_OK;
+  return aligned(ptr, 4) ? GDN_OK : GDN_EALIGN;
+}
+
+#define GDN_TRY(x)                   \
+  do {                               \
+    const gdn_status s_ = (x);       \
+    if (s_ != GDN_OK) return s_;     \
+  } while (0)
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T> T* take(size_t bytes) {
+    T* r = reinterpret_cast<T*>(base + off);
+    off += bytes;
+    return r;
+  }
+};
+
+void fill_common(gdn::Prob& P, const gdn_problem* p) {
+  P = gdn::Prob{};
+  P.N = p->N;
+  P.Hk = p->Hk;
+  P.Hv = p->Hv;
+  P.r = p->Hv / p->Hk;
+  P.D = p->Dk;
+  P.C = p->chunk;
+  P.nc_max = (int)chunk_bound(p);
+  P.T = p->cu_seqlens ? 0 : p->T;
+  P.T_total = p->T_total;
+  P.scale = p->scale;
+  P.cu = p->cu_seqlens;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_fwd_workspace_bytes(const gdn_problem* p) { return check_problem(p) == GDN_OK ? fwd_ws(p) : 0; }
+
+size_t gdn_bwd_workspace_bytes(const gdn_problem* p) { return check_problem(p) == GDN_OK ? bwd_ws(p) : 0; }
+
+size_t gdn_chunk_state_bytes(const gdn_problem* p) {
+  return check_problem(p) == GDN_OK ? regions(p).ddmat : 0;
+}
+
+gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                   const void* v, int64_t v_rs, const float* g, const float* beta, const float* S0, void* o,
+                   int64_t o_rs, float* S_T, void* chunk_states, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  GDN_TRY(check_problem(p));
+  const int es = p->dtype == GDN_BF16 ? 2 : 4;
+  const int64_t qkw = (int64_t)p->Hk * p->Dk, vw = (int64_t)p->Hv * p->Dv;
+  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total));
+  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total));
+  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total));
+  GDN_TRY(check_view(o, o_rs, vw, es, p->T_total));
+  GDN_TRY(check_f32(g, p->T_total > 0));
+  GDN_TRY(check_f32(beta, p->T_total > 0));
+  GDN_TRY(check_f32(S0, false));
+  GDN_TRY(check_f32(S_T, false));
+  if (p->N == 0) return GDN_OK;
+  if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
+  if (!chunk_states) return GDN_EINVAL;
+  if (!aligned(chunk_states, 16)) return GDN_EALIGN;
+  const size_t need = fwd_ws(p);
+  if (!workspace || workspace_bytes < need) return GDN_EWORKSPACE;
+  if (!aligned(workspace, kAlign)) return GDN_EALIGN;
+
+  gdn::Prob P;
+  fill_common(P, p);
+  P.q = q; P.q_rs = q_rs; P.k = k; P.k_rs = k_rs; P.v = v; P.v_rs = v_rs;
+  P.g = g; P.beta = beta; P.S0 = S0;
+  P.o = o; P.o_rs = o_rs; P.ST = S_T;
+  P.states = static_cast<float*>(chunk_states);
+  const Regions r = regions(p);
+  Carver cv{static_cast<char*>(workspace)};
+  P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
+  P.seq_chunk = cv.take<int>(r.seq_chunk);
+  P.gam = cv.take<float>(r.cvec);
+  P.Tm = cv.take<float>(r.ccmat);
+  P.W = cv.take<float>(r.cdmat);
+  P.U = cv.take<float>(r.cdmat);
+  const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                   const void* v, int64_t v_rs, const float* g, const float* beta, const float* S0,
+                   const void* chunk_states, const void* dO, int64_t dO_rs, const float* dS_T, void* dq,
+                   int64_t dq_rs, void* dk, int64_t dk_rs, void* dv, int64_t dv_rs, float* dg, float* dbeta,
+                   float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  GDN_TRY(check_problem(p));
+  const int es = p->dtype == GDN_BF16 ? 2 : 4;
+  const int64_t qkw = (int64_t)p->Hk * p->Dk, vw = (int64_t)p->Hv * p->Dv;
+  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total));
+  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total));
+  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total));
+  GDN_TRY(check_view(dO, dO_rs, vw, es, p->T_total));
+  GDN_TRY(check_view(dq, dq_rs, qkw, es, p->T_total));
+  GDN_TRY(check_view(dk, dk_rs, qkw, es, p->T_total));
+  GDN_TRY(check_view(dv, dv_rs, vw, es, p->T_total));
+  GDN_TRY(check_f32(g, p->T_total > 0));
+  GDN_TRY(check_f32(beta, p->T_total > 0));
+  GDN_TRY(check_f32(dg, p->T_total > 0));
+  GDN_TRY(check_f32(dbeta, p->T_total > 0));
+  GDN_TRY(check_f32(S0, false));
+  GDN_TRY(check_f32(dS_T, false));
+  GDN_TRY(check_f32(dS0, false));
+  if (p->N == 0) return GDN_OK;
+  if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
+  if (!chunk_states) return GDN_EINVAL;
+  if (!aligned(chunk_states, 16)) return GDN_EALIGN;
+  const size_t need = bwd_ws(p);
+  if (!workspace || workspace_bytes < need) return GDN_EWORKSPACE;
+  if (!aligned(workspace, kAlign)) return GDN_EALIGN;
+
+  gdn::Prob P;
+  fill_common(P, p);
+  P.q = q; P.q_rs = q_rs; P.k = k; P.k_rs = k_rs; P.v = v; P.v_rs = v_rs;
+  P.g = g; P.beta = beta; P.S0 = S0;
+  P.states = const_cast<float*>(static_cast<const float*>(chunk_states));
+  P.dO = dO; P.dO_rs = dO_rs; P.dST = dS_T;
+  P.dq = dq; P.dq_rs = dq_rs; P.dk = dk; P.dk_rs = dk_rs; P.dv = dv; P.dv_rs = dv_rs;
+  P.dg = dg; P.dbeta = dbeta; P.dS0 = dS0;
+  const Regions r = regions(p);
+  Carver cv{static_cast<char*>(workspace)};
+  P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
+  P.seq_chunk = cv.take<int>(r.seq_chunk);
+  P.gam = cv.take<float>(r.cvec);
+  P.ebar = cv.take<float>(r.cvec);
+  P.rq = cv.take<float>(r.cvec);
+  P.rho = cv.take<float>(r.cvec);
+  P.db1 = cv.take<float>(r.cvec);
+  P.Tm = cv.take<float>(r.ccmat);
+  P.Pb = cv.take<float>(r.ccmat);
+  P.dT = cv.take<float>(r.ccmat);
+  P.W = cv.take<float>(r.cdmat);
+  P.U = cv.take<float>(r.cdmat);
+  P.dDi = cv.take<float>(r.cdmat);
+  P.dDel = cv.take<float>(r.cdmat);
+  P.XQ = cv.take<float>(r.cdmat);
+  P.XW = cv.take<float>(r.cdmat);
+  P.XK = cv.take<float>(r.cdmat);
+  P.dKbb = cv.take<float>(r.cdmat);
+  P.dqh = cv.take<float>(r.cdmat);
+  P.dkh = cv.take<float>(r.cdmat);
+  P.dstates = cv.take<float>(r.ddmat);
+  P.sdot = cv.take<float>(r.scal);
+  const hipError_t e = gdn::launch_backward(P, p->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+const char* gdn_strerror(int status) {
+  switch (status) {
+    case GDN_OK: return "success";
+    case GDN_EINVAL: return "invalid argument (size, count, stride or missing pointer)";
+    case GDN_EUNSUPPORTED: return "unsupported head size, chunk length or dtype";
+    case GDN_EALIGN: return "misaligned pointer or row stride";
+    case GDN_EWORKSPACE: return "workspace missing or too small";
+    case GDN_EHIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta-net recurrence: forward and
+ * reverse-mode backward.
+ *
+ * The operation (lattice-inference 0.6.0, docs.rs source page of
+ * src/attention/gdn_backward.rs, module doc "Forward recap"), per sequence and per
+ * value head h, with q and k read from key head kh = h / (Hv / Hk):
+ *
+ *   kv_t    = S_{t-1}^T k_t                    (retrieval from the pre-decay state)
+ *   delta_t = beta_t * (v_t - g_t * kv_t)
+ *   S_t     = g_t * S_{t-1} + k_t (x) delta_t    (S is Dk x Dv, stored key-major)
+ *   o_t     = scale * S_t^T q_t
+ *
+ * starting from S_{-1} = S0 (zero when S0 is NULL). The backward is the same page's
+ * gdn_backward steps 4a-4d run in reverse time with the state adjoint dS carried
+ * across tokens, starting from dS_T (zero when NULL), and returns dq, dk, dv, dg,
+ * dbeta and dS0. dq and dk of a key head sum the contributions of every value head
+ * that reads it (the cross-head accumulation of page 1, the llama.cpp fork's
+ * "delta-net backward at the shape the 27B emits"); the sum is formed in float32 in
+ * ascending head order and rounded once, without atomics, so results are
+ * bit-reproducible run to run.
+ *
+ * Memory. Every pointer is a DEVICE pointer unless noted. The caller owns all memory;
+ * the library never allocates, never frees and never synchronises the stream: calls
+ * only enqueue kernels on `stream` (a hipStream_t; NULL = the default stream).
+ * Buffers written by a call must not be read or written by other work until that
+ * work is ordered after the call on the stream.
+ *
+ * Layout. A "row" is one token. q, k, v, o, dO, dq, dk, dv are row-strided views:
+ * element (t, head, d) of q is at q[t * q_rs + head * Dk + d]; row strides are in
+ * elements. So q, k and v may be column slices of one packed projection row
+ * [q heads | k heads | v heads], and dq, dk, dv may be the same slices of a packed
+ * gradient buffer. g, beta, dg, dbeta are contiguous [T_total][Hv] float32;
+ * S0, S_T, dS_T, dS0 are contiguous [N][Hv][Dk][Dv] float32.
+ *
+ * Errors. Arguments are checked on the host before anything is enqueued; a negative
+ * status means nothing was enqueued and nothing written. Device-side cu_seqlens are
+ * not readable from the host without a synchronisation; their values are clamped
+ * into [0, T_total] on the device, so a malformed table yields wrong results but
+ * never an out-of-bounds access.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,       /* bad size, count, stride or missing required pointer */
+  GDN_EUNSUPPORTED = -2, /* head size / chunk / dtype combination not built */
+  GDN_EALIGN = -3,       /* pointer or row stride not aligned as required */
+  GDN_EWORKSPACE = -4,   /* workspace missing or smaller than the size query returns */
+  GDN_EHIP = -5          /* a kernel launch failed (hipGetLastError) */
+} gdn_status;
+
+typedef enum {
+  GDN_F32 = 0, /* q, k, v, o, dO, dq, dk, dv are float32 */
+  GDN_BF16 = 1 /* ... are bfloat16; arithmetic and the state stay float32 */
+} gdn_dtype;
+
+typedef struct {
+  int32_t N;        /* number of sequences (>= 0) */
+  int32_t T;        /* tokens per sequence when cu_seqlens == NULL; ignored otherwise */
+  int64_t T_total;  /* total rows: N * T, or cu_seqlens[N] (host-known) */
+  const int32_t* cu_seqlens; /* DEVICE int32 [N + 1]: cu[0] = 0, nondecreasing, cu[N] = T_total;
+                                NULL = N sequences of T tokens. Zero-length sequences allowed:
+                                their S_T is S0 and their dS0 is dS_T. */
+  int32_t Hk, Hv;   /* key heads and value heads; Hv % Hk == 0, v_repeat = Hv / Hk */
+  int32_t Dk, Dv;   /* head sizes; this build requires Dk == Dv in {16, 32, 64, 128} */
+  int32_t chunk;    /* chunk length of the chunked algorithm: 16 or 64 (results agree
+                       up to rounding) */
+  float scale;      /* output scale, normally 1 / sqrt(Dk) */
+  int32_t dtype;    /* gdn_dtype */
+} gdn_problem;
+
+/* Bytes of device workspace gdn_fwd / gdn_bwd need for this problem (0 on invalid
+ * problem). The workspace is scratch: its contents on entry are ignored. */
+size_t gdn_fwd_workspace_bytes(const gdn_problem* p);
+size_t gdn_bwd_workspace_bytes(const gdn_problem* p);
+
+/* Bytes of the saved-state buffer gdn_fwd writes and gdn_bwd reads: the float32
+ * state at the start of every chunk (layout internal to the library). */
+size_t gdn_chunk_state_bytes(const gdn_problem* p);
+
+/*
+ * Forward. Reads q, k [rows][Hk*Dk], v [rows][Hv*Dv] (dtype), g, beta [T_total][Hv]
+ * (float32; 0 < g <= 1 is required by the chunked form: it works with log g), S0
+ * (float32 or NULL = zeros). Writes o [rows][Hv*Dv] (dtype, row stride o_rs),
+ * S_T (or NULL to skip) and chunk_states (required, gdn_chunk_state_bytes; keep it
+ * unchanged for gdn_bwd).
+ * Alignment: q, k, v, o and the row strides times the element size must be
+ * multiples of 16 bytes; float32 arrays need 4-byte alignment.
+ */
+gdn_status gdn_fwd(const gdn_problem* p,
+                   const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                   const void* v, int64_t v_rs, const float* g, const float* beta,
+                   const float* S0, void* o, int64_t o_rs, float* S_T, void* chunk_states,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward. q, k, v, g, beta, S0 and chunk_states must be those of the forward call
+ * on the same problem. dO [rows][Hv*Dv] (dtype), dS_T (float32 or NULL = zeros).
+ * Writes dq, dk [rows][Hk*Dk] and dv [rows][Hv*Dv] (dtype, overwritten, each with
+ * its own row stride; they may be disjoint slices of one packed buffer), dg and
+ * dbeta [T_total][Hv] float32, dS0 (float32, or NULL to skip). dg is the derivative
+ * with respect to the gate value g itself.
+ */
+gdn_status gdn_bwd(const gdn_problem* p,
+                   const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                   const void* v, int64_t v_rs, const float* g, const float* beta,
+                   const float* S0, const void* chunk_states,
+                   const void* dO, int64_t dO_rs, const float* dS_T,
+                   void* dq, int64_t dq_rs, void* dk, int64_t dk_rs, void* dv, int64_t dv_rs,
+                   float* dg, float* dbeta, float* dS0,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string for a status code. */
+const char* gdn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

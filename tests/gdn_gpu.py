@@ -1,0 +1,123 @@
+"""Helpers for the GPU tests: move a synth.GdnCase onto the device in the layout the
+workload uses (packed qkv rows or contiguous), run the HIP path through the C ABI
+binding, and compare with the oracle (normwise max|a-b| / max|b| per tensor)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+OUT_NAMES = ("o", "S_T")
+GRAD_NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+
+
+def normwise(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(b)))
+    num = float(np.max(np.abs(a - b)))
+    return num / den if den > 0 else num
+
+
+def tol_of(case):
+    return 2e-4 if case.dtype == "f32" else 2e-2
+
+
+def to_device(case, device="cuda", packed=None):
+    """Device tensors for a case. Packed workloads get one [T, 2*Hk*Dk + Hv*Dv] buffer
+    with q, k, v as row views; dq/dk/dv are views into one packed gradient buffer too."""
+    import torch
+
+    dt = torch.float32 if case.dtype == "f32" else torch.bfloat16
+    packed = case.packed if packed is None else packed
+    T, Hk, Hv, D = case.T_total, case.Hk, case.Hv, case.Dk
+    tt = lambda a, dtype=torch.float32: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(
+        torch.float32).to(dtype).to(device)
+    d = {}
+    if packed:
+        width = 2 * Hk * D + Hv * D
+        buf = torch.empty(T, width, dtype=dt, device=device)
+        buf[:, : Hk * D] = tt(case.q.reshape(T, Hk * D), dt)
+        buf[:, Hk * D: 2 * Hk * D] = tt(case.k.reshape(T, Hk * D), dt)
+        buf[:, 2 * Hk * D:] = tt(case.v.reshape(T, Hv * D), dt)
+        d["packed"] = buf
+        d["q"], d["k"], d["v"] = buf[:, : Hk * D], buf[:, Hk * D: 2 * Hk * D], buf[:, 2 * Hk * D:]
+        gbuf = torch.empty(T, width, dtype=dt, device=device)
+        d["gpacked"] = gbuf
+        d["dq"], d["dk"], d["dv"] = gbuf[:, : Hk * D], gbuf[:, Hk * D: 2 * Hk * D], gbuf[:, 2 * Hk * D:]
+    else:
+        d["q"], d["k"], d["v"] = tt(case.q, dt), tt(case.k, dt), tt(case.v, dt)
+        d["dq"] = torch.empty(T, Hk, D, dtype=dt, device=device)
+        d["dk"] = torch.empty(T, Hk, D, dtype=dt, device=device)
+        d["dv"] = torch.empty(T, Hv, D, dtype=dt, device=device)
+    d["g"], d["beta"] = tt(case.g), tt(case.beta)
+    d["S0"], d["dST"] = tt(case.S0), tt(case.dST)
+    d["dO"] = tt(case.dO, dt)
+    d["cu"] = torch.tensor(case.cu_seqlens, dtype=torch.int32, device=device) if case.varlen else None
+    return d
+
+
+def problem(case, d, chunk=None):
+    import gated_delta_rule_34_amd as G
+
+    if case.varlen:
+        return G.make_problem(case.N, case.T_total, case.Hk, case.Hv, case.Dk, cu_seqlens=d["cu"],
+                              chunk=chunk or case.chunk, scale=case.scale, dtype=case.dtype)
+    T = case.lens[0] if case.N else 0
+    assert all(L == T for L in case.lens)
+    return G.make_problem(case.N, case.T_total, case.Hk, case.Hv, case.Dk, T=T, chunk=chunk or case.chunk,
+                          scale=case.scale, dtype=case.dtype)
+
+
+def run_gpu(case, backward=True, chunk=None, packed=None, d=None):
+    """Run forward (+ backward) through the C ABI; returns numpy float64 results."""
+    import torch
+    import gated_delta_rule_34_amd as G
+
+    d = d or to_device(case, packed=packed)
+    p = problem(case, d, chunk)
+    T, Hk, Hv, D = case.T_total, case.Hk, case.Hv, case.Dk
+    o = torch.empty(T, Hv, D, dtype=d["v"].dtype, device=d["v"].device)
+    o, S_T, states = G.forward(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o=o)
+    res = dict(o=o, S_T=S_T)
+    if backward:
+        grads = dict(dq=d["dq"], dk=d["dk"], dv=d["dv"],
+                     dg=torch.empty(T, Hv, dtype=torch.float32, device=o.device),
+                     dbeta=torch.empty(T, Hv, dtype=torch.float32, device=o.device),
+                     dS0=torch.empty(case.N, Hv, D, D, dtype=torch.float32, device=o.device))
+        G.backward(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], states, d["dO"], d["dST"], grads=grads)
+        res.update(grads)
+    torch.cuda.synchronize()
+    out = {}
+    for name, t in res.items():
+        a = t.float().cpu().numpy().astype(np.float64)
+        if name in ("o", "dv"):
+            a = a.reshape(T, Hv, D)
+        elif name in ("dq", "dk"):
+            a = a.reshape(T, Hk, D)
+        out[name] = a
+    return out
+
+
+def compare(case, gpu, ref, names, tol=None, report=None):
+    """Per-tensor normwise error of gpu vs oracle on the oracle's (possibly sampled)
+    rows and heads. Returns {name: err}; asserts each below tol."""
+    tol = tol_of(case) if tol is None else tol
+    rows, vheads, kheads, seqs = ref["rows"], ref["vheads"], ref["key_heads"], ref["seqs"]
+    errs = {}
+    for name in names:
+        g = gpu[name]
+        if name in ("o", "dv", "dg", "dbeta"):
+            g = g[rows][:, vheads]
+        elif name in ("dq", "dk"):
+            g = g[rows][:, kheads]
+        elif name in ("S_T", "dS0"):
+            g = g[seqs][:, vheads]
+        errs[name] = normwise(g, ref[name])
+    if report is not None:
+        report.update(errs)
+    bad = {k: v for k, v in errs.items() if not v < tol}
+    assert not bad, f"{case.name}: normwise errors above {tol}: {bad} (all: {errs})"
+    return errs

@@ -1,0 +1,150 @@
+"""C ABI host-side contract (CPU only: no kernel is ever launched here).
+
+The library loads, exports every function include/gdn.h declares, sizes its
+workspaces, and rejects bad arguments with the documented status before it touches
+the GPU. Every call below fails validation by construction; none reaches a launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def G():
+    lib = os.path.join(ROOT, "gated_delta_rule_34_amd", "libgdn.so")
+    if not os.path.exists(lib):
+        from gated_delta_rule_34_amd.build import build
+
+        build()
+    import gated_delta_rule_34_amd as G
+
+    return G
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(G):
+    names = header_functions()
+    assert set(names) == set(G.EXPORTED), names
+    lib = ctypes.CDLL(G.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", G.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported as a text symbol"
+
+
+def prob(G, **kw):
+    base = dict(N=2, T_total=256, Hk=16, Hv=48, D=128, T=128, chunk=64, dtype="bf16")
+    base.update(kw)
+    N, T_total, Hk, Hv, D = (base.pop(k) for k in ("N", "T_total", "Hk", "Hv", "D"))
+    return G.make_problem(N, T_total, Hk, Hv, D, **base)
+
+
+def test_workspace_queries(G):
+    p = prob(G)
+    assert G.gdn_fwd_workspace_bytes(p) > 0
+    assert G.gdn_bwd_workspace_bytes(p) > G.gdn_fwd_workspace_bytes(p)
+    nc = 2 * 2  # two sequences of two chunks
+    assert G.gdn_chunk_state_bytes(p) >= nc * 48 * 128 * 128 * 4
+    bigger = prob(G, T_total=512, T=256)
+    assert G.gdn_bwd_workspace_bytes(bigger) > G.gdn_bwd_workspace_bytes(p)
+    bad = prob(G, Hv=47)
+    assert G.gdn_fwd_workspace_bytes(bad) == 0
+    assert G.gdn_bwd_workspace_bytes(bad) == 0
+    assert G.gdn_chunk_state_bytes(bad) == 0
+
+
+def test_strerror(G):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert G.gdn_strerror(code)
+    assert "unknown" in G.gdn_strerror(7)
+
+
+class FakeTensor:
+    """Stands in for a device tensor: a fixed address and 2-D row-view strides. It is
+    never dereferenced, since every call below is rejected on the host."""
+
+    def __init__(self, addr, rows, width, rs=None, nbytes=None):
+        self.addr, self.shape, self._rs = addr, (rows, width), rs or width
+        self._nbytes = nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def dim(self):
+        return 2
+
+    def stride(self, i):
+        return (self._rs, 1)[i]
+
+    def numel(self):
+        return self._nbytes or 0
+
+    def element_size(self):
+        return 1
+
+
+def fwd_args(G, p, **over):
+    T = p.T_total
+    a = dict(q=FakeTensor(0x10000, T, p.Hk * p.Dk, 10240), k=FakeTensor(0x20000, T, p.Hk * p.Dk, 10240),
+             v=FakeTensor(0x30000, T, p.Hv * p.Dv, 10240), g=FakeTensor(0x40000, T, p.Hv),
+             beta=FakeTensor(0x50000, T, p.Hv), S0=None, o=FakeTensor(0x60000, T, p.Hv * p.Dv),
+             S_T=None, chunk_states=FakeTensor(0x70000, 1, 1), workspace=FakeTensor(0x80000, 1, 1, nbytes=16))
+    a.update(over)
+    return a
+
+
+def status_of(G, p, **over):
+    a = fwd_args(G, p, **over)
+    with pytest.raises(G.GdnError) as e:
+        G.gdn_fwd(p, a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"], a["S_T"], a["chunk_states"],
+                  a["workspace"], stream=0)
+    return e.value.status
+
+
+def test_rejects_bad_problems(G):
+    assert status_of(G, prob(G, Hv=47)) == G.GDN_EINVAL
+    assert status_of(G, prob(G, D=96)) == G.GDN_EUNSUPPORTED
+    assert status_of(G, prob(G, chunk=32)) == G.GDN_EUNSUPPORTED
+    assert status_of(G, prob(G, dtype=5)) == G.GDN_EUNSUPPORTED
+    assert status_of(G, prob(G, T_total=255)) == G.GDN_EINVAL  # != N * T
+    p = prob(G)
+    p.Dv = 64
+    assert status_of(G, p) == G.GDN_EUNSUPPORTED
+    p = prob(G)
+    p.scale = float("nan")
+    assert status_of(G, p) == G.GDN_EINVAL
+
+
+def test_rejects_bad_views(G):
+    p = prob(G)
+    T = p.T_total
+    assert status_of(G, p, q=FakeTensor(0x10000, T, 2048, 1000)) == G.GDN_EINVAL  # row stride < width
+    assert status_of(G, p, q=FakeTensor(0x10002, T, 2048, 10240)) == G.GDN_EALIGN
+    assert status_of(G, p, v=FakeTensor(0x30000, T, 6144, 10241)) == G.GDN_EALIGN  # stride * 2 B % 16
+    assert status_of(G, p, g=FakeTensor(0x40002, T, 48)) == G.GDN_EALIGN
+    assert status_of(G, p, beta=None) == G.GDN_EINVAL
+    assert status_of(G, p, chunk_states=None) == G.GDN_EINVAL
+
+
+def test_rejects_small_workspace(G):
+    p = prob(G)
+    assert status_of(G, p) == G.GDN_EWORKSPACE
+    assert status_of(G, p, workspace=None) == G.GDN_EWORKSPACE
+
+
+def test_rejects_varlen_inconsistency(G):
+    p = prob(G)
+    p.N = 0
+    p.cu_seqlens = 0x90000
+    assert status_of(G, p) == G.GDN_EINVAL  # no sequences but rows

@@ -1,0 +1,118 @@
+"""GPU structural exactness and determinism (HIP path vs itself, bit for bit).
+
+* varlen-packed (cu_seqlens) equals per-sequence calls, on every output;
+* strided row views of a packed projection equal contiguous copies;
+* v_repeat = r equals explicit replication of q/k (r = 1): o, S_T, dv, dg, dbeta and dS0
+  bit-identical; dq/dk, which the library folds in float32 before one rounding,
+  within tolerance of the host-side sum of the replicated heads;
+* two runs are bit-identical (no atomics anywhere);
+* split resume at a chunk boundary: [0, m) then [m, T) with S0 = S_m equals the whole run.
+"""
+import numpy as np
+import pytest
+
+from synth import make_case
+from gdn_gpu import GRAD_NAMES, normwise, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+ALL = ("o", "S_T") + GRAD_NAMES
+
+
+def _case(lens, Hk=2, Hv=6, D=64, dtype="bf16", chunk=64, varlen=False, packed=True, seed=77):
+    return make_case(seed, lens, Hk, Hv, D, dtype=dtype, chunk=chunk, gate="clamp09", with_S0=True,
+                     with_dST=True, packed=packed, varlen=varlen, name=f"exact{lens}")
+
+
+def _sub(case, n):
+    """Sequence n of a case as its own single-sequence case."""
+    import copy
+
+    cu = case.cu_seqlens
+    a, b = cu[n], cu[n + 1]
+    c = copy.copy(case)
+    c.lens = [int(b - a)]
+    c.varlen = False
+    for name in ("q", "k", "v", "g", "beta", "dO"):
+        setattr(c, name, getattr(case, name)[a:b])
+    c.S0 = case.S0[n:n + 1]
+    c.dST = case.dST[n:n + 1]
+    return c
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_equals_per_sequence(dtype):
+    case = _case([70, 0, 129, 64, 5], dtype=dtype, varlen=True)
+    full = run_gpu(case)
+    cu = case.cu_seqlens
+    for n in range(case.N):
+        if case.lens[n] == 0:
+            assert np.array_equal(full["S_T"][n], case.S0[n])
+            assert np.array_equal(full["dS0"][n], case.dST[n])
+            continue
+        one = run_gpu(_sub(case, n))
+        rows = slice(cu[n], cu[n + 1])
+        for name in ("o", "dq", "dk", "dv", "dg", "dbeta"):
+            assert np.array_equal(full[name][rows], one[name]), (n, name)
+        for name in ("S_T", "dS0"):
+            assert np.array_equal(full[name][n], one[name][0]), (n, name)
+
+
+def test_strided_equals_contiguous():
+    case = _case([150, 150])
+    a = run_gpu(case, packed=True)
+    b = run_gpu(case, packed=False)
+    for name in ALL:
+        assert np.array_equal(a[name], b[name]), name
+
+
+def test_vrepeat_equals_replication():
+    case = _case([140], Hk=2, Hv=6)
+    r = case.Hv // case.Hk
+    heads = np.arange(case.Hv) // r
+    import copy
+
+    rep = copy.copy(case)
+    rep.Hk = case.Hv
+    rep.q = case.q[:, heads]
+    rep.k = case.k[:, heads]
+    a = run_gpu(case)
+    b = run_gpu(rep)
+    for name in ("o", "S_T", "dv", "dg", "dbeta", "dS0"):
+        assert np.array_equal(a[name], b[name]), name
+    for name in ("dq", "dk"):
+        folded = np.zeros_like(a[name])
+        for h in range(case.Hv):
+            folded[:, h // r] += b[name][:, h]
+        assert normwise(a[name], folded) < 1e-2, name
+
+
+def test_determinism_bitwise():
+    case = _case([300, 300], Hk=2, Hv=6, D=128)
+    a = run_gpu(case)
+    b = run_gpu(case)
+    for name in ALL:
+        assert np.array_equal(a[name], b[name]), name
+
+
+def test_split_resume_at_chunk_boundary():
+    import copy
+
+    case = _case([256], Hk=1, Hv=3, D=64, dtype="f32")
+    full = run_gpu(case)
+    m = 128
+    first, second = copy.copy(case), copy.copy(case)
+    first.lens, second.lens = [m], [256 - m]
+    for name in ("q", "k", "v", "g", "beta", "dO"):
+        setattr(first, name, getattr(case, name)[:m])
+        setattr(second, name, getattr(case, name)[m:])
+    a = run_gpu(first, backward=False)
+    second.S0 = a["S_T"]
+    b = run_gpu(second)
+    first.dST = b["dS0"]
+    a = run_gpu(first)
+    assert np.array_equal(np.concatenate([a["o"], b["o"]]), full["o"])
+    assert np.array_equal(b["S_T"], full["S_T"])
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.array_equal(np.concatenate([a[name], b[name]]), full[name]), name
+    assert np.array_equal(a["dS0"], full["dS0"])
