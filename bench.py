@@ -1,0 +1,163 @@
+#!/usr/bin/env python3
+"""Benchmark: gated delta-net forward + backward tokens/s on one MI355X.
+
+Workload: 4 sequences x 4096 tokens, 16 key heads shared by 48 value heads, head size
+128, q/k/v as bf16 row views of one packed [16384, 10240] projection, float32 gates
+and state, chunk 64, S0 = 0, dS_T ~ N(0, 0.1^2) (the 27B-layer training shape; inputs
+from synth.config_case(3), seeded, synthetic). One step = gdn_fwd (saving chunk
+states) + gdn_bwd over the whole batch; inputs are resident in HBM before timing.
+
+Prints one JSON line. ``roofline`` covers the kernel with the largest share of the
+step, timed live with HIP events recorded by the library around each launch on the
+launch stream; ``cpu_baseline`` times the float64 oracle on one of the four sequences
+(all 48 heads), fwd + bwd, on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd+bwd tokens/s @Hk16/Hv48/D128 T=4096; % MFMA / HBM roofline"
+PEAK = {"f32_mfma": 157.3e12, "bf16_mfma": 2.5e15, "hbm": 8.0e12}
+
+
+def kernel_work(name, C, D, Hk, Hv, n_chunks):
+    """Algorithmic MFMA flops of one launch (sum over its units) for the kernels of
+    the chunked path; the per-unit counts are the products each kernel forms, per
+    (chunk, value head)."""
+    units = n_chunks * Hv
+    per_unit = {
+        "k_wy": 6 * C * C * D,                          # K K^T, W, U
+        "k_fwd_state": 4 * C * D * D,                   # W S, K~^T Delta
+        "k_fwd_out": 4 * C * C * D + 2 * C * D * D,     # Q K^T, M Delta; Q S
+        "k_bwd_intra": 4 * C * C * D + 2 * C * D * D,   # Q K^T, M^T dO~; W S
+        "k_bwd_state": 6 * C * D * D,                   # K~ dS, Q^T dO~, W^T dDelta
+        "k_bwd_grad1": 6 * C * D * D + 6 * C * C * D,   # XQ, XW, XK; P, dT1, T^T dDelta
+        "k_bwd_grad2a": 6 * C * C * D,                  # (P o Gamma) K, T^T XW, XW K^T
+        "k_bwd_grad2b": 4 * C * C * C + 10 * C * C * D,  # dT T^T, T^T Z; 3 for dK; Q K^T, K K^T
+    }.get(name)
+    return None if per_unit is None else per_unit * units
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_34_amd as G
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gdn_gpu import problem, to_device
+    from synth import config_case
+
+    case = config_case(3)
+    d = to_device(case)
+    p = problem(case, d)
+    T, Hk, Hv, D, C = case.T_total, case.Hk, case.Hv, case.Dk, case.chunk
+    dev = d["v"].device
+    o = torch.empty(T, Hv, D, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty(case.N, Hv, D, D, dtype=torch.float32, device=dev)
+    states = torch.empty(G.gdn_chunk_state_bytes(p), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(G.gdn_fwd_workspace_bytes(p), G.gdn_bwd_workspace_bytes(p)), dtype=torch.uint8,
+                     device=dev)
+    dg = torch.empty(T, Hv, dtype=torch.float32, device=dev)
+    dbeta = torch.empty(T, Hv, dtype=torch.float32, device=dev)
+    dS0 = torch.empty(case.N, Hv, D, D, dtype=torch.float32, device=dev)
+
+    def fwd():
+        G.gdn_fwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T, states, ws)
+
+    def bwd():
+        G.gdn_bwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], states, d["dO"], d["dST"],
+                  d["dq"], d["dk"], d["dv"], dg, dbeta, dS0, ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    print(f"[bench] workload ready: T_total={T} Hk={Hk} Hv={Hv} D={D} C={C}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    G.gdn_trace_enable(True)
+    G.gdn_trace_collect()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    G.gdn_trace_enable(False)
+    trace = G.gdn_trace_collect()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        fwd()
+    end.record()
+    torch.cuda.synchronize()
+    ms_fwd = start.elapsed_time(end) / args.steps
+    print(f"[bench] timed: {ms_step:.3f} ms/step, fwd {ms_fwd:.3f} ms", file=sys.stderr, flush=True)
+
+    n_chunks = T // C
+    kernels = {k: round(v[0] / v[1], 4) for k, v in sorted(trace.items(), key=lambda kv: -kv[1][0])}
+    dom = max(trace.items(), key=lambda kv: kv[1][0])[0]
+    avg_s = trace[dom][0] / trace[dom][1] / 1e3
+    flops = kernel_work(dom, C, D, Hk, Hv, n_chunks)
+    achieved = flops / avg_s / 1e12
+    peak = PEAK["bf16_mfma"] / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "avg_launch_ms": round(avg_s * 1e3, 4), "operand_dtype": "bf16"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build()
+        nthreads = min(oracle.default_threads(), 16)
+        t0 = time.perf_counter()
+        oracle.run_case(case, backward=True, seqs=[0], nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(case.lens[0] / dt, 2), "unit": "tokens/s", "cores": min(nthreads, Hk),
+               "kind": "oracle",
+               "sample": f"sequence 0 of 4 ({case.lens[0]} tokens, all {Hv} value heads), fwd+bwd, float64; "
+                         f"{dt:.1f} s"}
+
+    line = {
+        "metric": METRIC, "value": round(T / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "B4 T4096 Hk16 Hv48 Dk=Dv=128, bf16 packed qkv [16384,10240], f32 gates/state, "
+                               "chunk 64, fwd (saving chunk states) + bwd",
+                   "global_batch": case.N, "seq_len": case.lens[0], "parallelism": "single GPU"},
+        "fwd_tokens_per_s": round(T / (ms_fwd / 1e3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_avg_ms": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,11 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_EWORKSPACE, GDN_EHIP = 0, 
 GDN_F32, GDN_BF16 = 0, 1
 
 EXPORTED = ("gdn_fwd", "gdn_bwd", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
-            "gdn_chunk_state_bytes", "gdn_strerror")
+            "gdn_chunk_state_bytes", "gdn_strerror", "gdn_trace_enable", "gdn_trace_collect")
+
+
+class gdn_trace_entry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("total_ms", ctypes.c_double), ("launches", ctypes.c_int64)]
 
 
 class gdn_problem(ctypes.Structure):
@@ -58,6 +62,10 @@ def _load():
     lib.gdn_bwd.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, P, P, I64, P,
                             P, I64, P, I64, P, I64, P, P, P, P, SZ, P]
     lib.gdn_bwd.restype = ctypes.c_int
+    lib.gdn_trace_enable.argtypes = [ctypes.c_int]
+    lib.gdn_trace_enable.restype = ctypes.c_int
+    lib.gdn_trace_collect.argtypes = [ctypes.POINTER(gdn_trace_entry), ctypes.c_int]
+    lib.gdn_trace_collect.restype = ctypes.c_int
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     lib.gdn_strerror.restype = ctypes.c_char_p
     return lib
@@ -88,6 +96,17 @@ def make_problem(N, T_total, Hk, Hv, D, *, T=None, cu_seqlens=None, chunk=64, sc
     p.scale = float(scale if scale is not None else D ** -0.5)
     p.dtype = {"f32": GDN_F32, "bf16": GDN_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
     return p
+
+
+def gdn_trace_enable(on: bool) -> None:
+    _lib.gdn_trace_enable(1 if on else 0)
+
+
+def gdn_trace_collect(max_entries: int = 64) -> dict:
+    """{kernel name: (total milliseconds, launches)} since the last collect."""
+    buf = (gdn_trace_entry * max_entries)()
+    n = _lib.gdn_trace_collect(buf, max_entries)
+    return {buf[i].name.decode(): (buf[i].total_ms, int(buf[i].launches)) for i in range(n)}
 
 
 def gdn_fwd_workspace_bytes(p: gdn_problem) -> int:

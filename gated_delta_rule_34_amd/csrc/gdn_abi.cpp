@@ -87,9 +87,9 @@ gdn_status check_view(const void* ptr, int64_t rs, int64_t width, int esize, int
   return GDN_OK;
 }
 
-gdn_status check_f32(const void* ptr, bool required) {
+gdn_status check_f32(const void* ptr, bool required, size_t align = 4) {
   if (!ptr) return required ? GDN_EINVAL : GDN_OK;
-  return aligned(ptr, 4) ? GDN_OK : GDN_EALIGN;
+  return aligned(ptr, align) ? GDN_OK : GDN_EALIGN;
 }
 
 #define GDN_TRY(x)                   \
@@ -148,8 +148,8 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   GDN_TRY(check_view(o, o_rs, vw, es, p->T_total));
   GDN_TRY(check_f32(g, p->T_total > 0));
   GDN_TRY(check_f32(beta, p->T_total > 0));
-  GDN_TRY(check_f32(S0, false));
-  GDN_TRY(check_f32(S_T, false));
+  GDN_TRY(check_f32(S0, false, 16));
+  GDN_TRY(check_f32(S_T, false, 16));
   if (p->N == 0) return GDN_OK;
   if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
   if (!chunk_states) return GDN_EINVAL;
@@ -195,9 +195,9 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   GDN_TRY(check_f32(beta, p->T_total > 0));
   GDN_TRY(check_f32(dg, p->T_total > 0));
   GDN_TRY(check_f32(dbeta, p->T_total > 0));
-  GDN_TRY(check_f32(S0, false));
-  GDN_TRY(check_f32(dS_T, false));
-  GDN_TRY(check_f32(dS0, false));
+  GDN_TRY(check_f32(S0, false, 16));
+  GDN_TRY(check_f32(dS_T, false, 16));
+  GDN_TRY(check_f32(dS0, false, 16));
   if (p->N == 0) return GDN_OK;
   if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
   if (!chunk_states) return GDN_EINVAL;

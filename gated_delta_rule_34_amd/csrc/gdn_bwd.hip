@@ -30,40 +30,25 @@ template <int D> struct BwdCfg {
   static constexpr int BG = 16;                // column block of k_bwd_grad1
 };
 
-template <int M, int N, class F>
-__device__ __forceinline__ void for_each2(const Acc<M, N>& x, const Acc<M, N>& y, F&& f) {
-  using TL = Tiles<M, N>;
-  const int l = lane_id();
-#pragma unroll
-  for (int q = 0; q < TL::PER; ++q) {
-    const int t = wave_id() + q * NW;
-    if (t < TL::TOT) {
-      const int i0 = (t / TL::NT) * 16 + (l >> 4) * 4, j = (t % TL::NT) * 16 + (l & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f(i0 + e, j, x.a[q][e], y.a[q][e]);
-    }
-  }
-}
-
 // Grid (nc_max, Hv): Delta = U - W S0 (overwrites U) and dDi = (Gamma o Q K^T)^T dO~.
 template <typename TI, int C, int D, int BV>
 __global__ __launch_bounds__(NTHREADS) void k_bwd_intra(Prob p) {
   constexpr Prec P = PrecOf<TI>::value;
   constexpr int LD = D + 4, LB = BV + 4, LC = C + 4;
-  __shared__ float sQ[C * LD];  // Q, then W
-  __shared__ float sK[C * LD];
-  __shared__ float sM[C * LC];
-  __shared__ float sS[D * LB];
-  __shared__ float sU[C * LB];
-  __shared__ float sO[C * LB];
-  __shared__ float sg[C], ssc[C];
+  __shared__ __align__(16) float sQ[C * LD];  // Q, then W
+  __shared__ __align__(16) float sK[C * LD];
+  __shared__ __align__(16) float sM[C * LC];
+  __shared__ __align__(16) float sS[D * LB];
+  __shared__ __align__(16) float sU[C * LB];
+  __shared__ __align__(16) float sO[C * LB];
+  __shared__ __align__(16) float sg[C], ssc[C];
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int kh = h / p.r, n = ci.len;
   const size_t ch = ch_idx(p, c, h);
-  load_tile<C, D>(sQ, LD, (const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n);
-  load_tile<C, D>(sK, LD, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
+  load_tile<C, D, LD>(sQ, (const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n);
+  load_tile<C, D, LD>(sK, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
   for (int i = threadIdx.x; i < C; i += NTHREADS) {
     sg[i] = p.gam[ch * C + i];
     ssc[i] = p.scale;
@@ -72,22 +57,22 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_intra(Prob p) {
   {
     Acc<C, C> m;
     m.zero();
-    mma<P, C, C, D>(m, rows(sQ, LD), cols(sK, LD));
+    mma<P, C, C, D>(m, rows<LD>(sQ), cols<LD>(sK));
     for_each(m, [&](int i, int j, float x) { sM[i * LC + j] = i >= j ? x * expf(sg[i] - sg[j]) : 0.f; });
   }
   __syncthreads();
-  load_tile<C, D>(sQ, LD, p.W + ch * C * D, D, C);
+  load_tile<C, D, LD>(sQ, p.W + ch * C * D, D, C);
   const TI* dO = (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D;
   for (int j0 = 0; j0 < D; j0 += BV) {
-    load_tile<D, BV>(sS, LB, p.states + ch * D * D + j0, D, D);
-    load_tile<C, BV>(sU, LB, p.U + ch * C * D + j0, D, C);
-    load_tile_rs<C, BV>(sO, LB, dO + j0, p.dO_rs, n, ssc);
+    load_tile<D, BV, LB>(sS, p.states + ch * D * D + j0, D, D);
+    load_tile<C, BV, LB>(sU, p.U + ch * C * D + j0, D, C);
+    load_tile<C, BV, LB>(sO, dO + j0, p.dO_rs, n, ssc);
     __syncthreads();
     Acc<C, BV> a, b;
     a.zero();
     b.zero();
-    mma<P, C, BV, D>(a, rows(sQ, LD), rows(sS, LB));
-    mma<P, C, BV, C>(b, cols(sM, LC), rows(sO, LB));
+    mma<P, C, BV, D>(a, rows<LD>(sQ), rows<LB>(sS));
+    mma<P, C, BV, C>(b, cols<LC>(sM), rows<LB>(sO));
     for_each2(a, b, [&](int i, int j, float x, float y) {
       p.U[ch * C * D + (size_t)i * D + j0 + j] = sU[i * LB + j] - x;
       p.dDi[ch * C * D + (size_t)i * D + j0 + j] = y;
@@ -102,29 +87,25 @@ template <typename TI, int C, int D, int BV>
 __global__ __launch_bounds__(NTHREADS) void k_bwd_state(Prob p) {
   constexpr Prec P = PrecOf<TI>::value;
   constexpr int LD = D + 4, LB = BV + 4;
-  __shared__ float sdS[D * LB];
-  __shared__ float sX[C * LD];
-  __shared__ float sDb[C * LB];
-  __shared__ float sO[C * LB];
-  __shared__ float sg[C], se[C], sb[C], ssc[C];
+  __shared__ __align__(16) float sdS[D * LB];
+  __shared__ __align__(16) float sX[C * LD];
+  __shared__ __align__(16) float sDb[C * LB];
+  __shared__ __align__(16) float sO[C * LB];
+  __shared__ __align__(16) float sg[C], se[C], sb[C], ssc[C];
   const int n = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * BV;
   const int kh = h / p.r;
   const size_t nh = (size_t)n * p.Hv + h;
-  for (int idx = threadIdx.x; idx < D * BV; idx += NTHREADS) {
-    const int i = idx / BV, j = idx % BV;
-    sdS[i * LB + j] = p.dST ? p.dST[nh * D * D + (size_t)i * D + j0 + j] : 0.f;
-  }
+  if (p.dST)
+    load_tile<D, BV, LB>(sdS, p.dST + nh * D * D + j0, D, D);
+  else
+    for (int idx = threadIdx.x; idx < D * BV; idx += NTHREADS) sdS[(idx / BV) * LB + idx % BV] = 0.f;
   for (int i = threadIdx.x; i < C; i += NTHREADS) ssc[i] = p.scale;
   const int c0 = p.seq_chunk[n], c1 = p.seq_chunk[n + 1];
   __syncthreads();
   for (int c = c1 - 1; c >= c0; --c) {
     const ChunkInfo ci = p.chunks[c];
     const size_t ch = ch_idx(p, c, h);
-    float* dst = p.dstates + ch * D * D;
-    for (int idx = threadIdx.x; idx < D * BV; idx += NTHREADS) {
-      const int i = idx / BV, j = idx % BV;
-      dst[(size_t)i * D + j0 + j] = sdS[i * LB + j];
-    }
+    store_tile<D, BV, LB>(p.dstates + ch * D * D + j0, D, sdS, D);
     for (int i = threadIdx.x; i < C; i += NTHREADS) sg[i] = p.gam[ch * C + i];
     __syncthreads();
     for (int i = threadIdx.x; i < C; i += NTHREADS) {
@@ -132,13 +113,13 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_state(Prob p) {
       sb[i] = expf(sg[i]);
     }
     __syncthreads();
-    load_tile_rs<C, D>(sX, LD, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, ci.len, se);
-    load_tile<C, BV>(sDb, LB, p.dDi + ch * C * D + j0, D, C);
+    load_tile<C, D, LD>(sX, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, ci.len, se);
+    load_tile<C, BV, LB>(sDb, p.dDi + ch * C * D + j0, D, C);
     __syncthreads();
     {
       Acc<C, BV> a;
       a.zero();
-      mma<P, C, BV, D>(a, rows(sX, LD), rows(sdS, LB));
+      mma<P, C, BV, D>(a, rows<LD>(sX), rows<LB>(sdS));
       for_each(a, [&](int i, int j, float x) {
         const float d = sDb[i * LB + j] + x;
         sDb[i * LB + j] = d;
@@ -146,26 +127,22 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_state(Prob p) {
       });
     }
     __syncthreads();
-    load_tile_rs<C, D>(sX, LD, (const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, ci.len, sb);
-    load_tile_rs<C, BV>(sO, LB, (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + j0, p.dO_rs, ci.len, ssc);
+    load_tile<C, D, LD>(sX, (const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, ci.len, sb);
+    load_tile<C, BV, LB>(sO, (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + j0, p.dO_rs, ci.len, ssc);
     __syncthreads();
     Acc<D, BV> s1, s2;
     s1.zero();
     s2.zero();
-    mma<P, D, BV, C>(s1, cols(sX, LD), rows(sO, LB));
+    mma<P, D, BV, C>(s1, cols<LD>(sX), rows<LB>(sO));
     __syncthreads();
-    load_tile<C, D>(sX, LD, p.W + ch * C * D, D, C);
+    load_tile<C, D, LD>(sX, p.W + ch * C * D, D, C);
     __syncthreads();
-    mma<P, D, BV, C>(s2, cols(sX, LD), rows(sDb, LB));
+    mma<P, D, BV, C>(s2, cols<LD>(sX), rows<LB>(sDb));
     const float bn = expf(sg[C - 1]);
     for_each2(s1, s2, [&](int i, int j, float x, float y) { sdS[i * LB + j] = bn * sdS[i * LB + j] + x - y; });
     __syncthreads();
   }
-  if (p.dS0)
-    for (int idx = threadIdx.x; idx < D * BV; idx += NTHREADS) {
-      const int i = idx / BV, j = idx % BV;
-      p.dS0[nh * D * D + (size_t)i * D + j0 + j] = sdS[i * LB + j];
-    }
+  if (p.dS0) store_tile<D, BV, LB>(p.dS0 + nh * D * D + j0, D, sdS, D);
 }
 
 // Grid (nc_max, Hv). Everything that needs the chunk's S0 or dS_C, streamed over
@@ -174,24 +151,24 @@ template <typename TI, int C, int D, int BG>
 __global__ __launch_bounds__(NTHREADS) void k_bwd_grad1(Prob p) {
   constexpr Prec P = PrecOf<TI>::value;
   constexpr int LB = BG + 4, LC = C + 4;
-  __shared__ float sS0[D * LB];
-  __shared__ float sdS[D * LB];
-  __shared__ float sDl[C * LB];   // Delta
-  __shared__ float sDe[C * LB];   // diag(e) Delta
-  __shared__ float sdD[C * LB];   // dDelta
-  __shared__ float sDi[C * LB];   // intra part of dDelta
-  __shared__ float sO[C * LB];    // dO~
-  __shared__ float sVb[C * LB];   // diag(beta) V
-  __shared__ float sV[C * LB];    // V
-  __shared__ float sR[C * LB];    // dVbeta o V
-  __shared__ float sT[C * LC];
-  __shared__ float sg[C], se[C], sbeta[C], ssc[C], sred[NTHREADS];
+  __shared__ __align__(16) float sS0[D * LB];
+  __shared__ __align__(16) float sdS[D * LB];
+  __shared__ __align__(16) float sDl[C * LB];   // Delta
+  __shared__ __align__(16) float sDe[C * LB];   // diag(e) Delta
+  __shared__ __align__(16) float sdD[C * LB];   // dDelta
+  __shared__ __align__(16) float sDi[C * LB];   // intra part of dDelta
+  __shared__ __align__(16) float sO[C * LB];    // dO~
+  __shared__ __align__(16) float sVb[C * LB];   // diag(beta) V
+  __shared__ __align__(16) float sV[C * LB];    // V
+  __shared__ __align__(16) float sR[C * LB];    // dVbeta o V
+  __shared__ __align__(16) float sT[C * LC];
+  __shared__ __align__(16) float sg[C], se[C], sbeta[C], ssc[C], sred[NTHREADS];
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int n = ci.len;
   const size_t ch = ch_idx(p, c, h);
-  load_tile<C, C>(sT, LC, p.Tm + ch * C * C, C, C);
+  load_tile<C, C, LC>(sT, p.Tm + ch * C * C, C, C);
   for (int i = threadIdx.x; i < C; i += NTHREADS) {
     sg[i] = p.gam[ch * C + i];
     sbeta[i] = i < n ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
@@ -208,25 +185,25 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_grad1(Prob p) {
   TI* dV = (TI*)p.dv + (int64_t)ci.t0 * p.dv_rs + h * D;
   for (int j0 = 0; j0 < D; j0 += BG) {
     __syncthreads();
-    load_tile<D, BG>(sS0, LB, p.states + ch * D * D + j0, D, D);
-    load_tile<D, BG>(sdS, LB, p.dstates + ch * D * D + j0, D, D);
-    load_tile<C, BG>(sDl, LB, p.U + ch * C * D + j0, D, C);
-    load_tile_rs<C, BG>(sDe, LB, p.U + ch * C * D + j0, D, C, se);
-    load_tile<C, BG>(sdD, LB, p.dDel + ch * C * D + j0, D, C);
-    load_tile<C, BG>(sDi, LB, p.dDi + ch * C * D + j0, D, C);
-    load_tile_rs<C, BG>(sO, LB, dO + j0, p.dO_rs, n, ssc);
-    load_tile_rs<C, BG>(sVb, LB, V + j0, p.v_rs, n, sbeta);
-    load_tile<C, BG>(sV, LB, V + j0, p.v_rs, n);
+    load_tile<D, BG, LB>(sS0, p.states + ch * D * D + j0, D, D);
+    load_tile<D, BG, LB>(sdS, p.dstates + ch * D * D + j0, D, D);
+    load_tile<C, BG, LB>(sDl, p.U + ch * C * D + j0, D, C);
+    load_tile<C, BG, LB>(sDe, p.U + ch * C * D + j0, D, C, se);
+    load_tile<C, BG, LB>(sdD, p.dDel + ch * C * D + j0, D, C);
+    load_tile<C, BG, LB>(sDi, p.dDi + ch * C * D + j0, D, C);
+    load_tile<C, BG, LB>(sO, dO + j0, p.dO_rs, n, ssc);
+    load_tile<C, BG, LB>(sVb, V + j0, p.v_rs, n, sbeta);
+    load_tile<C, BG, LB>(sV, V + j0, p.v_rs, n);
     __syncthreads();
-    mma<P, C, D, BG>(XQ, rows(sO, LB), cols(sS0, LB));
-    mma<P, C, D, BG>(XW, rows(sdD, LB), cols(sS0, LB));
-    mma<P, C, D, BG>(XK, rows(sDe, LB), cols(sdS, LB));
-    mma<P, C, C, BG>(PP, rows(sO, LB), cols(sDl, LB));
-    mma<P, C, C, BG>(dT1, rows(sdD, LB), cols(sVb, LB));
+    mma<P, C, D, BG>(XQ, rows<LB>(sO), cols<LB>(sS0));
+    mma<P, C, D, BG>(XW, rows<LB>(sdD), cols<LB>(sS0));
+    mma<P, C, D, BG>(XK, rows<LB>(sDe), cols<LB>(sdS));
+    mma<P, C, C, BG>(PP, rows<LB>(sO), cols<LB>(sDl));
+    mma<P, C, C, BG>(dT1, rows<LB>(sdD), cols<LB>(sVb));
     {
       Acc<C, BG> a;
       a.zero();
-      mma<P, C, BG, C>(a, cols(sT, LC), rows(sdD, LB));
+      mma<P, C, BG, C>(a, cols<LC>(sT), rows<LB>(sdD));
       for_each(a, [&](int i, int j, float x) {
         if (i < n) dV[(int64_t)i * p.dv_rs + j0 + j] = from_f<TI>(sbeta[i] * x);
         sR[i * LB + j] = x * sV[i * LB + j];
@@ -270,20 +247,20 @@ template <typename TI, int C, int D>
 __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2a(Prob p) {
   constexpr Prec P = PrecOf<TI>::value;
   constexpr int LD = D + 4, LC = C + 4;
-  __shared__ float sK[C * LD];
-  __shared__ float sX[C * LD];  // XQ, then XW, then dK_beta_b o K
-  __shared__ float sT[C * LC];
-  __shared__ float sPG[C * LC];
-  __shared__ float sg[C], sb[C], sbeta[C];
+  __shared__ __align__(16) float sK[C * LD];
+  __shared__ __align__(16) float sX[C * LD];  // XQ, then XW, then dK_beta_b o K
+  __shared__ __align__(16) float sT[C * LC];
+  __shared__ __align__(16) float sPG[C * LC];
+  __shared__ __align__(16) float sg[C], sb[C], sbeta[C];
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int kh = h / p.r, n = ci.len;
   const size_t ch = ch_idx(p, c, h);
   const size_t cd = ch * C * D, cc = ch * C * C;
-  load_tile<C, D>(sK, LD, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
-  load_tile<C, C>(sT, LC, p.Tm + cc, C, C);
-  load_tile<C, D>(sX, LD, p.XQ + cd, D, C);
+  load_tile<C, D, LD>(sK, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
+  load_tile<C, C, LC>(sT, p.Tm + cc, C, C);
+  load_tile<C, D, LD>(sX, p.XQ + cd, D, C);
   for (int i = threadIdx.x; i < C; i += NTHREADS) {
     sg[i] = p.gam[ch * C + i];
     sbeta[i] = i < n ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
@@ -298,7 +275,7 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2a(Prob p) {
   {
     Acc<C, D> a;
     a.zero();
-    mma<P, C, D, C>(a, rows(sPG, LC), rows(sK, LD));
+    mma<P, C, D, C>(a, rows<LC>(sPG), rows<LD>(sK));
     for_each(a, [&](int i, int j, float x) { p.dqh[cd + i * D + j] = sb[i] * sX[i * LD + j] + x; });
   }
   if (threadIdx.x < C) {
@@ -311,14 +288,14 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2a(Prob p) {
     p.rq[ch * C + i] = s;
   }
   __syncthreads();
-  load_tile<C, D>(sX, LD, p.XW + cd, D, C);
+  load_tile<C, D, LD>(sX, p.XW + cd, D, C);
   __syncthreads();
   Acc<C, D> kb;
   Acc<C, C> dt;
   kb.zero();
   dt.zero();
-  mma<P, C, D, C>(kb, cols(sT, LC), rows(sX, LD));
-  mma<P, C, C, D>(dt, rows(sX, LD), cols(sK, LD));
+  mma<P, C, D, C>(kb, cols<LC>(sT), rows<LD>(sX));
+  mma<P, C, C, D>(dt, rows<LD>(sX), cols<LD>(sK));
   for_each(dt, [&](int i, int j, float x) { p.dT[cc + i * C + j] -= sbeta[j] * sb[j] * x; });
   __syncthreads();
   for_each(kb, [&](int i, int j, float x) {
@@ -339,20 +316,20 @@ template <typename TI, int C, int D>
 __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2b(Prob p) {
   constexpr Prec P = PrecOf<TI>::value;
   constexpr int LD = D + 4, LC = C + 4;
-  __shared__ float sQ[C * LD];
-  __shared__ float sK[C * LD];
-  __shared__ float sB1[C * LC];  // T, then dL
-  __shared__ float sB2[C * LC];  // dT, then Z = dT T^T, then G, then dL o Gamma o KK
-  __shared__ float sB3[C * LC];  // P o Gamma, then Gbar o Gamma
-  __shared__ float sg[C], sb[C], sbeta[C], sdg[C];
+  __shared__ __align__(16) float sQ[C * LD];
+  __shared__ __align__(16) float sK[C * LD];
+  __shared__ __align__(16) float sB1[C * LC];  // T, then dL
+  __shared__ __align__(16) float sB2[C * LC];  // dT, then Z = dT T^T, then G, then dL o Gamma o KK
+  __shared__ __align__(16) float sB3[C * LC];  // P o Gamma, then Gbar o Gamma
+  __shared__ __align__(16) float sg[C], sb[C], sbeta[C], sdg[C];
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int kh = h / p.r, n = ci.len;
   const size_t ch = ch_idx(p, c, h);
   const size_t cd = ch * C * D, cc = ch * C * C;
-  load_tile<C, C>(sB1, LC, p.Tm + cc, C, C);
-  load_tile<C, C>(sB2, LC, p.dT + cc, C, C);
+  load_tile<C, C, LC>(sB1, p.Tm + cc, C, C);
+  load_tile<C, C, LC>(sB2, p.dT + cc, C, C);
   for (int i = threadIdx.x; i < C; i += NTHREADS) {
     sg[i] = p.gam[ch * C + i];
     sbeta[i] = i < n ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
@@ -362,7 +339,7 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2b(Prob p) {
   {
     Acc<C, C> z;
     z.zero();
-    mma<P, C, C, C>(z, rows(sB2, LC), cols(sB1, LC));
+    mma<P, C, C, C>(z, rows<LC>(sB2), cols<LC>(sB1));
     __syncthreads();
     for_each(z, [&](int i, int j, float x) { sB2[i * LC + j] = x; });
   }
@@ -370,7 +347,7 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2b(Prob p) {
   {
     Acc<C, C> dl;
     dl.zero();
-    mma<P, C, C, C>(dl, cols(sB1, LC), rows(sB2, LC));
+    mma<P, C, C, C>(dl, cols<LC>(sB1), rows<LC>(sB2));
     __syncthreads();
     for_each(dl, [&](int i, int j, float x) { sB1[i * LC + j] = i > j ? -x : 0.f; });
   }
@@ -381,15 +358,15 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2b(Prob p) {
     sB2[i * LC + j] = sB1[i * LC + j] * sbeta[i] * G;
     sB3[i * LC + j] = p.Pb[cc + idx] * G;
   }
-  load_tile<C, D>(sQ, LD, (const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n);
-  load_tile<C, D>(sK, LD, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
+  load_tile<C, D, LD>(sQ, (const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n);
+  load_tile<C, D, LD>(sK, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
   __syncthreads();
   {
     Acc<C, D> a;
     a.zero();
-    mma<P, C, D, C>(a, cols(sB3, LC), rows(sQ, LD));
-    mma<P, C, D, C>(a, rows(sB2, LC), rows(sK, LD));
-    mma<P, C, D, C>(a, cols(sB2, LC), rows(sK, LD));
+    mma<P, C, D, C>(a, cols<LC>(sB3), rows<LD>(sQ));
+    mma<P, C, D, C>(a, rows<LC>(sB2), rows<LD>(sK));
+    mma<P, C, D, C>(a, cols<LC>(sB2), rows<LD>(sK));
     for_each(a, [&](int i, int j, float x) {
       p.dkh[cd + i * D + j] = x + p.XK[cd + i * D + j] + sbeta[i] * sb[i] * p.dKbb[cd + i * D + j];
     });
@@ -397,8 +374,8 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_grad2b(Prob p) {
   Acc<C, C> qk, kk;
   qk.zero();
   kk.zero();
-  mma<P, C, C, D>(qk, rows(sQ, LD), cols(sK, LD));
-  mma<P, C, C, D>(kk, rows(sK, LD), cols(sK, LD));
+  mma<P, C, C, D>(qk, rows<LD>(sQ), cols<LD>(sK));
+  mma<P, C, C, D>(kk, rows<LD>(sK), cols<LD>(sK));
   __syncthreads();
   for_each2(qk, kk, [&](int i, int j, float xq, float xk) {
     float gb = 0.f, dbt = 0.f;
@@ -470,17 +447,17 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_fold(Prob p) {
 template <typename TI, int C, int D>
 static hipError_t bwd_seq(const Prob& p, hipStream_t s) {
   constexpr int BV = BwdCfg<D>::BV, BG = BwdCfg<D>::BG;
-  k_table<C><<<1, NTHREADS, 0, s>>>(p);
+  traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
   if (p.nc_max > 0) {
-    k_wy<TI, C, D><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p);
-    k_bwd_intra<TI, C, D, BV><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p);
+    traced("k_wy", s, [&] { k_wy<TI, C, D><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p); });
+    traced("k_bwd_intra", s, [&] { k_bwd_intra<TI, C, D, BV><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p); });
   }
-  if (p.N > 0) k_bwd_state<TI, C, D, BV><<<dim3(p.N, p.Hv, D / BV), NTHREADS, 0, s>>>(p);
+  if (p.N > 0) traced("k_bwd_state", s, [&] { k_bwd_state<TI, C, D, BV><<<dim3(p.N, p.Hv, D / BV), NTHREADS, 0, s>>>(p); });
   if (p.nc_max > 0) {
-    k_bwd_grad1<TI, C, D, BG><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p);
-    k_bwd_grad2a<TI, C, D><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p);
-    k_bwd_grad2b<TI, C, D><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p);
-    k_bwd_fold<TI, C, D><<<dim3(p.nc_max, p.Hk), NTHREADS, 0, s>>>(p);
+    traced("k_bwd_grad1", s, [&] { k_bwd_grad1<TI, C, D, BG><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p); });
+    traced("k_bwd_grad2a", s, [&] { k_bwd_grad2a<TI, C, D><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p); });
+    traced("k_bwd_grad2b", s, [&] { k_bwd_grad2b<TI, C, D><<<dim3(p.nc_max, p.Hv), NTHREADS, 0, s>>>(p); });
+    traced("k_bwd_fold", s, [&] { k_bwd_fold<TI, C, D><<<dim3(p.nc_max, p.Hk), NTHREADS, 0, s>>>(p); });
   }
   return hipGetLastError();
 }

@@ -18,7 +18,7 @@ namespace gdn {
 
 // Operand precision of the MFMA products for each storage type.
 template <typename TI> struct PrecOf { static constexpr Prec value = Prec::F32; };
-template <> struct PrecOf<__bf16> { static constexpr Prec value = Prec::F32; };
+template <> struct PrecOf<__bf16> { static constexpr Prec value = Prec::BF16; };
 
 __device__ __forceinline__ size_t ch_idx(const Prob& p, int c, int h) { return (size_t)c * p.Hv + h; }
 
@@ -86,17 +86,17 @@ template <typename TI, int C, int D>
 __global__ __launch_bounds__(NTHREADS) void k_wy(Prob p) {
   constexpr Prec P = PrecOf<TI>::value;
   constexpr int LD = D + 4, LC = C + 4;
-  __shared__ float sK[C * LD];  // K, then V
-  __shared__ float sA[C * LC];  // L, then T diag(beta b), then T diag(beta)
-  __shared__ float sT[C * LC];
-  __shared__ float sg[C], sb[C], sbeta[C];
+  __shared__ __align__(16) float sK[C * LD];  // K, then V
+  __shared__ __align__(16) float sA[C * LC];  // L, then T diag(beta b), then T diag(beta)
+  __shared__ __align__(16) float sT[C * LC];
+  __shared__ __align__(16) float sg[C], sb[C], sbeta[C];
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int kh = h / p.r, n = ci.len;
   const size_t ch = ch_idx(p, c, h);
 
-  load_tile<C, D>(sK, LD, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
+  load_tile<C, D, LD>(sK, (const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
   for (int i = threadIdx.x; i < C; i += NTHREADS) {
     const bool ok = i < n;
     sbeta[i] = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NTHREADS) void k_wy(Prob p) {
   {
     Acc<C, C> a;
     a.zero();
-    mma<P, C, C, D>(a, rows(sK, LD), cols(sK, LD));
+    mma<P, C, C, D>(a, rows<LD>(sK), cols<LD>(sK));
     for_each(a, [&](int i, int j, float x) {
       sA[i * LC + j] = i > j ? sbeta[i] * expf(sg[i] - sg[j]) * x : 0.f;
     });
@@ -139,11 +139,11 @@ __global__ __launch_bounds__(NTHREADS) void k_wy(Prob p) {
   {
     Acc<C, D> w;
     w.zero();
-    mma<P, C, D, C>(w, rows(sA, LC), rows(sK, LD));
+    mma<P, C, D, C>(w, rows<LC>(sA), rows<LD>(sK));
     for_each(w, [&](int i, int j, float x) { p.W[ch * C * D + i * D + j] = x; });
   }
   __syncthreads();
-  load_tile<C, D>(sK, LD, (const TI*)p.v + (int64_t)ci.t0 * p.v_rs + h * D, p.v_rs, n);
+  load_tile<C, D, LD>(sK, (const TI*)p.v + (int64_t)ci.t0 * p.v_rs + h * D, p.v_rs, n);
   for (int idx = threadIdx.x; idx < C * C; idx += NTHREADS) {
     const int i = idx / C, j = idx % C;
     sA[i * LC + j] = sT[i * LC + j] * sbeta[j];
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(NTHREADS) void k_wy(Prob p) {
   {
     Acc<C, D> u;
     u.zero();
-    mma<P, C, D, C>(u, rows(sA, LC), rows(sK, LD));
+    mma<P, C, D, C>(u, rows<LC>(sA), rows<LD>(sK));
     for_each(u, [&](int i, int j, float x) { p.U[ch * C * D + i * D + j] = x; });
   }
 }

@@ -69,6 +69,20 @@ struct Prob {
   float* dkh;   // [c][h][C][D] per-value-head dk
 };
 
+// Benchmark tracing (gdn_trace.cpp): runs launch(ctx), bracketed by HIP events on s
+// while tracing is enabled.
+bool trace_on();
+void trace_launch(const char* name, hipStream_t s, void (*launch)(const void*), const void* ctx);
+
+template <class F>
+inline void traced(const char* name, hipStream_t s, const F& f) {
+  if (!trace_on()) {
+    f();
+    return;
+  }
+  trace_launch(name, s, [](const void* c) { (*static_cast<const F*>(c))(); }, &f);
+}
+
 // Kernel launch sequences (defined in gdn_fwd.hip / gdn_bwd.hip). Return a HIP error code.
 hipError_t launch_forward(const Prob& p, int dtype, hipStream_t s);
 hipError_t launch_backward(const Prob& p, int dtype, hipStream_t s);

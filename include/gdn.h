@@ -94,7 +94,8 @@ size_t gdn_chunk_state_bytes(const gdn_problem* p);
  * S_T (or NULL to skip) and chunk_states (required, gdn_chunk_state_bytes; keep it
  * unchanged for gdn_bwd).
  * Alignment: q, k, v, o and the row strides times the element size must be
- * multiples of 16 bytes; float32 arrays need 4-byte alignment.
+ * multiples of 16 bytes; S0, S_T, dS_T, dS0 need 16-byte alignment, g, beta, dg,
+ * dbeta 4-byte alignment (the same rules hold for gdn_bwd).
  */
 gdn_status gdn_fwd(const gdn_problem* p,
                    const void* q, int64_t q_rs, const void* k, int64_t k_rs,
@@ -118,6 +119,23 @@ gdn_status gdn_bwd(const gdn_problem* p,
                    void* dq, int64_t dq_rs, void* dk, int64_t dk_rs, void* dv, int64_t dv_rs,
                    float* dg, float* dbeta, float* dS0,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-kernel timing for benchmarks. While enabled (process-wide), every kernel that
+ * gdn_fwd / gdn_bwd enqueue is bracketed by two HIP events recorded on the call's
+ * stream (the events are created by the library on first use and reused; no device
+ * memory is allocated). gdn_trace_collect waits for the recorded events, returns up
+ * to max per-kernel totals (kernel name, summed elapsed milliseconds, launch count)
+ * and resets them. Names are static strings owned by the library. Returns the number
+ * of entries written.
+ */
+typedef struct {
+  const char* name;
+  double total_ms;
+  int64_t launches;
+} gdn_trace_entry;
+gdn_status gdn_trace_enable(int on);
+int gdn_trace_collect(gdn_trace_entry* out, int max);
 
 /* Static string for a status code. */
 const char* gdn_strerror(int status);
