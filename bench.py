@@ -28,19 +28,20 @@ PEAK = {"f32_mfma": 157.3e12, "bf16_mfma": 2.5e15, "hbm": 8.0e12}
 
 
 def kernel_work(name, C, D, Hk, Hv, n_chunks):
-    """Algorithmic MFMA flops of one launch (sum over its units) for the kernels of
-    the chunked path; the per-unit counts are the products each kernel forms, per
-    (chunk, value head)."""
+    """Algorithmic MFMA flops of one launch: the products each kernel forms, per
+    (chunk, value head), times chunks x value heads."""
+    r = Hv // Hk
     units = n_chunks * Hv
     per_unit = {
-        "k_wy": 6 * C * C * D,                          # K K^T, W, U
-        "k_fwd_state": 4 * C * D * D,                   # W S, K~^T Delta
-        "k_fwd_out": 4 * C * C * D + 2 * C * D * D,     # Q K^T, M Delta; Q S
-        "k_bwd_intra": 4 * C * C * D + 2 * C * D * D,   # Q K^T, M^T dO~; W S
-        "k_bwd_state": 6 * C * D * D,                   # K~ dS, Q^T dO~, W^T dDelta
-        "k_bwd_grad1": 6 * C * D * D + 6 * C * C * D,   # XQ, XW, XK; P, dT1, T^T dDelta
-        "k_bwd_grad2a": 6 * C * C * D,                  # (P o Gamma) K, T^T XW, XW K^T
-        "k_bwd_grad2b": 4 * C * C * C + 10 * C * C * D,  # dT T^T, T^T Z; 3 for dK; Q K^T, K K^T
+        # K K^T and Q K^T once per key head; W, U per value head
+        "k_prep": 4 * C * C * D // r + 4 * C * C * D,
+        # W S, Q S, K^T (e o Delta); M Delta
+        "k_sweep": 6 * C * D * D + 2 * C * C * D,
+        # K dS, (bQ)^T dO~, W^T dDelta; M^T dO~
+        "k_bwd_sweep": 6 * C * D * D + 2 * C * C * D,
+        # XQ, XW, XK, K dS; P, dT1, T^T dDelta, (P o Gamma) K, T^T XW, XW K^T, three for dK;
+        # dT T^T, T^T Z; K K^T once per key head
+        "k_bwd_grad": 8 * C * D * D + 18 * C * C * D + 4 * C * C * C + 2 * C * C * D // r,
     }.get(name)
     return None if per_unit is None else per_unit * units
 

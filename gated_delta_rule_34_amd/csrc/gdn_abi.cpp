@@ -35,6 +35,7 @@ gdn_status check_problem(const gdn_problem* p) {
   if (p->Dk != p->Dv) return GDN_EUNSUPPORTED;
   if (p->Dk != 16 && p->Dk != 32 && p->Dk != 64 && p->Dk != 128) return GDN_EUNSUPPORTED;
   if (p->chunk != 16 && p->chunk != 64) return GDN_EUNSUPPORTED;
+  if (p->dtype == GDN_F32 && p->chunk == 64 && p->Dk > 32) return GDN_EUNSUPPORTED;  // LDS budget
   if (!std::isfinite(p->scale)) return GDN_EINVAL;
   if (!p->cu_seqlens) {
     if (p->T < 0 || (int64_t)p->N * p->T != p->T_total) return GDN_EINVAL;
@@ -47,34 +48,59 @@ gdn_status check_problem(const gdn_problem* p) {
   return GDN_OK;
 }
 
-// Region sizes in bytes, in the order they are carved out of the workspace.
+// Region sizes in bytes (each rounded up to 256 B).
 struct Regions {
-  size_t chunks, seq_chunk, cvec, ccmat, cdmat, ddmat, scal;
+  size_t chunks, seq_chunk;      // chunk table
+  size_t oS, oW, oM, oKt, gam;   // [c][h][D][D], [c][h][C][D], [c][h][C][C], [c][kh][D][C], [c][h][C] f32
 };
 
 Regions regions(const gdn_problem* p) {
   const size_t nc = (size_t)chunk_bound(p), Hv = (size_t)p->Hv, C = (size_t)p->chunk, D = (size_t)p->Dk;
+  const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
   Regions r;
   r.chunks = align_up(nc * sizeof(gdn::ChunkInfo));
   r.seq_chunk = align_up(((size_t)p->N + 1) * sizeof(int));
-  r.cvec = align_up(nc * Hv * C * sizeof(float));
-  r.ccmat = align_up(nc * Hv * C * C * sizeof(float));
-  r.cdmat = align_up(nc * Hv * C * D * sizeof(float));
-  r.ddmat = align_up(nc * Hv * D * D * sizeof(float));
-  r.scal = align_up(nc * Hv * sizeof(float));
+  r.oS = align_up(nc * Hv * D * D * es);
+  r.oW = align_up(nc * Hv * C * D * es);
+  r.oM = align_up(nc * Hv * C * C * es);
+  r.oKt = align_up(nc * (size_t)p->Hk * D * C * es);
+  r.gam = align_up(nc * Hv * C * sizeof(float));
   return r;
 }
 
 size_t fwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.cvec + r.ccmat + 2 * r.cdmat;
+  return r.chunks + r.seq_chunk + r.oW;  // table, U^T
 }
 
 size_t bwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  // table, gam, Tm, W, U, dDi, dDel, dstates, XQ, XW, XK, Pb, dT, ebar, rq, rho, db1, sdot,
-  // dKbb, dqh, dkh
-  return r.chunks + r.seq_chunk + 5 * r.cvec + 3 * r.ccmat + 10 * r.cdmat + r.ddmat + r.scal;
+  return r.chunks + r.seq_chunk + r.oS + r.oW;  // table, dS per chunk, dDelta^T
+}
+
+// Saved activations: S, W, Delta^T, (diag(b) Q)^T, M, T, gamma, K^T.
+size_t saved_bytes(const gdn_problem* p) {
+  const Regions r = regions(p);
+  return r.oS + 3 * r.oW + 2 * r.oM + r.gam + r.oKt;
+}
+
+void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
+  char* b = static_cast<char*>(saved);
+  P.sv_S = b;
+  b += r.oS;
+  P.sv_W = b;
+  b += r.oW;
+  P.sv_Dl = b;
+  b += r.oW;
+  P.sv_Qbt = b;
+  b += r.oW;
+  P.sv_M = b;
+  b += r.oM;
+  P.sv_T = b;
+  b += r.oM;
+  P.sv_gam = reinterpret_cast<float*>(b);
+  b += r.gam;
+  P.sv_Kt = b;
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -102,7 +128,7 @@ struct Carver {
   char* base;
   size_t off = 0;
   template <typename T> T* take(size_t bytes) {
-    T* r = reinterpret_cast<T*>(base + off);
+    T* r = reinterpret_cast<T*>(reinterpret_cast<void*>(base + off));
     off += bytes;
     return r;
   }
@@ -131,9 +157,7 @@ size_t gdn_fwd_workspace_bytes(const gdn_problem* p) { return check_problem(p) =
 
 size_t gdn_bwd_workspace_bytes(const gdn_problem* p) { return check_problem(p) == GDN_OK ? bwd_ws(p) : 0; }
 
-size_t gdn_chunk_state_bytes(const gdn_problem* p) {
-  return check_problem(p) == GDN_OK ? regions(p).ddmat : 0;
-}
+size_t gdn_chunk_state_bytes(const gdn_problem* p) { return check_problem(p) == GDN_OK ? saved_bytes(p) : 0; }
 
 gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,
                    const void* v, int64_t v_rs, const float* g, const float* beta, const float* S0, void* o,
@@ -163,15 +187,12 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.q = q; P.q_rs = q_rs; P.k = k; P.k_rs = k_rs; P.v = v; P.v_rs = v_rs;
   P.g = g; P.beta = beta; P.S0 = S0;
   P.o = o; P.o_rs = o_rs; P.ST = S_T;
-  P.states = static_cast<float*>(chunk_states);
   const Regions r = regions(p);
+  carve_saved(P, r, chunk_states);
   Carver cv{static_cast<char*>(workspace)};
   P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
   P.seq_chunk = cv.take<int>(r.seq_chunk);
-  P.gam = cv.take<float>(r.cvec);
-  P.Tm = cv.take<float>(r.ccmat);
-  P.W = cv.take<float>(r.cdmat);
-  P.U = cv.take<float>(r.cdmat);
+  P.ws_Ut = cv.take<void>(r.oW);
   const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
@@ -210,34 +231,16 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   fill_common(P, p);
   P.q = q; P.q_rs = q_rs; P.k = k; P.k_rs = k_rs; P.v = v; P.v_rs = v_rs;
   P.g = g; P.beta = beta; P.S0 = S0;
-  P.states = const_cast<float*>(static_cast<const float*>(chunk_states));
   P.dO = dO; P.dO_rs = dO_rs; P.dST = dS_T;
   P.dq = dq; P.dq_rs = dq_rs; P.dk = dk; P.dk_rs = dk_rs; P.dv = dv; P.dv_rs = dv_rs;
   P.dg = dg; P.dbeta = dbeta; P.dS0 = dS0;
   const Regions r = regions(p);
+  carve_saved(P, r, const_cast<void*>(chunk_states));
   Carver cv{static_cast<char*>(workspace)};
   P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
   P.seq_chunk = cv.take<int>(r.seq_chunk);
-  P.gam = cv.take<float>(r.cvec);
-  P.ebar = cv.take<float>(r.cvec);
-  P.rq = cv.take<float>(r.cvec);
-  P.rho = cv.take<float>(r.cvec);
-  P.db1 = cv.take<float>(r.cvec);
-  P.Tm = cv.take<float>(r.ccmat);
-  P.Pb = cv.take<float>(r.ccmat);
-  P.dT = cv.take<float>(r.ccmat);
-  P.W = cv.take<float>(r.cdmat);
-  P.U = cv.take<float>(r.cdmat);
-  P.dDi = cv.take<float>(r.cdmat);
-  P.dDel = cv.take<float>(r.cdmat);
-  P.XQ = cv.take<float>(r.cdmat);
-  P.XW = cv.take<float>(r.cdmat);
-  P.XK = cv.take<float>(r.cdmat);
-  P.dKbb = cv.take<float>(r.cdmat);
-  P.dqh = cv.take<float>(r.cdmat);
-  P.dkh = cv.take<float>(r.cdmat);
-  P.dstates = cv.take<float>(r.ddmat);
-  P.sdot = cv.take<float>(r.scal);
+  P.ws_dS = cv.take<void>(r.oS);
+  P.ws_dDt = cv.take<void>(r.oW);
   const hipError_t e = gdn::launch_backward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }

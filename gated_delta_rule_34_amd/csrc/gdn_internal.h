@@ -13,9 +13,8 @@ struct ChunkInfo {
   int pad;
 };
 
-// Everything a kernel needs, passed by value. Dk == Dv == D.
-// Per-(chunk, value head) workspace arrays are indexed [c][h][...] with
-// c < nc_max; the layout of each is given next to its pointer.
+// Everything a kernel needs, passed by value. Dk == Dv == D. Per-(chunk, head)
+// arrays are indexed [c][h][...] with c < nc_max (the chunk table's numbering).
 struct Prob {
   int N, Hk, Hv, r, D, C, nc_max, T;  // T: tokens per sequence when cu == nullptr
   int64_t T_total;
@@ -30,8 +29,7 @@ struct Prob {
   const float* S0;    // [N][Hv][D][D] or nullptr
 
   void* o; int64_t o_rs;
-  float* ST;      // [N][Hv][D][D] or nullptr
-  float* states;  // [nc_max][Hv][D][D]: state at the start of every chunk
+  float* ST;  // [N][Hv][D][D] or nullptr
 
   const void* dO; int64_t dO_rs;
   const float* dST;  // or nullptr
@@ -46,27 +44,21 @@ struct Prob {
   ChunkInfo* chunks;  // [nc_max]
   int* seq_chunk;     // [N + 1] first chunk of each sequence
 
-  // workspace
-  float* gam;   // [c][h][C]    within-chunk cumulative log decay
-  float* Tm;    // [c][h][C][C] (I + L)^-1
-  float* W;     // [c][h][C][D]
-  float* U;     // [c][h][C][D] U, overwritten by Delta = U - W S0
-  float* dDi;   // [c][h][C][D] intra-chunk part of dDelta
-  float* dDel;  // [c][h][C][D] dDelta
-  float* dstates;  // [c][h][D][D] state adjoint at the end of every chunk
-  float* XQ;    // [c][h][C][D] dO~ S0^T
-  float* XW;    // [c][h][C][D] dDelta S0^T
-  float* XK;    // [c][h][C][D] (e * Delta) dS^T
-  float* Pb;    // [c][h][C][C] tril(dO~ Delta^T)
-  float* dT;    // [c][h][C][C] dT (first its dU part)
-  float* ebar;  // [c][h][C]
-  float* rq;    // [c][h][C] rowsum(Q * XQ)
-  float* rho;   // [c][h][C]
-  float* db1;   // [c][h][C]
-  float* sdot;  // [c][h]
-  float* dKbb;  // [c][h][C][D]
-  float* dqh;   // [c][h][C][D] per-value-head dq
-  float* dkh;   // [c][h][C][D] per-value-head dk
+  // Saved activations written by the forward for the backward (element type = the
+  // problem's storage type OT unless noted), per chunk c and value head h / key head kh:
+  void* sv_S;    // [c][h][D][D]  state at the start of the chunk, value-major: S^T[v][d]
+  void* sv_W;    // [c][h][C][D]  W, row-major
+  void* sv_Dl;   // [c][h][D][C]  Delta^T
+  void* sv_M;    // [c][h][C][C]  Gamma o Q K^T (lower incl. diagonal), row-major
+  void* sv_T;    // [c][h][C][C]  (I + L)^-1, row-major
+  float* sv_gam; // [c][h][C]     float32
+  void* sv_Kt;   // [c][kh][D][C] K^T
+  void* sv_Qbt;  // [c][h][D][C]  (diag(b) Q)^T
+  // forward workspace
+  void* ws_Ut;   // [c][h][D][C]  U^T
+  // backward workspace
+  void* ws_dS;   // [c][h][D][D]  state adjoint at the end of the chunk, value-major
+  void* ws_dDt;  // [c][h][D][C]  dDelta^T
 };
 
 // Benchmark tracing (gdn_trace.cpp): runs launch(ctx), bracketed by HIP events on s

@@ -117,6 +117,7 @@ def test_rejects_bad_problems(G):
     assert status_of(G, prob(G, D=96)) == G.GDN_EUNSUPPORTED
     assert status_of(G, prob(G, chunk=32)) == G.GDN_EUNSUPPORTED
     assert status_of(G, prob(G, dtype=5)) == G.GDN_EUNSUPPORTED
+    assert status_of(G, prob(G, dtype="f32", D=64)) == G.GDN_EUNSUPPORTED  # f32 + chunk 64 needs D <= 32
     assert status_of(G, prob(G, T_total=255)) == G.GDN_EINVAL  # != N * T
     p = prob(G)
     p.Dv = 64
