@@ -75,13 +75,13 @@ size_t fwd_ws(const gdn_problem* p) {
 
 size_t bwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.oS + r.oW;  // table, dS per chunk, dDelta^T
+  return r.chunks + r.seq_chunk + r.oS + 2 * r.oW;  // table, dS per chunk, dDelta, dDelta^T
 }
 
-// Saved activations: S, W, Delta^T, (diag(b) Q)^T, M, T, gamma, K^T.
+// Saved activations: S, W, Delta, (diag(b) Q)^T, M, T, T^T, gamma, K^T, Q^T.
 size_t saved_bytes(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.oS + 3 * r.oW + 2 * r.oM + r.gam + r.oKt;
+  return r.oS + 3 * r.oW + 3 * r.oM + r.gam + 2 * r.oKt;
 }
 
 void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
@@ -98,9 +98,13 @@ void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
   b += r.oM;
   P.sv_T = b;
   b += r.oM;
+  P.sv_Tt = b;
+  b += r.oM;
   P.sv_gam = reinterpret_cast<float*>(b);
   b += r.gam;
   P.sv_Kt = b;
+  b += r.oKt;
+  P.sv_Qt = b;
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -240,6 +244,7 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
   P.seq_chunk = cv.take<int>(r.seq_chunk);
   P.ws_dS = cv.take<void>(r.oS);
+  P.ws_dD = cv.take<void>(r.oW);
   P.ws_dDt = cv.take<void>(r.oW);
   const hipError_t e = gdn::launch_backward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;

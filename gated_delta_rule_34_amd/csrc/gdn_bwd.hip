@@ -8,76 +8,94 @@
 //   dS_0   = b_n dS_C + (diag(b) Q)^T dO~ - W^T dDelta    (carried to the previous chunk)
 //   XQ = dO~ S0^T,  XW = dDelta S0^T,  XK = Delta dS_C^T,  P = tril(dO~ Delta^T)
 //   dQ     = diag(b) XQ + (P o Gamma) K
-//   dV     = diag(beta) T^T dDelta;  dK_beta_b = -T^T XW
+//   dV     = diag(beta) T^T dDelta;  dK_beta_b = -T^T XW = -(T^T dDelta) S0^T
 //   dT     = dDelta (diag(beta) V)^T - XW (diag(beta b) K)^T;  dL = strictly_lower(-T^T dT T^T)
 //   dK     = (P o Gamma)^T Q + diag(e) XK + diag(beta b) dK_beta_b + G K + G^T K,
 //            G = dL o (beta_i Gamma_ij)
 //   dbeta  = rowsum(dV / beta o V) + b o rho + rowsum(dL o Gamma o K K^T),
-//            rho = rowsum(dK_beta_b o K)
+//            rho = rowsum(dK_beta_b o K) = -colsum(T o (XW K^T))
 //   dgamma = b o rowsum(Q o XQ) + beta b rho - ebar + rowsum(Gbar o Gamma) - colsum(Gbar o Gamma),
-//            ebar = e o rowsum((K dS_C) o Delta), Gbar o Gamma = P o M + dL o beta_i K K^T o Gamma,
+//            ebar = e o rowsum(K o XK), Gbar o Gamma = P o M + dL o beta_i K K^T o Gamma,
 //            and the last valid row also gets b_n <S0, dS_C> + sum(ebar)
 //   dlog g = reverse cumulative sum of dgamma within the chunk;  dg = dlog g / g.
 //
 // Kernels after the chunk table:
-//  k_bwd_sweep (sequence x value head, 8 waves): the reverse chunk-serial pass; the
-//      adjoint lives in float32 MFMA accumulators; saves dS_C and dDelta per chunk.
-//  k_bwd_grad  (chunk x key head, 8 waves): all remaining gradients for the r value
-//      heads of the key head, one head after the other. dq and dk of the key head are
-//      summed over its value heads in ascending order in registers and stored once:
-//      no atomics anywhere, every run is bit-identical. Row sums go through per-wave
-//      partial arrays added in a fixed order.
+//  k_bwd_sweep (sequence x value head, 16 waves): the reverse chunk-serial pass; the
+//      adjoint lives in float32 MFMA accumulators; saves dS_C, dDelta and dDelta^T.
+//  k_bwd_grad  (chunk x key head, 16 waves): all remaining gradients for the r value
+//      heads of the key head, one head after the other. Every operand arrives in the
+//      layout its product reads (no transposes while staging). dq and dk of the key
+//      head are summed over its value heads in ascending order in registers and stored
+//      once: no atomics, every run is bit-identical. Row sums go through partial arrays
+//      indexed by tile column block and are added in a fixed order.
 #include "gdn_common.h"
 #include "gdn_mma.h"
 
 namespace gdn {
 
-constexpr int kWavesB = 8;
+constexpr int kWavesB = 16;
+constexpr int kWavesG = 8;  // k_bwd_grad
+constexpr int kThreadsG = kWavesG * 64;
 constexpr int kThreadsB = kWavesB * 64;
 
 __host__ __device__ constexpr int bblk2(int x) { return x >= 32 ? 2 : 1; }
 
-template <int R, int Cn, int LD, int NT, typename OT>
-__device__ __forceinline__ void lds_rows_to_global(OT* __restrict__ dst, const OT* src) {
-  using V = Vec16<OT>;
-  constexpr int VPR = Cn / V::N;
-  for (int idx = threadIdx.x; idx < R * VPR; idx += NT) {
-    const int r = idx / VPR, c = (idx % VPR) * V::N;
-    *reinterpret_cast<typename V::type*>(dst + (size_t)r * Cn + c) =
-        *reinterpret_cast<const typename V::type*>(src + r * LD + c);
+// Row sums of f(i, j, x) over an accumulator tile, added into red[column block][M].
+// Each (row block, column block) belongs to one wave, so no two waves touch the same
+// entry; the caller adds the column-block partials in order after a barrier.
+template <int M, int N, int TM, int TN, int NWV, class F>
+__device__ __forceinline__ void acc_rowsum(Tile<M, N, TM, TN, NWV>& t, F&& f, float* red) {
+  using B = Blk<M, N, TM, TN, NWV>;
+  const int w = threadIdx.x / 64, l = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < B::PER; ++q) {
+    const int b = w + q * NWV;
+    if (b < B::NB) {
+      const int cb = b % B::BN, bi = (b / B::BN) * 16 * TM, bj = cb * 16 * TN;
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y) {
+          const int i0 = bi + x * 16 + (l >> 4) * 4, j = bj + y * 16 + (l & 15);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = f(i0 + e, j, t.a[q][x][y][e]);
+#pragma unroll
+          for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], m);
+          if ((l & 15) == 0)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[cb * M + i0 + e] += v[e];
+        }
+    }
   }
 }
 
-// Row sums of f(i, j, x) over the elements of an accumulator tile, added into the
-// per-wave partial array red[wave][M] (no barrier; the caller sums the NWV partials
-// in wave order after a barrier).
-template <int M, int N, int TM, int TN, int NWV, class F>
-__device__ __forceinline__ void acc_rowsum(Tile<M, N, TM, TN, NWV>& t, F&& f, float* red) {
-  const int w = threadIdx.x / 64, l = threadIdx.x & 63;
-  t.each4([&](int i0, int j, f32x4& x) {
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = f(i0 + e, j, x[e]);
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], m);
-    if ((l & 15) == 0)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[w * M + i0 + e] += v[e];
-  });
-}
-
-// Column sums, same conventions (red[wave][N]).
+// Column sums, added into red[row block][N].
 template <int M, int N, int TM, int TN, int NWV, class F>
 __device__ __forceinline__ void acc_colsum(Tile<M, N, TM, TN, NWV>& t, F&& f, float* red) {
+  using B = Blk<M, N, TM, TN, NWV>;
   const int w = threadIdx.x / 64, l = threadIdx.x & 63;
-  t.each4([&](int i0, int j, f32x4& x) {
-    float v = f(i0, j, x[0]) + f(i0 + 1, j, x[1]) + f(i0 + 2, j, x[2]) + f(i0 + 3, j, x[3]);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    if (l < 16) red[w * N + j] += v;
-  });
+#pragma unroll
+  for (int q = 0; q < B::PER; ++q) {
+    const int b = w + q * NWV;
+    if (b < B::NB) {
+      const int rb = b / B::BN, bi = rb * 16 * TM, bj = (b % B::BN) * 16 * TN;
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y) {
+          const int i0 = bi + x * 16 + (l >> 4) * 4, j = bj + y * 16 + (l & 15);
+          float v = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v += f(i0 + e, j, t.a[q][x][y][e]);
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (l < 16) red[rb * N + j] += v;
+        }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------- sweep
@@ -85,7 +103,7 @@ __device__ __forceinline__ void acc_colsum(Tile<M, N, TM, TN, NWV>& t, F&& f, fl
 template <typename TI, int C, int D>
 __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
   using OT = TI;
-  constexpr int NT = kThreadsB, LDO = D + 8, LCO = C + 8;
+  constexpr int NT = kThreadsB, NWV = kWavesB, LDO = D + 8, LCO = C + 8;
   constexpr int SM = bblk2(D), DN = bblk2(D);
   __shared__ __align__(16) OT sMt[C * LCO];   // M^T
   __shared__ __align__(16) OT sOt[D * LCO];   // dO~^T
@@ -100,8 +118,8 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
   const int n = blockIdx.x, h = blockIdx.y, kh = h / p.r;
   const size_t nh = (size_t)n * p.Hv + h;
   const int c0 = p.seq_chunk[n], c1 = p.seq_chunk[n + 1];
-  using TS = Tile<D, D, SM, SM, kWavesB>;
-  using TD = Tile<C, D, 1, DN, kWavesB>;
+  using TS = Tile<D, D, SM, SM, NWV>;
+  using TD = Tile<C, D, 1, DN, NWV>;
   TS dS;
   if (p.dST) {
     const float* s = p.dST + nh * D * D;
@@ -128,8 +146,8 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
   auto commit = [&]() {
     nM.template to_cols<LCO>(sMt);
     nO.template to_cols<LCO>(sOt, nullptr, p.scale);
-    nK.template to_rows<LDO>(sK);
-    nQb.template to_rows<LCO>(sQbt);
+    nK.template to_rows_raw<LDO>(sK);
+    nQb.template to_rows_raw<LCO>(sQbt);
     nW.template to_cols<LCO>(sWt, nullptr, -1.f);
     if (threadIdx.x < C) sg[threadIdx.x] = ng;
   };
@@ -147,24 +165,25 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
   __syncthreads();
   for (int c = c1 - 1; c >= c0; --c) {
     const size_t ch = ch_idx(p, c, h);
-    lds_rows_to_global<D, D, LDO, NT>((OT*)p.ws_dS + ch * D * D, sdSt);  // dS_C, value-major
+    lds_to_global_t<D, D, LDO, NT>((OT*)p.ws_dS + ch * D * D, sdSt);  // dS_C, key-major
     if (threadIdx.x < C) se[threadIdx.x] = expf(sg[C - 1] - sg[threadIdx.x]);
     const float bn = expf(sg[C - 1]);
     if (c - 1 >= c0) issue(c - 1);
     TD dD;
     dD.zero();
-    gemm_nt<OT, C, D, D, 1, DN, kWavesB, LDO, LDO>(dD, sK, sdSt);  // K dS
+    gemm_nt<OT, C, D, D, 1, DN, NWV, LDO, LDO>(dD, sK, sdSt);  // K dS
     dS.each([&](int, int, float& x) { x *= bn; });
-    gemm_nt<OT, D, D, C, SM, SM, kWavesB, LCO, LCO>(dS, sQbt, sOt);  // + (diag(b) Q)^T dO~
+    gemm_nt<OT, D, D, C, SM, SM, NWV, LCO, LCO>(dS, sQbt, sOt);  // + (diag(b) Q)^T dO~
     __syncthreads();  // se visible
     dD.each([&](int i, int, float& x) { x *= se[i]; });
-    gemm_nt<OT, C, D, C, 1, DN, kWavesB, LCO, LCO>(dD, sMt, sOt);  // + M^T dO~
+    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dD, sMt, sOt);  // + M^T dO~
     dD.each4([&](int i0, int v, f32x4& x) {
       *reinterpret_cast<o4*>(sdDt + v * LCO + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
     });
     __syncthreads();
-    gemm_nt<OT, D, D, C, SM, SM, kWavesB, LCO, LCO>(dS, sWt, sdDt);  // - W^T dDelta
-    lds_rows_to_global<D, C, LCO, NT>((OT*)p.ws_dDt + ch * D * C, sdDt);
+    gemm_nt<OT, D, D, C, SM, SM, NWV, LCO, LCO>(dS, sWt, sdDt);  // - W^T dDelta
+    lds_to_global<D, C, LCO, NT>((OT*)p.ws_dDt + ch * D * C, sdDt);
+    lds_to_global_t<D, C, LCO, NT>((OT*)p.ws_dD + ch * C * D, sdDt);
     __syncthreads();
     adj_to_lds();
     if (c - 1 >= c0) commit();
@@ -177,92 +196,143 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
 }
 
 // ---------------------------------------------------------------------------- grad
-// Row-vector slots of the per-wave partial sums in k_bwd_grad.
+// Row-vector slots of the partial sums in k_bwd_grad.
 enum { R_EBAR = 0, R_DB1, R_RQ, R_RHO, R_DB3, R_GROW, R_GCOL, R_NSLOT };
+constexpr int kRedBlocks = 4;  // column (row) blocks per partial-sum slot
 
 template <typename TI, int C, int D> struct GradCfg {
-  static constexpr int LDO = D + 8, LCO = C + 8, BV = D < 32 ? D : 32, LBO = BV + 8;
-  // phase 1 (one value-column block): S0 and dS_C key-major, dS_C value-major,
-  // dO, Delta, dDelta, V row blocks, dDelta^T
-  static constexpr int G1 = 2 * D * LBO + BV * LDO + 4 * C * LBO + BV * LCO;
-  // phase 2: XW^T (later Z^T), XW (later G), P o Gamma, its transpose, dT (later G^T)
-  static constexpr int G2 = D * LCO + C * LDO + 3 * C * LCO;
+  static constexpr int LDO = D + 8, LCO = C + 8;
+  static constexpr int BV = sizeof(TI) == 2 ? (D < 64 ? D : 64) : 16, LBO = BV + 8;
+  // phase 1 (one block of BV value columns): S0 and dS_C (key-major), dO, Delta,
+  // dDelta, V, -beta b o dVbeta (row-major), dDelta^T
+  static constexpr int G1 = 2 * D * LBO + 5 * C * LBO + BV * LCO;
+  // phase 2: XW rows, K^T, Q^T, dT (later G^T), Z^T (later G), P o Gamma, its transpose
+  static constexpr int G2 = C * LDO + 2 * D * LCO + 4 * C * LCO;
   static constexpr int GR = G1 > G2 ? G1 : G2;
 };
 
-// Grid (nc_max, Hk).
+// Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk.
+// Phase 1 streams blocks of value columns and accumulates
+//   XQ += dO S0^T    XW += dDelta S0^T    XK += Delta dS_C^T    dk += (-beta b o T^T dDelta) S0^T
+//   P += dO Delta^T  dT1 += dDelta V^T    (the scale of dO~ is applied afterwards)
+// plus dV = beta o T^T dDelta and the row sums of dVbeta o V and <S0, dS_C>. Phase 2
+// finishes dq, dT, dL, the rest of dk and the gate gradients.
 template <typename TI, int C, int D>
-__global__ __launch_bounds__(kThreadsB) void k_bwd_grad(Prob p) {
+__global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   using OT = TI;
   using CF = GradCfg<TI, C, D>;
-  constexpr int NT = kThreadsB, NWV = kWavesB, LDO = CF::LDO, LCO = CF::LCO;
+  constexpr int NT = kThreadsG, NWV = kWavesG, LDO = CF::LDO, LCO = CF::LCO;
   constexpr int BV = CF::BV, LBO = CF::LBO;
-  constexpr int DN = bblk2(D), BN = bblk2(BV);
+  constexpr int DN = bblk2(D);
+  constexpr int RS = kRedBlocks * C;  // floats per partial-sum slot
   typedef OT o4 __attribute__((ext_vector_type(4)));
 
-  __shared__ __align__(16) OT sK[C * LDO];   // K rows (shared by the value heads)
-  __shared__ __align__(16) OT sKt[D * LCO];  // K^T
-  __shared__ __align__(16) OT sQt[D * LCO];  // Q^T
-  __shared__ __align__(16) OT sT[C * LCO];   // T rows (per value head)
-  __shared__ __align__(16) OT sTt[C * LCO];  // T^T
+  using TCC = Tile<C, C, 1, 1, NWV>;
+  using TCD = Tile<C, D, 1, DN, NWV>;
+  using TCB = Tile<C, BV, 1, 1, NWV>;
+  static_assert(TCD::B::BN <= kRedBlocks && TCC::B::BN <= kRedBlocks && TCC::B::BM <= kRedBlocks &&
+                    TCB::B::BN <= kRedBlocks,
+                "partial-sum slots too small");
+
+  __shared__ __align__(16) OT sK[C * LDO];  // K rows
+  __shared__ __align__(16) OT sT[C * LCO];  // T rows
+  __shared__ __align__(16) OT sTt[C * LCO]; // T^T rows
   __shared__ __align__(16) OT sR[CF::GR];
-  __shared__ float red[R_NSLOT * NWV * C];
+  __shared__ float red[R_NSLOT * RS];
   __shared__ float rowv[R_NSLOT * C];
-  __shared__ float sg[C], sb[C], se[C], sbeta[C], sdg[C], sred[NT];
+  __shared__ float sg[C], sb[C], se[C], sbeta[C], swv[NWV];
 
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int n = ci.len;
+  const int w = threadIdx.x / 64, lane = threadIdx.x & 63;
+  const size_t ck = (size_t)c * p.Hk + kh;
+
+  // phase-1 buffers
+  OT* sS0k = sR;              // [D][LBO]  S0 block, key-major
+  OT* sdSk = sS0k + D * LBO;  // [D][LBO]  dS_C block, key-major
+  OT* sO = sdSk + D * LBO;    // [C][LBO]  dO
+  OT* sDl = sO + C * LBO;     // [C][LBO]  Delta
+  OT* sdD = sDl + C * LBO;    // [C][LBO]  dDelta
+  OT* sV = sdD + C * LBO;     // [C][LBO]  V
+  OT* sdVb = sV + C * LBO;    // [C][LBO]  -beta b o dVbeta
+  OT* sdDt = sdVb + C * LBO;  // [BV][LCO] dDelta^T
+  // phase-2 buffers
+  OT* sXW = sR;               // [C][LDO]
+  OT* sKt = sXW + C * LDO;    // [D][LCO]
+  OT* sQt = sKt + D * LCO;    // [D][LCO]
+  OT* sdT = sQt + D * LCO;    // [C][LCO]  dT, then G^T
+  OT* sZt = sdT + C * LCO;    // [C][LCO]  Z^T, then G
+  OT* sPG = sZt + C * LCO;    // [C][LCO]
+  OT* sPGt = sPG + C * LCO;   // [C][LCO]
+  OT* sGt = sdT;
+  OT* sG = sZt;
 
   {
-    Stage<C, D, NT, TI> gk, gq;
+    Stage<C, D, NT, TI> gk;
     gk.issue((const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
-    gq.issue((const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n);
-    gk.template to_rows<LDO>(sK);
-    gk.template to_cols<LCO>(sKt);
-    gq.template to_cols<LCO>(sQt);
+    gk.template to_rows_raw<LDO>(sK);
   }
-  __syncthreads();
-  using TCC = Tile<C, C, 1, 1, NWV>;
-  using TCD = Tile<C, D, 1, DN, NWV>;
-  using TCB = Tile<C, BV, 1, BN, NWV>;
-  TCC KK;
-  KK.zero();
-  gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(KK, sK, sK);
-  TCD dqf, dkf;  // dq, dk of the key head, summed over its value heads
+  TCD dqf, dkf;  // dq, dk of the key head, summed over its value heads in order
   dqf.zero();
   dkf.zero();
+  __syncthreads();
+
+  Stage<C, C, NT, OT> nT, nTt;
+  float ngam = 0.f, nbeta = 0.f;
+  auto issue_head = [&](int h) {
+    const size_t ch = ch_idx(p, c, h);
+    nT.issue((const OT*)p.sv_T + ch * C * C, C, C);
+    nTt.issue((const OT*)p.sv_Tt + ch * C * C, C, C);
+    if (threadIdx.x < C) {
+      ngam = p.sv_gam[ch * C + threadIdx.x];
+      nbeta = threadIdx.x < n ? p.beta[(int64_t)(ci.t0 + threadIdx.x) * p.Hv + h] : 0.f;
+    }
+  };
+  issue_head(kh * p.r);
 
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = kh * p.r + hh;
     const size_t ch = ch_idx(p, c, h);
-    // ---- per-head set-up
-    {
-      Stage<C, C, NT, OT> gt;
-      gt.issue((const OT*)p.sv_T + ch * C * C, C, C);
-      gt.template to_rows<LCO>(sT);
-      gt.template to_cols<LCO>(sTt);
+    const OT* S0k = (const OT*)p.sv_S + ch * D * D;
+    const OT* dSk = (const OT*)p.ws_dS + ch * D * D;
+    const OT* Dl = (const OT*)p.sv_Dl + ch * C * D;
+    const OT* dD = (const OT*)p.ws_dD + ch * C * D;
+    const OT* dDt = (const OT*)p.ws_dDt + ch * D * C;
+    const TI* dO = (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D;
+    const TI* V = (const TI*)p.v + (int64_t)ci.t0 * p.v_rs + h * D;
+    TI* dV = (TI*)p.dv + (int64_t)ci.t0 * p.dv_rs + h * D;
+
+    // ---- set-up: T, T^T, gates, M (in the accumulator layout), zeroed partial sums
+    nT.template to_rows_raw<LCO>(sT);
+    nTt.template to_rows_raw<LCO>(sTt);
+    if (threadIdx.x < C) {
+      sg[threadIdx.x] = ngam;
+      sbeta[threadIdx.x] = nbeta;
     }
-    for (int i = threadIdx.x; i < C; i += NT) {
-      sg[i] = p.sv_gam[ch * C + i];
-      sbeta[i] = i < n ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
-    }
-    for (int i = threadIdx.x; i < R_NSLOT * NWV * C; i += NT) red[i] = 0.f;
+    for (int i = threadIdx.x; i < R_NSLOT * RS; i += NT) red[i] = 0.f;
+    Stage<D, BV, NT, OT> gs, gd;
+    Stage<C, BV, NT, OT> gdl, gdd;
+    Stage<BV, C, NT, OT> gdt;
+    Stage<C, BV, NT, TI> go, gv;
+    auto issue_blk = [&](int v0) {
+      gs.issue(S0k + v0, D, D);
+      gd.issue(dSk + v0, D, D);
+      gdl.issue(Dl + v0, D, C);
+      gdd.issue(dD + v0, D, C);
+      gdt.issue(dDt + (size_t)v0 * C, C, BV);
+      go.issue(dO + v0, p.dO_rs, n);
+      gv.issue(V + v0, p.v_rs, n);
+    };
+    issue_blk(0);
     __syncthreads();
-    for (int i = threadIdx.x; i < C; i += NT) {
-      sb[i] = expf(sg[i]);
-      se[i] = expf(sg[C - 1] - sg[i]);
+    if (threadIdx.x < C) {
+      sb[threadIdx.x] = expf(sg[threadIdx.x]);
+      se[threadIdx.x] = expf(sg[C - 1] - sg[threadIdx.x]);
     }
-    // ---- phase 1: everything that needs S0 or dS_C, streamed over value-column blocks
-    OT* sS0k = sR;              // [D][LBO]  S0 block, key-major
-    OT* sdSk = sS0k + D * LBO;  // [D][LBO]  dS_C block, key-major
-    OT* sdSv = sdSk + D * LBO;  // [BV][LDO] dS_C block, value-major
-    OT* sO = sdSv + BV * LDO;   // [C][LBO]  dO (scale applied to the products)
-    OT* sDl = sO + C * LBO;     // [C][LBO]  Delta
-    OT* sdD = sDl + C * LBO;    // [C][LBO]  dDelta
-    OT* sV = sdD + C * LBO;     // [C][LBO]  V
-    OT* sdDt = sV + C * LBO;    // [BV][LCO] dDelta^T
+
+    // ---- phase 1
     TCD XQ, XW, XK;
     TCC PP, dT1;
     XQ.zero();
@@ -271,107 +341,71 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_grad(Prob p) {
     PP.zero();
     dT1.zero();
     float sdot = 0.f;
-    const OT* S0v = (const OT*)p.sv_S + ch * D * D;
-    const OT* dSv = (const OT*)p.ws_dS + ch * D * D;
-    const OT* Dlt = (const OT*)p.sv_Dl + ch * D * C;
-    const OT* dDt = (const OT*)p.ws_dDt + ch * D * C;
-    const TI* dO = (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D;
-    const TI* V = (const TI*)p.v + (int64_t)ci.t0 * p.v_rs + h * D;
-    TI* dV = (TI*)p.dv + (int64_t)ci.t0 * p.dv_rs + h * D;
     for (int v0 = 0; v0 < D; v0 += BV) {
-      {
-        Stage<BV, D, NT, OT> gs, gd;
-        Stage<BV, C, NT, OT> gdl, gdd;
-        Stage<C, BV, NT, TI> go, gv;
-        gs.issue(S0v + (size_t)v0 * D, D, BV);
-        gd.issue(dSv + (size_t)v0 * D, D, BV);
-        gdl.issue(Dlt + (size_t)v0 * C, C, BV);
-        gdd.issue(dDt + (size_t)v0 * C, C, BV);
-        go.issue(dO + v0, p.dO_rs, n);
-        gv.issue(V + v0, p.v_rs, n);
-        __syncthreads();  // the previous block's readers are done
-        gs.template to_cols<LBO>(sS0k);
-        gd.template to_cols<LBO>(sdSk);
-        gd.template to_rows<LDO>(sdSv);
-        gdl.template to_cols<LBO>(sDl);
-        gdd.template to_cols<LBO>(sdD);
-        gdd.template to_rows<LCO>(sdDt);
-        go.template to_rows<LBO>(sO);
-        gv.template to_rows<LBO>(sV);
-      }
+      gs.template to_rows_raw<LBO>(sS0k);
+      gd.template to_rows_raw<LBO>(sdSk);
+      gdl.template to_rows_raw<LBO>(sDl);
+      gdd.template to_rows_raw<LBO>(sdD);
+      gdt.template to_rows_raw<LCO>(sdDt);
+      go.template to_rows_raw<LBO>(sO);
+      gv.template to_rows_raw<LBO>(sV);
       __syncthreads();
-      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XQ, sO, sS0k);
-      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XW, sdD, sS0k);
-      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XK, sDl, sdSk);
-      gemm_nt<OT, C, C, BV, 1, 1, NWV, LBO, LBO>(PP, sO, sDl);
-      gemm_nt<OT, C, C, BV, 1, 1, NWV, LBO, LBO>(dT1, sdD, sV);
-      {
-        TCB kds;
-        kds.zero();
-        gemm_nt<OT, C, BV, D, 1, BN, NWV, LDO, LDO>(kds, sK, sdSv);
-        acc_rowsum(kds, [&](int i, int j, float x) { return se[i] * x * (float)sDl[i * LBO + j]; },
-                   red + R_EBAR * NWV * C);
-      }
+      if (v0 + BV < D) issue_blk(v0 + BV);
       {
         TCB dvb;
         dvb.zero();
-        gemm_nt<OT, C, BV, C, 1, BN, NWV, LCO, LCO>(dvb, sTt, sdDt);
+        gemm_nt<OT, C, BV, C, 1, 1, NWV, LCO, LCO>(dvb, sTt, sdDt);  // T^T dDelta
         dvb.each([&](int i, int j, float& x) {
           if (i < n) dV[(int64_t)i * p.dv_rs + v0 + j] = (TI)(sbeta[i] * x);
+          sdVb[i * LBO + j] = (OT)(-sbeta[i] * sb[i] * x);
         });
-        acc_rowsum(dvb, [&](int i, int j, float x) { return x * (float)sV[i * LBO + j]; },
-                   red + R_DB1 * NWV * C);
+        acc_rowsum(dvb, [&](int i, int j, float x) { return x * (float)sV[i * LBO + j]; }, red + R_DB1 * RS);
       }
       for (int idx = threadIdx.x; idx < D * BV; idx += NT) {
-        const int d = idx / BV, v = idx % BV;
-        sdot += (float)sS0k[d * LBO + v] * (float)sdSk[d * LBO + v];
+        const int d = idx / BV, vv = idx % BV;
+        sdot += (float)sS0k[d * LBO + vv] * (float)sdSk[d * LBO + vv];
       }
+      __syncthreads();  // sdVb visible
+      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XQ, sO, sS0k);
+      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XW, sdD, sS0k);
+      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XK, sDl, sdSk);
+      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(dkf, sdVb, sS0k);
+      gemm_nt<OT, C, C, BV, 1, 1, NWV, LBO, LBO>(PP, sO, sDl);
+      gemm_nt<OT, C, C, BV, 1, 1, NWV, LBO, LBO>(dT1, sdD, sV);
+      __syncthreads();  // block buffers free
     }
-    // dO~ = scale dO: XQ and P were formed with dO
-    const float sc = p.scale;
-    XQ.each([&](int, int, float& x) { x *= sc; });
-    PP.each([&](int i, int j, float& x) { x = i >= j ? x * sc : 0.f; });
-    XK.each([&](int i, int, float& x) { x *= se[i]; });
-    dT1.each([&](int, int j, float& x) { x *= sbeta[j]; });
-    __syncthreads();  // phase-1 buffers free
+    if (hh + 1 < p.r) issue_head(h + 1);
+
     // ---- phase 2
-    OT* sXWt = sR;               // [D][LCO]  XW^T; later Z^T
-    OT* sXW = sXWt + D * LCO;    // [C][LDO]  XW;   later G
-    OT* sPG = sXW + C * LDO;     // [C][LCO]  P o Gamma
-    OT* sPGt = sPG + C * LCO;    // [C][LCO]  (P o Gamma)^T
-    OT* sdT = sPGt + C * LCO;    // [C][LCO]  dT;   later G^T
-    OT* sZt = sXWt;
-    OT* sG = sXW;
-    OT* sGt = sdT;
-    XW.each4([&](int i0, int d, f32x4& x) {
-      *reinterpret_cast<o4*>(sXWt + d * LCO + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
-    });
+    {
+      Stage<D, C, NT, OT> gkt, gqt;
+      gkt.issue((const OT*)p.sv_Kt + ck * D * C, C, D);
+      gqt.issue((const OT*)p.sv_Qt + ck * D * C, C, D);
+      gkt.template to_rows_raw<LCO>(sKt);
+      gqt.template to_rows_raw<LCO>(sQt);
+    }
+    const float sc = p.scale;
     XW.each([&](int i, int d, float& x) { sXW[i * LDO + d] = (OT)x; });
     PP.each([&](int i, int j, float& x) {
+      x = i >= j ? x * sc : 0.f;
       const float pg = i >= j ? x * expf(sg[i] - sg[j]) : 0.f;
       sPG[i * LCO + j] = (OT)pg;
       sPGt[j * LCO + i] = (OT)pg;
     });
-    {
-      const TI* Q = (const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D;
-      acc_rowsum(XQ, [&](int i, int d, float x) { return i < n ? x * (float)Q[(int64_t)i * p.q_rs + d] : 0.f; },
-                 red + R_RQ * NWV * C);
-    }
-    XQ.each([&](int i, int, float& x) { x *= sb[i]; });
+    acc_rowsum(XK, [&](int i, int d, float x) { return se[i] * x * (float)sK[i * LDO + d]; }, red + R_EBAR * RS);
+    dkf.each_with(XK, [&](int i, int, float& a, float& x) { a += se[i] * x; });
     __syncthreads();
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(XQ, sPG, sKt);  // dQ of this head
-    dqf.each_with(XQ, [&](int, int, float& a, float& b) { a += b; });
-    TCD kb;  // dK_beta_b
-    kb.zero();
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(kb, sTt, sXWt);  // T^T XW
-    kb.each([&](int, int, float& x) { x = -x; });
-    acc_rowsum(kb, [&](int i, int d, float x) { return x * (float)sK[i * LDO + d]; }, red + R_RHO * NWV * C);
+    acc_rowsum(XQ, [&](int i, int d, float x) { return sc * x * (float)sQt[d * LCO + i]; }, red + R_RQ * RS);
+    dqf.each_with(XQ, [&](int i, int, float& a, float& x) { a += sc * sb[i] * x; });
+    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dqf, sPG, sKt);  // (P o Gamma) K
     {
-      TCC dT;
-      dT.zero();
-      gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(dT, sXW, sK);  // XW K^T
-      dT.each_with(dT1, [&](int, int j, float& x, float& t1) { x = t1 - sbeta[j] * sb[j] * x; });
-      dT.each([&](int i, int j, float& x) { sdT[i * LCO + j] = (OT)x; });
+      TCC XWK;
+      XWK.zero();
+      gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(XWK, sXW, sK);  // XW K^T
+      // rho_i = -sum_j T[j][i] XWK[j][i]: column sums of T o XWK
+      acc_colsum(XWK, [&](int j, int i, float x) { return -(float)sT[j * LCO + i] * x; }, red + R_RHO * RS);
+      XWK.each_with(dT1, [&](int, int j, float& xk, float& t1) { xk = sbeta[j] * (t1 - sb[j] * xk); });
+      XWK.each([&](int i, int j, float& x) { sdT[i * LCO + j] = (OT)x; });
     }
     __syncthreads();
     {
@@ -386,6 +420,7 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_grad(Prob p) {
     TCC dL;
     dL.zero();
     gemm_nt<OT, C, C, C, 1, 1, NWV, LCO, LCO>(dL, sTt, sZt);  // T^T Z
+    __syncthreads();  // sdT and sZt free: G and G^T take their place
     dL.each([&](int i, int j, float& x) {
       x = i > j ? -x : 0.f;
       const float gv = i > j ? x * sbeta[i] * expf(sg[i] - sg[j]) : 0.f;
@@ -393,63 +428,58 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_grad(Prob p) {
       sGt[j * LCO + i] = (OT)gv;
     });
     __syncthreads();
-    // dK of this head: e o XK + beta b o dK_beta_b + (P o Gamma)^T Q + G K + G^T K
-    XK.each_with(kb, [&](int i, int, float& x, float& y) { x += sbeta[i] * sb[i] * y; });
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(XK, sPGt, sQt);
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(XK, sG, sKt);
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(XK, sGt, sKt);
-    dkf.each_with(XK, [&](int, int, float& a, float& b) { a += b; });
-    // Gbar o Gamma = P o M + dL o beta_i K K^T o Gamma; dbeta's K K^T term
+    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dkf, sPGt, sQt);  // (P o Gamma)^T Q
+    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dkf, sG, sKt);    // G K
+    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dkf, sGt, sKt);   // G^T K
+    // Gbar o Gamma = P o M + dL o beta_i K K^T o Gamma, and dbeta's K K^T term
     {
-      const OT* M = (const OT*)p.sv_M + ch * C * C;
       TCC gb = PP;
-      gb.each([&](int i, int j, float& x) { x *= (float)M[i * C + j]; });
-      dL.each_with(KK, [&](int i, int j, float& x, float& kk) {
-        x = i > j ? x * expf(sg[i] - sg[j]) * kk : 0.f;  // dL o Gamma o KK
-      });
+      {
+        const OT* M = (const OT*)p.sv_M + ch * C * C;
+        gb.each([&](int i, int j, float& x) { x *= (float)M[i * C + j]; });
+      }
+      TCC KK;
+      KK.zero();
+      gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(KK, sK, sK);
+      dL.each_with(KK, [&](int i, int j, float& x, float& kk) { x = i > j ? x * expf(sg[i] - sg[j]) * kk : 0.f; });
       gb.each_with(dL, [&](int i, int, float& x, float& t) { x += sbeta[i] * t; });
-      acc_rowsum(dL, [&](int, int, float x) { return x; }, red + R_DB3 * NWV * C);
-      acc_rowsum(gb, [&](int, int, float x) { return x; }, red + R_GROW * NWV * C);
-      acc_colsum(gb, [&](int, int, float x) { return x; }, red + R_GCOL * NWV * C);
+      acc_rowsum(dL, [&](int, int, float x) { return x; }, red + R_DB3 * RS);
+      acc_rowsum(gb, [&](int, int, float x) { return x; }, red + R_GROW * RS);
+      acc_colsum(gb, [&](int, int, float x) { return x; }, red + R_GCOL * RS);
     }
-    sred[threadIdx.x] = sdot;
+    sdot = wave_sum(sdot);
+    if (lane == 0) swv[w] = sdot;
     __syncthreads();
     if (threadIdx.x < C) {
       const int i = threadIdx.x;
       for (int s = 0; s < R_NSLOT; ++s) {
         float a = 0.f;
-        for (int ww = 0; ww < NWV; ++ww) a += red[(s * NWV + ww) * C + i];
+        for (int b = 0; b < kRedBlocks; ++b) a += red[s * RS + b * C + i];
         rowv[s * C + i] = a;
       }
     }
     __syncthreads();
-    if (threadIdx.x < C) {
+    if (threadIdx.x < 64) {
       const int i = threadIdx.x;
-      const float ebar = rowv[R_EBAR * C + i], rho = rowv[R_RHO * C + i];
-      float dgam = sb[i] * rowv[R_RQ * C + i] + sbeta[i] * sb[i] * rho - ebar + rowv[R_GROW * C + i] -
-                   rowv[R_GCOL * C + i];
+      const bool ok = i < C;
+      const float ebar = ok ? rowv[R_EBAR * C + i] : 0.f;
+      const float rho = ok ? rowv[R_RHO * C + i] : 0.f;
+      float dgam = 0.f;
+      if (ok)
+        dgam = sb[i] * rowv[R_RQ * C + i] + sbeta[i] * sb[i] * rho - ebar + rowv[R_GROW * C + i] -
+               rowv[R_GCOL * C + i];
+      const float ebsum = wave_sum(ebar);
       if (i == n - 1) {
-        float st = 0.f, eb = 0.f;
-        for (int k = 0; k < NT; ++k) st += sred[k];
-        for (int k = 0; k < C; ++k) eb += rowv[R_EBAR * C + k];
-        dgam += expf(sg[C - 1]) * st + eb;
+        float st = 0.f;
+        for (int k = 0; k < NWV; ++k) st += swv[k];
+        dgam += expf(sg[C - 1]) * st + ebsum;
       }
-      sdg[i] = dgam;
-      if (i < n)
-        p.dbeta[(int64_t)(ci.t0 + i) * p.Hv + h] = rowv[R_DB1 * C + i] + sb[i] * rho + rowv[R_DB3 * C + i];
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float s = 0.f;
-      for (int i = C - 1; i >= 0; --i) {
-        s += sdg[i];
-        sdg[i] = s;
+      const float dlg = wave_rscan_incl(dgam);
+      if (i < n) {
+        const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
+        p.dbeta[row] = rowv[R_DB1 * C + i] + sb[i] * rho + rowv[R_DB3 * C + i];
+        p.dg[row] = dlg / p.g[row];
       }
-    }
-    __syncthreads();
-    if (threadIdx.x < n) {
-      const int64_t row = (int64_t)(ci.t0 + threadIdx.x) * p.Hv + h;
-      p.dg[row] = sdg[threadIdx.x] / p.g[row];
     }
     __syncthreads();
   }
@@ -479,7 +509,7 @@ static hipError_t bwd_seq(const Prob& p, hipStream_t s) {
   traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
   if (p.N > 0) traced("k_bwd_sweep", s, [&] { k_bwd_sweep<TI, C, D><<<dim3(p.N, p.Hv), kThreadsB, 0, s>>>(p); });
   if (p.nc_max > 0)
-    traced("k_bwd_grad", s, [&] { k_bwd_grad<TI, C, D><<<dim3(p.nc_max, p.Hk), kThreadsB, 0, s>>>(p); });
+    traced("k_bwd_grad", s, [&] { k_bwd_grad<TI, C, D><<<dim3(p.nc_max, p.Hk), kThreadsG, 0, s>>>(p); });
   return hipGetLastError();
 }
 

@@ -7,6 +7,31 @@ namespace gdn {
 
 constexpr int NTHREADS = 256;  // threads of the chunk-table kernel
 
+// Wave-level scans and sums over 64 lanes (fixed combination order: deterministic).
+__device__ __forceinline__ float wave_scan_incl(float x) {  // sum of lanes 0..l
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_up(x, off);
+    if (l >= off) x += t;
+  }
+  return x;
+}
+__device__ __forceinline__ float wave_rscan_incl(float x) {  // sum of lanes l..63
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_down(x, off);
+    if (l + off < 64) x += t;
+  }
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 __device__ __forceinline__ size_t ch_idx(const Prob& p, int c, int h) { return (size_t)c * p.Hv + h; }
 
 // Sequence n occupies rows [a, b). Device-side cu_seqlens are clamped into

@@ -24,22 +24,12 @@
 
 namespace gdn {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;              // k_sweep
 constexpr int kThreads = kWaves * 64;
+constexpr int kPrepWaves = 16;         // k_prep
+constexpr int kPrepThreads = kPrepWaves * 64;
 
 __host__ __device__ constexpr int blk2(int x) { return x >= 32 ? 2 : 1; }
-
-// Copy an LDS matrix [R][Cn] (row stride LD) to a contiguous global [R][Cn], 16 B at a time.
-template <int R, int Cn, int LD, int NT, typename OT>
-__device__ __forceinline__ void lds_to_global(OT* __restrict__ dst, const OT* src) {
-  using V = Vec16<OT>;
-  constexpr int VPR = Cn / V::N;
-  for (int idx = threadIdx.x; idx < R * VPR; idx += NT) {
-    const int r = idx / VPR, c = (idx % VPR) * V::N;
-    *reinterpret_cast<typename V::type*>(dst + (size_t)r * Cn + c) =
-        *reinterpret_cast<const typename V::type*>(src + r * LD + c);
-  }
-}
 
 // T := (I + L)^-1 for strictly lower triangular L (float32 LDS, row stride LC).
 // Diagonal 16 x 16 blocks by forward substitution, one column per lane, then the
@@ -100,9 +90,9 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T, floa
 
 // Grid (nc_max, Hk).
 template <typename TI, int C, int D>
-__global__ __launch_bounds__(kThreads) void k_prep(Prob p) {
+__global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   using OT = TI;
-  constexpr int NT = kThreads, LDO = D + 8, LCO = C + 8, LCF = C + 4;
+  constexpr int NT = kPrepThreads, NWV = kPrepWaves, LDO = D + 8, LCO = C + 8, LCF = C + 4;
   __shared__ __align__(16) OT sK[C * LDO];
   __shared__ __align__(16) OT sQ[C * LDO];
   __shared__ __align__(16) OT sKt[D * LCO];
@@ -128,14 +118,16 @@ __global__ __launch_bounds__(kThreads) void k_prep(Prob p) {
     gk.template to_rows<LDO>(sK);
     gk.template to_cols<LCO>(sKt);
     gq.template to_rows<LDO>(sQ);
+    gq.template to_cols<LCO>(sVt);  // Q^T, saved for the backward
   }
   __syncthreads();
   lds_to_global<D, C, LCO, NT>((OT*)p.sv_Kt + ck * D * C, sKt);
-  Tile<C, C, 1, 1, kWaves> KK, QK;
+  lds_to_global<D, C, LCO, NT>((OT*)p.sv_Qt + ck * D * C, sVt);
+  Tile<C, C, 1, 1, NWV> KK, QK;
   KK.zero();
   QK.zero();
-  gemm_nt<OT, C, C, D, 1, 1, kWaves, LDO, LDO>(KK, sK, sK);
-  gemm_nt<OT, C, C, D, 1, 1, kWaves, LDO, LDO>(QK, sQ, sK);
+  gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(KK, sK, sK);
+  gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(QK, sQ, sK);
 
   Stage<C, D, NT, TI> gv;
   gv.issue((const TI*)p.v + (int64_t)ci.t0 * p.v_rs + (kh * p.r) * D, p.v_rs, n);
@@ -150,12 +142,9 @@ __global__ __launch_bounds__(kThreads) void k_prep(Prob p) {
     __syncthreads();
     gv.template to_cols<LCO>(sVt);
     if (hh + 1 < p.r) gv.issue((const TI*)p.v + (int64_t)ci.t0 * p.v_rs + (h + 1) * D, p.v_rs, n);
-    if (threadIdx.x == 0) {
-      float s = 0.f;
-      for (int i = 0; i < C; ++i) {
-        s += sg[i];
-        sg[i] = s;
-      }
+    if (threadIdx.x < 64) {
+      const float x = wave_scan_incl(threadIdx.x < C ? sg[threadIdx.x] : 0.f);
+      if (threadIdx.x < C) sg[threadIdx.x] = x;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < C; i += NT) {
@@ -168,27 +157,29 @@ __global__ __launch_bounds__(kThreads) void k_prep(Prob p) {
     OT* M = (OT*)p.sv_M + ch * C * C;
     QK.each([&](int i, int j, float& x) { M[i * C + j] = (OT)(i >= j ? expf(sg[i] - sg[j]) * x : 0.f); });
     __syncthreads();
-    invert_unit_lower<C, LCF, kWaves>(sL, sT, sX);
+    invert_unit_lower<C, LCF, NWV>(sL, sT, sX);
     OT* Tsv = (OT*)p.sv_T + ch * C * C;
+    OT* Ttsv = (OT*)p.sv_Tt + ch * C * C;
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
       const int i = idx / C, j = idx % C;
       const float t = sT[i * LCF + j];
       Tsv[idx] = (OT)t;
+      Ttsv[idx] = (OT)sT[j * LCF + i];
       sTp[i * LCO + j] = (OT)(t * sbeta[j] * sb[j]);
       sTpp[i * LCO + j] = (OT)(t * sbeta[j]);
     }
     __syncthreads();
     {
-      Tile<C, D, 1, blk2(D), kWaves> w;
+      Tile<C, D, 1, blk2(D), NWV> w;
       w.zero();
-      gemm_nt<OT, C, D, C, 1, blk2(D), kWaves, LCO, LCO>(w, sTp, sKt);
+      gemm_nt<OT, C, D, C, 1, blk2(D), NWV, LCO, LCO>(w, sTp, sKt);
       OT* W = (OT*)p.sv_W + ch * C * D;
       w.each([&](int i, int d, float& x) { W[i * D + d] = (OT)x; });
     }
     {
-      Tile<C, D, 1, blk2(D), kWaves> u;
+      Tile<C, D, 1, blk2(D), NWV> u;
       u.zero();
-      gemm_nt<OT, C, D, C, 1, blk2(D), kWaves, LCO, LCO>(u, sTpp, sVt);
+      gemm_nt<OT, C, D, C, 1, blk2(D), NWV, LCO, LCO>(u, sTpp, sVt);
       OT* Ut = (OT*)p.ws_Ut + ch * D * C;
       u.each4([&](int i0, int v, f32x4& x) {
         *reinterpret_cast<o4*>(Ut + v * C + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
@@ -280,8 +271,8 @@ __global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
         x = f32x4{(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
       });
     }
-    // the chunk's start state, saved for the backward (value-major, from its LDS copy)
-    lds_to_global<D, D, LDO, NT>((OT*)p.sv_S + ch * D * D, sSt);
+    // the chunk's start state, saved for the backward (key-major, from its LDS copy)
+    lds_to_global_t<D, D, LDO, NT>((OT*)p.sv_S + ch * D * D, sSt);
     TD WS, O;
     WS.zero();
     O.zero();
@@ -301,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
       O.each([&](int i, int v, float& x) { x *= sb[i]; });
     }
     __syncthreads();
-    lds_to_global<D, C, LCO, NT>((OT*)p.sv_Dl + ch * D * C, sDt);  // Delta^T for the backward
+    lds_to_global_t<D, C, LCO, NT>((OT*)p.sv_Dl + ch * C * D, sDt);  // Delta, row-major
     gemm_nt<OT, C, D, C, 1, DN, kWaves, LCO, LCO>(O, sM, sDt);
     {
       TI* o = (TI*)p.o + (int64_t)ci.t0 * p.o_rs + h * D;
@@ -330,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
 template <typename TI, int C, int D>
 static hipError_t fwd_seq(const Prob& p, hipStream_t s) {
   traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
-  if (p.nc_max > 0) traced("k_prep", s, [&] { k_prep<TI, C, D><<<dim3(p.nc_max, p.Hk), kThreads, 0, s>>>(p); });
+  if (p.nc_max > 0) traced("k_prep", s, [&] { k_prep<TI, C, D><<<dim3(p.nc_max, p.Hk), kPrepThreads, 0, s>>>(p); });
   if (p.N > 0) traced("k_sweep", s, [&] { k_sweep<TI, C, D><<<dim3(p.N, p.Hv), kThreads, 0, s>>>(p); });
   return hipGetLastError();
 }

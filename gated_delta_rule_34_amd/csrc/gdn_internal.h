@@ -46,18 +46,21 @@ struct Prob {
 
   // Saved activations written by the forward for the backward (element type = the
   // problem's storage type OT unless noted), per chunk c and value head h / key head kh:
-  void* sv_S;    // [c][h][D][D]  state at the start of the chunk, value-major: S^T[v][d]
+  void* sv_S;    // [c][h][D][D]  state at the start of the chunk, key-major
   void* sv_W;    // [c][h][C][D]  W, row-major
-  void* sv_Dl;   // [c][h][D][C]  Delta^T
+  void* sv_Dl;   // [c][h][C][D]  Delta, row-major
   void* sv_M;    // [c][h][C][C]  Gamma o Q K^T (lower incl. diagonal), row-major
   void* sv_T;    // [c][h][C][C]  (I + L)^-1, row-major
+  void* sv_Tt;   // [c][h][C][C]  its transpose
   float* sv_gam; // [c][h][C]     float32
   void* sv_Kt;   // [c][kh][D][C] K^T
   void* sv_Qbt;  // [c][h][D][C]  (diag(b) Q)^T
+  void* sv_Qt;   // [c][kh][D][C] Q^T
   // forward workspace
   void* ws_Ut;   // [c][h][D][C]  U^T
   // backward workspace
-  void* ws_dS;   // [c][h][D][D]  state adjoint at the end of the chunk, value-major
+  void* ws_dS;   // [c][h][D][D]  state adjoint at the end of the chunk, key-major
+  void* ws_dD;   // [c][h][C][D]  dDelta, row-major
   void* ws_dDt;  // [c][h][D][C]  dDelta^T
 };
 

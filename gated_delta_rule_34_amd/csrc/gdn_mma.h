@@ -196,15 +196,15 @@ template <int R, int Cn, int NT, typename T> struct Stage {
         v[u] = typename V::type{};
     }
   }
-  // LDS [r][c] (row stride LD) as OT, optionally times s[r].
+  // LDS [r][c] (row stride LD) as OT, optionally times s[r] and k.
   template <int LD, typename OT>
-  __device__ __forceinline__ void to_rows(OT* dst, const float* s = nullptr) const {
+  __device__ __forceinline__ void to_rows(OT* dst, const float* s = nullptr, float k = 1.f) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = threadIdx.x + u * NT;
       if (idx < NV) {
         const int r = idx / VPR, c = (idx % VPR) * V::N;
-        const float sc = s ? s[r] : 1.f;
+        const float sc = (s ? s[r] : 1.f) * k;
         typedef OT ot_vec __attribute__((ext_vector_type(V::N)));
         ot_vec o;
 #pragma unroll
@@ -213,9 +213,22 @@ template <int R, int Cn, int NT, typename T> struct Stage {
       }
     }
   }
-  // LDS [c][r] (the transpose, row stride LD) as OT, optionally times s[r] and k.
+  // LDS [r][c] (row stride LD), bits copied unchanged (storage type already the LDS type).
+  template <int LD>
+  __device__ __forceinline__ void to_rows_raw(T* dst) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = threadIdx.x + u * NT;
+      if (idx < NV) {
+        const int r = idx / VPR, c = (idx % VPR) * V::N;
+        *reinterpret_cast<typename V::type*>(dst + r * LD + c) = v[u];
+      }
+    }
+  }
+  // LDS [c][r] (the transpose, row stride LD) as OT, optionally times s[r], k and sc[c].
   template <int LD, typename OT>
-  __device__ __forceinline__ void to_cols(OT* dst, const float* s = nullptr, float k = 1.f) const {
+  __device__ __forceinline__ void to_cols(OT* dst, const float* s = nullptr, float k = 1.f,
+                                          const float* scol = nullptr) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = threadIdx.x + u * NT;
@@ -223,10 +236,39 @@ template <int R, int Cn, int NT, typename T> struct Stage {
         const int r = idx / VPR, c = (idx % VPR) * V::N;
         const float sc = (s ? s[r] : 1.f) * k;
 #pragma unroll
-        for (int e = 0; e < V::N; ++e) dst[(c + e) * LD + r] = cvt<OT>((float)v[u][e] * sc);
+        for (int e = 0; e < V::N; ++e)
+          dst[(c + e) * LD + r] = cvt<OT>((float)v[u][e] * sc * (scol ? scol[c + e] : 1.f));
       }
     }
   }
 };
+
+// Contiguous global [Cn][R] = transpose of the LDS matrix [R][LD] (its first Cn
+// columns): each thread gathers one 16-byte run down a column, lanes walk the columns.
+template <int R, int Cn, int LD, int NT, typename OT>
+__device__ __forceinline__ void lds_to_global_t(OT* __restrict__ dst, const OT* src) {
+  using V = Vec16<OT>;
+  constexpr int VR = R / V::N;
+  static_assert(R % V::N == 0, "rows must fill whole vectors");
+  for (int idx = threadIdx.x; idx < Cn * VR; idx += NT) {
+    const int c = idx % Cn, r0 = (idx / Cn) * V::N;
+    typename V::type x;
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) x[e] = src[(r0 + e) * LD + c];
+    *reinterpret_cast<typename V::type*>(dst + (size_t)c * R + r0) = x;
+  }
+}
+
+// Contiguous global [R][Cn] = LDS [R][LD] (its first Cn columns), 16 B at a time.
+template <int R, int Cn, int LD, int NT, typename OT>
+__device__ __forceinline__ void lds_to_global(OT* __restrict__ dst, const OT* src) {
+  using V = Vec16<OT>;
+  constexpr int VPR = Cn / V::N;
+  for (int idx = threadIdx.x; idx < R * VPR; idx += NT) {
+    const int r = idx / VPR, c = (idx % VPR) * V::N;
+    *reinterpret_cast<typename V::type*>(dst + (size_t)r * Cn + c) =
+        *reinterpret_cast<const typename V::type*>(src + r * LD + c);
+  }
+}
 
 }  // namespace gdn
