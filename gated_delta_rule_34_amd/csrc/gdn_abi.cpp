@@ -75,13 +75,13 @@ size_t fwd_ws(const gdn_problem* p) {
 
 size_t bwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.oS + 2 * r.oW;  // table, dS per chunk, dDelta, dDelta^T
+  return r.chunks + r.seq_chunk + r.oS + r.oW;  // table, dS per chunk, dDelta^T
 }
 
-// Saved activations: S, W, Delta, (diag(b) Q)^T, M, T, T^T, gamma, K^T, Q^T.
+// Saved activations: S, W, Delta, (diag(b) Q)^T, M, T^T, gamma, K^T, Q^T.
 size_t saved_bytes(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.oS + 3 * r.oW + 3 * r.oM + r.gam + 2 * r.oKt;
+  return r.oS + 3 * r.oW + 2 * r.oM + r.gam + 2 * r.oKt;
 }
 
 void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
@@ -95,8 +95,6 @@ void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
   P.sv_Qbt = b;
   b += r.oW;
   P.sv_M = b;
-  b += r.oM;
-  P.sv_T = b;
   b += r.oM;
   P.sv_Tt = b;
   b += r.oM;
@@ -244,7 +242,6 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
   P.seq_chunk = cv.take<int>(r.seq_chunk);
   P.ws_dS = cv.take<void>(r.oS);
-  P.ws_dD = cv.take<void>(r.oW);
   P.ws_dDt = cv.take<void>(r.oW);
   const hipError_t e = gdn::launch_backward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;

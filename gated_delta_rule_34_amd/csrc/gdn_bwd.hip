@@ -53,21 +53,21 @@ __device__ __forceinline__ void acc_rowsum(Tile<M, N, TM, TN, NWV>& t, F&& f, fl
     if (b < B::NB) {
       const int cb = b % B::BN, bi = (b / B::BN) * 16 * TM, bj = cb * 16 * TN;
 #pragma unroll
-      for (int x = 0; x < TM; ++x)
+      for (int x = 0; x < TM; ++x) {
+        const int i0 = bi + x * 16 + (l >> 4) * 4;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int y = 0; y < TN; ++y) {
-          const int i0 = bi + x * 16 + (l >> 4) * 4, j = bj + y * 16 + (l & 15);
-          float v[4];
+          const int j = bj + y * 16 + (l & 15);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = f(i0 + e, j, t.a[q][x][y][e]);
-#pragma unroll
-          for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], m);
-          if ((l & 15) == 0)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) red[cb * M + i0 + e] += v[e];
+          for (int e = 0; e < 4; ++e) v[e] += f(i0 + e, j, t.a[q][x][y][e]);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = row16_sum(v[e]);
+        if ((l & 15) == 0)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[cb * M + i0 + e] += v[e];
+      }
     }
   }
 }
@@ -83,17 +83,17 @@ __device__ __forceinline__ void acc_colsum(Tile<M, N, TM, TN, NWV>& t, F&& f, fl
     if (b < B::NB) {
       const int rb = b / B::BN, bi = rb * 16 * TM, bj = (b % B::BN) * 16 * TN;
 #pragma unroll
-      for (int x = 0; x < TM; ++x)
+      for (int y = 0; y < TN; ++y) {
+        const int j = bj + y * 16 + (l & 15);
+        float v = 0.f;
 #pragma unroll
-        for (int y = 0; y < TN; ++y) {
-          const int i0 = bi + x * 16 + (l >> 4) * 4, j = bj + y * 16 + (l & 15);
-          float v = 0.f;
+        for (int x = 0; x < TM; ++x)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v += f(i0 + e, j, t.a[q][x][y][e]);
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 32);
-          if (l < 16) red[rb * N + j] += v;
-        }
+          for (int e = 0; e < 4; ++e) v += f(bi + x * 16 + (l >> 4) * 4 + e, j, t.a[q][x][y][e]);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (l < 16) red[rb * N + j] += v;
+      }
     }
   }
 }
@@ -183,7 +183,6 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
     __syncthreads();
     gemm_nt<OT, D, D, C, SM, SM, NWV, LCO, LCO>(dS, sWt, sdDt);  // - W^T dDelta
     lds_to_global<D, C, LCO, NT>((OT*)p.ws_dDt + ch * D * C, sdDt);
-    lds_to_global_t<D, C, LCO, NT>((OT*)p.ws_dD + ch * C * D, sdDt);
     __syncthreads();
     adj_to_lds();
     if (c - 1 >= c0) commit();
@@ -198,49 +197,66 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
 // ---------------------------------------------------------------------------- grad
 // Row-vector slots of the partial sums in k_bwd_grad.
 enum { R_EBAR = 0, R_DB1, R_RQ, R_RHO, R_DB3, R_GROW, R_GCOL, R_NSLOT };
-constexpr int kRedBlocks = 4;  // column (row) blocks per partial-sum slot
+constexpr int kRedBlocks = 4;  // column blocks per partial-sum slot
 
 template <typename TI, int C, int D> struct GradCfg {
-  static constexpr int LDO = D + 8, LCO = C + 8;
-  static constexpr int BV = sizeof(TI) == 2 ? (D < 64 ? D : 64) : 16, LBO = BV + 8;
-  // phase 1 (one block of BV value columns): S0 and dS_C (key-major), dO, Delta,
-  // dDelta, V, -beta b o dVbeta (row-major), dDelta^T
-  static constexpr int G1 = 2 * D * LBO + 5 * C * LBO + BV * LCO;
-  // phase 2: XW rows, K^T, Q^T, dT (later G^T), Z^T (later G), P o Gamma, its transpose
-  static constexpr int G2 = C * LDO + 2 * D * LCO + 4 * C * LCO;
-  static constexpr int GR = G1 > G2 ? G1 : G2;
+  static constexpr int E = (int)sizeof(TI);
+  static constexpr int BV = E == 2 ? (D >= 32 ? 32 : D) : 16;  // value columns per block
+  static constexpr int NBH = D / BV;                            // blocks per head
+  static constexpr bool DBUF = NBH % 2 == 0;  // blocks alternate between two buffers
+  // One block buffer (element offsets): S0 and dS_C column blocks [D][BV] (key-major),
+  // Delta, dO, V and A = T^T dDelta column blocks [C][BV], dDelta^T row block [BV][C].
+  static constexpr int O_S0 = 0, O_DS = D * BV, O_DL = 2 * D * BV, O_DO = O_DL + C * BV, O_V = O_DO + C * BV,
+                       O_A = O_V + C * BV, O_DDT = O_A + C * BV, BUF = O_DDT + BV * C;
+  // Scratch of the second phase (padded rows of LC = C + 8): P o Gamma, its transpose,
+  // G' = dL o Gamma, and G^T = (diag(beta) G')^T.
+  static constexpr int LC = C + 8, SCR = 4 * C * LC;
+  // With two buffers the scratch shares the second one (free once the head's last block,
+  // which always sits there, is consumed); otherwise it has its own array.
+  static constexpr int BUFY = DBUF ? (BUF > SCR ? BUF : SCR) : 16;
+  static constexpr int SCRZ = DBUF ? 16 : SCR;
+  static_assert(BUF >= 2 * C * D, "dq/dk staging must fit the first buffer");
 };
 
-// Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk.
-// Phase 1 streams blocks of value columns and accumulates
-//   XQ += dO S0^T    XW += dDelta S0^T    XK += Delta dS_C^T    dk += (-beta b o T^T dDelta) S0^T
-//   P += dO Delta^T  dT1 += dDelta V^T    (the scale of dO~ is applied afterwards)
-// plus dV = beta o T^T dDelta and the row sums of dVbeta o V and <S0, dS_C>. Phase 2
-// finishes dq, dT, dL, the rest of dk and the gate gradients.
+// Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk, one head
+// after the other; dq and dk of the key head stay in registers across its value heads.
+//
+// Phase 1 streams the value dimension in blocks of BV columns (global -> LDS by direct
+// loads, the next block in flight while the current one is used) and accumulates
+//   A = T^T dDelta (per block, to LDS), dV = diag(beta) A, rowsum(A o V), <S0, dS_C>,
+//   XQ += dO S0^T,  XK += Delta dS_C^T,  Y += A S0^T,  P += dO Delta^T,  AD += A Delta^T,
+// with dO unscaled (the scale is applied afterwards). Since (I + L) Delta is exactly the
+// right factor of dT, dL = -stril(T^T dT T^T) reduces to -stril(A Delta^T) = -stril(AD),
+// and the W-path gradient of K is -diag(beta b) Y with rho = -rowsum(Y o K).
+// Phase 2 forms Zq = (P o Gamma) K, Zk = (P o Gamma)^T Q, Z1 = G' K and Z2 = G^T K on MFMA
+// and folds them into dq and dk. The row and column sums of Gbar o Gamma that the gate
+// gradient needs are row sums against Q and K of these same products:
+//   rowsum(P o M) = rowsum(Q o Zq),   colsum(P o M) = rowsum(K o Zk),
+//   rowsum(dL o Gamma o K K^T) = rowsum(K o Z1),   colsum(beta_i dL o Gamma o K K^T) = rowsum(K o Z2),
+// so neither K K^T nor M is needed here.
 template <typename TI, int C, int D>
 __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   using OT = TI;
   using CF = GradCfg<TI, C, D>;
-  constexpr int NT = kThreadsG, NWV = kWavesG, LDO = CF::LDO, LCO = CF::LCO;
-  constexpr int BV = CF::BV, LBO = CF::LBO;
-  constexpr int DN = bblk2(D);
-  constexpr int RS = kRedBlocks * C;  // floats per partial-sum slot
-  typedef OT o4 __attribute__((ext_vector_type(4)));
-
+  constexpr int NT = kThreadsG, NWV = kWavesG, BV = CF::BV, NBH = CF::NBH;
+  constexpr int DN = bblk2(D), RS = kRedBlocks * C;
+  using LC = Swz<OT, C>;        // rows of C: K^T, Q^T, T^T, dDelta^T
+  using LB = Swz<OT, BV>;       // rows of BV: the column blocks
+  using LP = Pad<CF::LC>;       // scratch
   using TCC = Tile<C, C, 1, 1, NWV>;
   using TCD = Tile<C, D, 1, DN, NWV>;
   using TCB = Tile<C, BV, 1, 1, NWV>;
-  static_assert(TCD::B::BN <= kRedBlocks && TCC::B::BN <= kRedBlocks && TCC::B::BM <= kRedBlocks &&
-                    TCB::B::BN <= kRedBlocks,
-                "partial-sum slots too small");
+  static_assert(TCD::B::BN <= kRedBlocks && TCB::B::BN <= kRedBlocks, "partial-sum slots too small");
 
-  __shared__ __align__(16) OT sK[C * LDO];  // K rows
-  __shared__ __align__(16) OT sT[C * LCO];  // T rows
-  __shared__ __align__(16) OT sTt[C * LCO]; // T^T rows
-  __shared__ __align__(16) OT sR[CF::GR];
+  __shared__ __align__(16) OT sKt[D * C];
+  __shared__ __align__(16) OT sQt[D * C];
+  __shared__ __align__(16) OT sTt[C * C];
+  __shared__ __align__(16) OT sX[CF::BUF];
+  __shared__ __align__(16) OT sY[CF::BUFY];
+  __shared__ __align__(16) OT sZ[CF::SCRZ];
   __shared__ float red[R_NSLOT * RS];
   __shared__ float rowv[R_NSLOT * C];
-  __shared__ float sg[C], sb[C], se[C], sbeta[C], swv[NWV];
+  __shared__ float sg[C], sb[C], se[C], sbeta[C], sgate[C], swv[NWV];
 
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
@@ -248,208 +264,157 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   const int n = ci.len;
   const int w = threadIdx.x / 64, lane = threadIdx.x & 63;
   const size_t ck = (size_t)c * p.Hk + kh;
+  OT* const scr = CF::DBUF ? sY : sZ;
+  OT* const sPG = scr;
+  OT* const sPGt = scr + C * CF::LC;
+  OT* const sGp = scr + 2 * C * CF::LC;
+  OT* const sGt = scr + 3 * C * CF::LC;
 
-  // phase-1 buffers
-  OT* sS0k = sR;              // [D][LBO]  S0 block, key-major
-  OT* sdSk = sS0k + D * LBO;  // [D][LBO]  dS_C block, key-major
-  OT* sO = sdSk + D * LBO;    // [C][LBO]  dO
-  OT* sDl = sO + C * LBO;     // [C][LBO]  Delta
-  OT* sdD = sDl + C * LBO;    // [C][LBO]  dDelta
-  OT* sV = sdD + C * LBO;     // [C][LBO]  V
-  OT* sdVb = sV + C * LBO;    // [C][LBO]  -beta b o dVbeta
-  OT* sdDt = sdVb + C * LBO;  // [BV][LCO] dDelta^T
-  // phase-2 buffers
-  OT* sXW = sR;               // [C][LDO]
-  OT* sKt = sXW + C * LDO;    // [D][LCO]
-  OT* sQt = sKt + D * LCO;    // [D][LCO]
-  OT* sdT = sQt + D * LCO;    // [C][LCO]  dT, then G^T
-  OT* sZt = sdT + C * LCO;    // [C][LCO]  Z^T, then G
-  OT* sPG = sZt + C * LCO;    // [C][LCO]
-  OT* sPGt = sPG + C * LCO;   // [C][LCO]
-  OT* sGt = sdT;
-  OT* sG = sZt;
+  auto issue_block = [&](OT* buf, int h, int blk) {
+    const size_t ch = ch_idx(p, c, h);
+    const int v0 = blk * BV;
+    dma_tile<D, BV, NT>(buf + CF::O_S0, (const OT*)p.sv_S + ch * D * D + v0, D, D);
+    dma_tile<D, BV, NT>(buf + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + v0, D, D);
+    dma_tile<C, BV, NT>(buf + CF::O_DL, (const OT*)p.sv_Dl + ch * C * D + v0, D, C);
+    dma_tile<C, BV, NT>(buf + CF::O_DO, (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n);
+    dma_tile<C, BV, NT>(buf + CF::O_V, (const TI*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n);
+    dma_tile<BV, C, NT>(buf + CF::O_DDT, (const OT*)p.ws_dDt + ch * D * C + (size_t)v0 * C, C, BV);
+  };
+  float ngam = 0.f, nbeta = 0.f, ngate = 1.f;
+  auto issue_head = [&](int h) {  // T^T and the per-row gate values of value head h
+    const size_t ch = ch_idx(p, c, h);
+    dma_tile<C, C, NT>(sTt, (const OT*)p.sv_Tt + ch * C * C, C, C);
+    if (threadIdx.x < C) {
+      const int i = threadIdx.x;
+      ngam = p.sv_gam[ch * C + i];
+      nbeta = i < n ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
+      ngate = i < n ? p.g[(int64_t)(ci.t0 + i) * p.Hv + h] : 1.f;
+    }
+  };
+  const int h0 = kh * p.r;
+  dma_tile<D, C, NT>(sKt, (const OT*)p.sv_Kt + ck * D * C, C, D);
+  dma_tile<D, C, NT>(sQt, (const OT*)p.sv_Qt + ck * D * C, C, D);
+  issue_head(h0);
+  issue_block(sX, h0, 0);
 
-  {
-    Stage<C, D, NT, TI> gk;
-    gk.issue((const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
-    gk.template to_rows_raw<LDO>(sK);
-  }
   TCD dqf, dkf;  // dq, dk of the key head, summed over its value heads in order
   dqf.zero();
   dkf.zero();
-  __syncthreads();
-
-  Stage<C, C, NT, OT> nT, nTt;
-  float ngam = 0.f, nbeta = 0.f;
-  auto issue_head = [&](int h) {
-    const size_t ch = ch_idx(p, c, h);
-    nT.issue((const OT*)p.sv_T + ch * C * C, C, C);
-    nTt.issue((const OT*)p.sv_Tt + ch * C * C, C, C);
-    if (threadIdx.x < C) {
-      ngam = p.sv_gam[ch * C + threadIdx.x];
-      nbeta = threadIdx.x < n ? p.beta[(int64_t)(ci.t0 + threadIdx.x) * p.Hv + h] : 0.f;
-    }
-  };
-  issue_head(kh * p.r);
 
   for (int hh = 0; hh < p.r; ++hh) {
-    const int h = kh * p.r + hh;
-    const size_t ch = ch_idx(p, c, h);
-    const OT* S0k = (const OT*)p.sv_S + ch * D * D;
-    const OT* dSk = (const OT*)p.ws_dS + ch * D * D;
-    const OT* Dl = (const OT*)p.sv_Dl + ch * C * D;
-    const OT* dD = (const OT*)p.ws_dD + ch * C * D;
-    const OT* dDt = (const OT*)p.ws_dDt + ch * D * C;
-    const TI* dO = (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D;
-    const TI* V = (const TI*)p.v + (int64_t)ci.t0 * p.v_rs + h * D;
+    const int h = h0 + hh;
     TI* dV = (TI*)p.dv + (int64_t)ci.t0 * p.dv_rs + h * D;
-
-    // ---- set-up: T, T^T, gates, M (in the accumulator layout), zeroed partial sums
-    nT.template to_rows_raw<LCO>(sT);
-    nTt.template to_rows_raw<LCO>(sTt);
     if (threadIdx.x < C) {
       sg[threadIdx.x] = ngam;
       sbeta[threadIdx.x] = nbeta;
+      sgate[threadIdx.x] = ngate;
     }
     for (int i = threadIdx.x; i < R_NSLOT * RS; i += NT) red[i] = 0.f;
-    Stage<D, BV, NT, OT> gs, gd;
-    Stage<C, BV, NT, OT> gdl, gdd;
-    Stage<BV, C, NT, OT> gdt;
-    Stage<C, BV, NT, TI> go, gv;
-    auto issue_blk = [&](int v0) {
-      gs.issue(S0k + v0, D, D);
-      gd.issue(dSk + v0, D, D);
-      gdl.issue(Dl + v0, D, C);
-      gdd.issue(dD + v0, D, C);
-      gdt.issue(dDt + (size_t)v0 * C, C, BV);
-      go.issue(dO + v0, p.dO_rs, n);
-      gv.issue(V + v0, p.v_rs, n);
-    };
-    issue_blk(0);
-    __syncthreads();
-    if (threadIdx.x < C) {
-      sb[threadIdx.x] = expf(sg[threadIdx.x]);
-      se[threadIdx.x] = expf(sg[C - 1] - sg[threadIdx.x]);
-    }
 
     // ---- phase 1
-    TCD XQ, XW, XK;
-    TCC PP, dT1;
+    TCD XQ, XK, Y;
+    TCC P, AD;
     XQ.zero();
-    XW.zero();
     XK.zero();
-    PP.zero();
-    dT1.zero();
+    Y.zero();
+    P.zero();
+    AD.zero();
     float sdot = 0.f;
-    for (int v0 = 0; v0 < D; v0 += BV) {
-      gs.template to_rows_raw<LBO>(sS0k);
-      gd.template to_rows_raw<LBO>(sdSk);
-      gdl.template to_rows_raw<LBO>(sDl);
-      gdd.template to_rows_raw<LBO>(sdD);
-      gdt.template to_rows_raw<LCO>(sdDt);
-      go.template to_rows_raw<LBO>(sO);
-      gv.template to_rows_raw<LBO>(sV);
-      __syncthreads();
-      if (v0 + BV < D) issue_blk(v0 + BV);
+    auto block = [&](OT* cur, OT* nxt, int b) {
+      dma_wait();
+      lds_barrier();  // block b (and everything issued with it) is in LDS
+      if (b == 0 && threadIdx.x < C) {
+        sb[threadIdx.x] = expf(sg[threadIdx.x]);
+        se[threadIdx.x] = expf(sg[C - 1] - sg[threadIdx.x]);
+      }
+      if (b + 1 < NBH) issue_block(nxt, h, b + 1);
+      const int v0 = b * BV;
       {
-        TCB dvb;
-        dvb.zero();
-        gemm_nt<OT, C, BV, C, 1, 1, NWV, LCO, LCO>(dvb, sTt, sdDt);  // T^T dDelta
-        dvb.each([&](int i, int j, float& x) {
+        TCB A;
+        A.zero();
+        gemm_l<OT, C, BV, C, 1, 1, NWV, LC, LC>(A, sTt, cur + CF::O_DDT);
+        A.each([&](int i, int j, float& x) {
           if (i < n) dV[(int64_t)i * p.dv_rs + v0 + j] = (TI)(sbeta[i] * x);
-          sdVb[i * LBO + j] = (OT)(-sbeta[i] * sb[i] * x);
+          cur[CF::O_A + LB::at(i, j)] = (OT)x;
         });
-        acc_rowsum(dvb, [&](int i, int j, float x) { return x * (float)sV[i * LBO + j]; }, red + R_DB1 * RS);
+        acc_rowsum(A, [&](int i, int j, float x) { return x * (float)cur[CF::O_V + LB::at(i, j)]; },
+                   red + R_DB1 * RS);
       }
-      for (int idx = threadIdx.x; idx < D * BV; idx += NT) {
-        const int d = idx / BV, vv = idx % BV;
-        sdot += (float)sS0k[d * LBO + vv] * (float)sdSk[d * LBO + vv];
+      {
+        using V = Vec16<OT>;
+        for (int idx = threadIdx.x; idx < D * BV / V::N; idx += NT) {  // same layout: index-wise product
+          const typename V::type a = reinterpret_cast<const typename V::type*>(cur + CF::O_S0)[idx];
+          const typename V::type d = reinterpret_cast<const typename V::type*>(cur + CF::O_DS)[idx];
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) sdot += (float)a[e] * (float)d[e];
+        }
       }
-      __syncthreads();  // sdVb visible
-      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XQ, sO, sS0k);
-      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XW, sdD, sS0k);
-      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(XK, sDl, sdSk);
-      gemm_nt<OT, C, D, BV, 1, DN, NWV, LBO, LBO>(dkf, sdVb, sS0k);
-      gemm_nt<OT, C, C, BV, 1, 1, NWV, LBO, LBO>(PP, sO, sDl);
-      gemm_nt<OT, C, C, BV, 1, 1, NWV, LBO, LBO>(dT1, sdD, sV);
-      __syncthreads();  // block buffers free
+      lds_barrier();  // A visible
+      gemm_l<OT, C, D, BV, 1, DN, NWV, LB, LB>(XQ, cur + CF::O_DO, cur + CF::O_S0);
+      gemm_l<OT, C, D, BV, 1, DN, NWV, LB, LB>(XK, cur + CF::O_DL, cur + CF::O_DS);
+      gemm_l<OT, C, D, BV, 1, DN, NWV, LB, LB>(Y, cur + CF::O_A, cur + CF::O_S0);
+      gemm_l<OT, C, C, BV, 1, 1, NWV, LB, LB>(P, cur + CF::O_DO, cur + CF::O_DL);
+      gemm_l<OT, C, C, BV, 1, 1, NWV, LB, LB>(AD, cur + CF::O_A, cur + CF::O_DL);
+    };
+    if constexpr (CF::DBUF) {
+      for (int b = 0; b < NBH; b += 2) {
+        block(sX, sY, b);
+        block(sY, sX, b + 1);
+      }
+    } else {
+      block(sX, sX, 0);
     }
-    if (hh + 1 < p.r) issue_head(h + 1);
+    lds_barrier();  // the last block and T^T are consumed
+    const bool more = hh + 1 < p.r;
+    if (more) {
+      issue_head(h + 1);
+      issue_block(sX, h + 1, 0);
+    }
 
     // ---- phase 2
-    {
-      Stage<D, C, NT, OT> gkt, gqt;
-      gkt.issue((const OT*)p.sv_Kt + ck * D * C, C, D);
-      gqt.issue((const OT*)p.sv_Qt + ck * D * C, C, D);
-      gkt.template to_rows_raw<LCO>(sKt);
-      gqt.template to_rows_raw<LCO>(sQt);
-    }
     const float sc = p.scale;
-    XW.each([&](int i, int d, float& x) { sXW[i * LDO + d] = (OT)x; });
-    PP.each([&](int i, int j, float& x) {
-      x = i >= j ? x * sc : 0.f;
-      const float pg = i >= j ? x * expf(sg[i] - sg[j]) : 0.f;
-      sPG[i * LCO + j] = (OT)pg;
-      sPGt[j * LCO + i] = (OT)pg;
+    P.each([&](int i, int j, float& x) {
+      const float pg = i >= j ? sc * x * expf(sg[i] - sg[j]) : 0.f;
+      sPG[LP::at(i, j)] = (OT)pg;
+      sPGt[LP::at(j, i)] = (OT)pg;
     });
-    acc_rowsum(XK, [&](int i, int d, float x) { return se[i] * x * (float)sK[i * LDO + d]; }, red + R_EBAR * RS);
+    AD.each([&](int i, int j, float& x) {  // dL = -stril(AD); G' = dL o Gamma
+      const float gp = i > j ? -x * expf(sg[i] - sg[j]) : 0.f;
+      sGp[LP::at(i, j)] = (OT)gp;
+      sGt[LP::at(j, i)] = (OT)(sbeta[i] * gp);
+    });
+    acc_rowsum(XK, [&](int i, int d, float x) { return se[i] * x * (float)sKt[LC::at(d, i)]; }, red + R_EBAR * RS);
     dkf.each_with(XK, [&](int i, int, float& a, float& x) { a += se[i] * x; });
-    __syncthreads();
-    acc_rowsum(XQ, [&](int i, int d, float x) { return sc * x * (float)sQt[d * LCO + i]; }, red + R_RQ * RS);
+    acc_rowsum(XQ, [&](int i, int d, float x) { return sc * x * (float)sQt[LC::at(d, i)]; }, red + R_RQ * RS);
     dqf.each_with(XQ, [&](int i, int, float& a, float& x) { a += sc * sb[i] * x; });
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dqf, sPG, sKt);  // (P o Gamma) K
-    {
-      TCC XWK;
-      XWK.zero();
-      gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(XWK, sXW, sK);  // XW K^T
-      // rho_i = -sum_j T[j][i] XWK[j][i]: column sums of T o XWK
-      acc_colsum(XWK, [&](int j, int i, float x) { return -(float)sT[j * LCO + i] * x; }, red + R_RHO * RS);
-      XWK.each_with(dT1, [&](int, int j, float& xk, float& t1) { xk = sbeta[j] * (t1 - sb[j] * xk); });
-      XWK.each([&](int i, int j, float& x) { sdT[i * LCO + j] = (OT)x; });
-    }
-    __syncthreads();
-    {
-      TCC Z;
-      Z.zero();
-      gemm_nt<OT, C, C, C, 1, 1, NWV, LCO, LCO>(Z, sdT, sT);  // dT T^T
-      Z.each4([&](int i0, int m, f32x4& x) {
-        *reinterpret_cast<o4*>(sZt + m * LCO + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
-      });
-    }
-    __syncthreads();
-    TCC dL;
-    dL.zero();
-    gemm_nt<OT, C, C, C, 1, 1, NWV, LCO, LCO>(dL, sTt, sZt);  // T^T Z
-    __syncthreads();  // sdT and sZt free: G and G^T take their place
-    dL.each([&](int i, int j, float& x) {
-      x = i > j ? -x : 0.f;
-      const float gv = i > j ? x * sbeta[i] * expf(sg[i] - sg[j]) : 0.f;
-      sG[i * LCO + j] = (OT)gv;
-      sGt[j * LCO + i] = (OT)gv;
-    });
-    __syncthreads();
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dkf, sPGt, sQt);  // (P o Gamma)^T Q
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dkf, sG, sKt);    // G K
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dkf, sGt, sKt);   // G^T K
-    // Gbar o Gamma = P o M + dL o beta_i K K^T o Gamma, and dbeta's K K^T term
-    {
-      TCC gb = PP;
-      {
-        const OT* M = (const OT*)p.sv_M + ch * C * C;
-        gb.each([&](int i, int j, float& x) { x *= (float)M[i * C + j]; });
-      }
-      TCC KK;
-      KK.zero();
-      gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(KK, sK, sK);
-      dL.each_with(KK, [&](int i, int j, float& x, float& kk) { x = i > j ? x * expf(sg[i] - sg[j]) * kk : 0.f; });
-      gb.each_with(dL, [&](int i, int, float& x, float& t) { x += sbeta[i] * t; });
-      acc_rowsum(dL, [&](int, int, float x) { return x; }, red + R_DB3 * RS);
-      acc_rowsum(gb, [&](int, int, float x) { return x; }, red + R_GROW * RS);
-      acc_colsum(gb, [&](int, int, float x) { return x; }, red + R_GCOL * RS);
-    }
+    acc_rowsum(Y, [&](int i, int d, float x) { return -x * (float)sKt[LC::at(d, i)]; }, red + R_RHO * RS);
+    dkf.each_with(Y, [&](int i, int, float& a, float& y) { a -= sbeta[i] * sb[i] * y; });
     sdot = wave_sum(sdot);
     if (lane == 0) swv[w] = sdot;
-    __syncthreads();
+    lds_barrier();  // scratch written
+    {
+      TCD Z;
+      Z.zero();
+      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sPG, sKt);  // (P o Gamma) K
+      acc_rowsum(Z, [&](int i, int d, float x) { return x * (float)sQt[LC::at(d, i)]; }, red + R_GROW * RS);
+      dqf.each_with(Z, [&](int, int, float& a, float& z) { a += z; });
+    }
+    {
+      TCD Z;
+      Z.zero();
+      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sPGt, sQt);  // (P o Gamma)^T Q
+      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sGt, sKt);   // + G^T K
+      acc_rowsum(Z, [&](int i, int d, float x) { return x * (float)sKt[LC::at(d, i)]; }, red + R_GCOL * RS);
+      dkf.each_with(Z, [&](int, int, float& a, float& z) { a += z; });
+    }
+    {
+      TCD Z;
+      Z.zero();
+      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sGp, sKt);  // G' K
+      acc_rowsum(Z, [&](int i, int d, float x) { return x * (float)sKt[LC::at(d, i)]; }, red + R_DB3 * RS);
+      dkf.each_with(Z, [&](int i, int, float& a, float& z) { a += sbeta[i] * z; });
+    }
+    lds_barrier();
     if (threadIdx.x < C) {
       const int i = threadIdx.x;
       for (int s = 0; s < R_NSLOT; ++s) {
@@ -458,16 +423,17 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         rowv[s * C + i] = a;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < 64) {
       const int i = threadIdx.x;
       const bool ok = i < C;
       const float ebar = ok ? rowv[R_EBAR * C + i] : 0.f;
       const float rho = ok ? rowv[R_RHO * C + i] : 0.f;
+      const float db3 = ok ? rowv[R_DB3 * C + i] : 0.f;
       float dgam = 0.f;
       if (ok)
-        dgam = sb[i] * rowv[R_RQ * C + i] + sbeta[i] * sb[i] * rho - ebar + rowv[R_GROW * C + i] -
-               rowv[R_GCOL * C + i];
+        dgam = sb[i] * rowv[R_RQ * C + i] + sbeta[i] * sb[i] * rho - ebar + rowv[R_GROW * C + i] +
+               sbeta[i] * db3 - rowv[R_GCOL * C + i];
       const float ebsum = wave_sum(ebar);
       if (i == n - 1) {
         float st = 0.f;
@@ -477,18 +443,18 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const float dlg = wave_rscan_incl(dgam);
       if (i < n) {
         const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
-        p.dbeta[row] = rowv[R_DB1 * C + i] + sb[i] * rho + rowv[R_DB3 * C + i];
-        p.dg[row] = dlg / p.g[row];
+        p.dbeta[row] = rowv[R_DB1 * C + i] + sb[i] * rho + db3;
+        p.dg[row] = dlg / sgate[i];
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
-  // dq, dk of the key head: stage rows through LDS, then 16-byte stores
+  // dq, dk of the key head: rows through LDS (the first block buffer), 16-byte stores
   {
-    TI* st = (TI*)sR;
-    dqf.each([&](int i, int d, float& x) { st[i * LDO + d] = (TI)x; });
-    dkf.each([&](int i, int d, float& x) { st[(C + i) * LDO + d] = (TI)x; });
-    __syncthreads();
+    TI* st = (TI*)sX;
+    dqf.each([&](int i, int d, float& x) { st[i * D + d] = (TI)x; });
+    dkf.each([&](int i, int d, float& x) { st[(C + i) * D + d] = (TI)x; });
+    lds_barrier();
     using V = Vec16<TI>;
     constexpr int VPR = D / V::N;
     TI* dq = (TI*)p.dq + (int64_t)ci.t0 * p.dq_rs + kh * D;
@@ -498,7 +464,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const int i = r % C;
       if (i < n) {
         TI* dst = r < C ? dq + (int64_t)i * p.dq_rs + cc : dk + (int64_t)i * p.dk_rs + cc;
-        *reinterpret_cast<typename V::type*>(dst) = *reinterpret_cast<const typename V::type*>(st + r * LDO + cc);
+        *reinterpret_cast<typename V::type*>(dst) = *reinterpret_cast<const typename V::type*>(st + r * D + cc);
       }
     }
   }

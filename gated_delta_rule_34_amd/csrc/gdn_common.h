@@ -32,6 +32,19 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k + 15), returned in every lane of
+// the row: pair and quad swaps, then the half-row and row mirrors (no LDS traffic).
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
 __device__ __forceinline__ size_t ch_idx(const Prob& p, int c, int h) { return (size_t)c * p.Hv + h; }
 
 // Sequence n occupies rows [a, b). Device-side cu_seqlens are clamped into

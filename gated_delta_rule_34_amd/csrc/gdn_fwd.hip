@@ -158,12 +158,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
     QK.each([&](int i, int j, float& x) { M[i * C + j] = (OT)(i >= j ? expf(sg[i] - sg[j]) * x : 0.f); });
     __syncthreads();
     invert_unit_lower<C, LCF, NWV>(sL, sT, sX);
-    OT* Tsv = (OT*)p.sv_T + ch * C * C;
     OT* Ttsv = (OT*)p.sv_Tt + ch * C * C;
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
       const int i = idx / C, j = idx % C;
       const float t = sT[i * LCF + j];
-      Tsv[idx] = (OT)t;
       Ttsv[idx] = (OT)sT[j * LCF + i];
       sTp[i * LCO + j] = (OT)(t * sbeta[j] * sb[j]);
       sTpp[i * LCO + j] = (OT)(t * sbeta[j]);

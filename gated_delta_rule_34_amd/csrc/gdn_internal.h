@@ -50,8 +50,7 @@ struct Prob {
   void* sv_W;    // [c][h][C][D]  W, row-major
   void* sv_Dl;   // [c][h][C][D]  Delta, row-major
   void* sv_M;    // [c][h][C][C]  Gamma o Q K^T (lower incl. diagonal), row-major
-  void* sv_T;    // [c][h][C][C]  (I + L)^-1, row-major
-  void* sv_Tt;   // [c][h][C][C]  its transpose
+  void* sv_Tt;   // [c][h][C][C]  T^T, T = (I + L)^-1
   float* sv_gam; // [c][h][C]     float32
   void* sv_Kt;   // [c][kh][D][C] K^T
   void* sv_Qbt;  // [c][h][D][C]  (diag(b) Q)^T
@@ -60,7 +59,6 @@ struct Prob {
   void* ws_Ut;   // [c][h][D][C]  U^T
   // backward workspace
   void* ws_dS;   // [c][h][D][D]  state adjoint at the end of the chunk, key-major
-  void* ws_dD;   // [c][h][C][D]  dDelta, row-major
   void* ws_dDt;  // [c][h][D][C]  dDelta^T
 };
 

@@ -133,9 +133,26 @@ template <int M, int N, int TM, int TN, int NWV> struct Tile {
   }
 };
 
-// acc += A * Bt^T. A: LDS [M][LDA], Bt: LDS [N][LDB] (element type OT).
-template <typename OT, int M, int N, int K, int TM, int TN, int NWV, int LDA, int LDB>
-__device__ __forceinline__ void gemm_nt(Tile<M, N, TM, TN, NWV>& acc, const OT* A, const OT* Bt) {
+// ------------------------------------------------------------------ LDS layouts
+// Padded row-major: element (r, c) at r * LD + c.
+template <int LD> struct Pad {
+  __device__ __forceinline__ static int at(int r, int c) { return r * LD + c; }
+};
+
+// Dense row-major [R][Cn] whose 16-byte chunks are XOR-permuted within each row. An MFMA
+// fragment load reads the same chunk of 16 consecutive rows; the permutation puts those
+// 16 chunks in distinct banks without padding, and dense rows are what the direct
+// global-to-LDS loads (dma_tile) write.
+template <typename T, int Cn> struct Swz {
+  static constexpr int CE = 16 / (int)sizeof(T), NCH = Cn / CE;
+  static_assert(Cn % CE == 0 && (NCH & (NCH - 1)) == 0, "row must be a power-of-two count of 16-byte chunks");
+  __device__ __forceinline__ static int s(int r) { return NCH >= 16 ? (r & 15) : ((r * NCH) >> 4) & (NCH - 1); }
+  __device__ __forceinline__ static int at(int r, int c) { return r * Cn + (((c / CE) ^ s(r)) * CE) + (c % CE); }
+};
+
+// acc += A * Bt^T with A [M][K] in layout LA and Bt [N][K] in layout LB (element type OT).
+template <typename OT, int M, int N, int K, int TM, int TN, int NWV, class LA, class LB>
+__device__ __forceinline__ void gemm_l(Tile<M, N, TM, TN, NWV>& acc, const OT* A, const OT* Bt) {
   using Op = MmaOp<OT, K>;
   using B = Blk<M, N, TM, TN, NWV>;
   static_assert(K % Op::KS == 0, "K must be a multiple of the MFMA depth");
@@ -150,9 +167,9 @@ __device__ __forceinline__ void gemm_nt(Tile<M, N, TM, TN, NWV>& acc, const OT* 
       for (int k0 = 0; k0 < K; k0 += Op::KS) {
         typename Op::frag fa[TM], fb[TN];
 #pragma unroll
-        for (int x = 0; x < TM; ++x) fa[x] = Op::ld(A + (bi + x * 16 + r) * LDA + k0 + kq);
+        for (int x = 0; x < TM; ++x) fa[x] = Op::ld(A + LA::at(bi + x * 16 + r, k0 + kq));
 #pragma unroll
-        for (int y = 0; y < TN; ++y) fb[y] = Op::ld(Bt + (bj + y * 16 + r) * LDB + k0 + kq);
+        for (int y = 0; y < TN; ++y) fb[y] = Op::ld(Bt + LB::at(bj + y * 16 + r, k0 + kq));
 #pragma unroll
         for (int x = 0; x < TM; ++x)
 #pragma unroll
@@ -161,6 +178,51 @@ __device__ __forceinline__ void gemm_nt(Tile<M, N, TM, TN, NWV>& acc, const OT* 
     }
   }
 }
+
+// acc += A * Bt^T. A: LDS [M][LDA], Bt: LDS [N][LDB] (padded row-major).
+template <typename OT, int M, int N, int K, int TM, int TN, int NWV, int LDA, int LDB>
+__device__ __forceinline__ void gemm_nt(Tile<M, N, TM, TN, NWV>& acc, const OT* A, const OT* Bt) {
+  gemm_l<OT, M, N, K, TM, TN, NWV, Pad<LDA>, Pad<LDB>>(acc, A, Bt);
+}
+
+// ------------------------------------------------------------------ direct global -> LDS
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Asynchronous copy of the global tile [R][Cn] (row stride rs elements) into LDS in the
+// layout Swz<T, Cn>, by 16-byte direct global-to-LDS loads (global_load_lds_dwordx4): no
+// registers are involved, and each wave instruction fills 1 KiB of LDS. Rows at or past
+// nvalid (>= 1) repeat row nvalid - 1, so nothing outside the caller's rows is read.
+// Completion: every wave waits with dma_wait(), then the workgroup synchronises.
+template <int R, int Cn, int NT, typename T>
+__device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ src, int64_t rs, int nvalid) {
+  using L = Swz<T, Cn>;
+  constexpr int TOT = R * L::NCH, NW = NT / 64, U = (TOT + NT - 1) / NT;
+  const int l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int base = (u * NW + w) * 64;  // first chunk this wave instruction writes
+    if (base < TOT) {
+      const int pch = base + l;
+      if (pch < TOT) {
+        const int r = pch / L::NCH, c = (pch % L::NCH) ^ L::s(r);
+        const int rr = r < nvalid ? r : nvalid - 1;
+        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)rr * rs + c * L::CE),
+                                         (lds_void_t*)(lds + base * L::CE), 16, 0, 0);
+      }
+    }
+  }
+}
+
+// Wait until this wave's outstanding vector-memory operations (loads into LDS included)
+// have completed: s_waitcnt vmcnt(0), other counters left alone.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier that orders LDS accesses only. Unlike __syncthreads() it does not wait
+// for the wave's outstanding global memory operations, so loads into LDS issued before it
+// stay in flight across it (dma_wait() waits for them).
+// (A fence, even one limited to LDS, would also wait for loads into LDS still in flight.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ------------------------------------------------------------------ LDS staging
 template <typename T> struct Vec16;
