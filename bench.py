@@ -27,23 +27,37 @@ METRIC = "GDN fwd+bwd tokens/s @Hk16/Hv48/D128 T=4096; % MFMA / HBM roofline"
 PEAK = {"f32_mfma": 157.3e12, "bf16_mfma": 2.5e15, "hbm": 8.0e12}
 
 
-def kernel_work(name, C, D, Hk, Hv, n_chunks):
-    """Algorithmic MFMA flops of one launch: the products each kernel forms, per
-    (chunk, value head), times chunks x value heads."""
+def kernel_model(name, C, D, Hk, Hv, n_chunks, es=2):
+    """Algorithmic MFMA flops and HBM bytes of one launch of a kernel: the products it
+    forms and the tensors it must read and write, per unit of work (chunk x value head,
+    or chunk x key head), times the units of one launch. Activations are es bytes."""
     r = Hv // Hk
-    units = n_chunks * Hv
-    per_unit = {
-        # K K^T and Q K^T once per key head; W, U per value head
-        "k_prep": 4 * C * C * D // r + 4 * C * C * D,
-        # W S, Q S, K^T (e o Delta); M Delta
-        "k_sweep": 6 * C * D * D + 2 * C * C * D,
-        # K dS, (bQ)^T dO~, W^T dDelta; M^T dO~
-        "k_bwd_sweep": 6 * C * D * D + 2 * C * C * D,
-        # XQ, XW, XK, K dS; P, dT1, T^T dDelta, (P o Gamma) K, T^T XW, XW K^T, three for dK;
-        # dT T^T, T^T Z; K K^T once per key head
-        "k_bwd_grad": 8 * C * D * D + 18 * C * C * D + 4 * C * C * C + 2 * C * C * D // r,
-    }.get(name)
-    return None if per_unit is None else per_unit * units
+    ch, ck = n_chunks * Hv, n_chunks * Hk  # (chunk, value head) and (chunk, key head) units
+    cd, cc, dd = C * D * es, C * C * es, D * D * es
+    model = {
+        # K K^T, Q K^T per key head; W = T diag(beta b) K, U = T diag(beta) V per value head.
+        # Reads K, Q, V, g, beta; writes K^T, Q^T, and per value head gamma, M, T^T, W, U^T, (diag(b) Q)^T.
+        "k_prep": (ck * (4 * C * C * D) + ch * (4 * C * C * D),
+                   ck * (4 * cd) + ch * (cd + 8 * C + 4 * C + 2 * cc + 3 * cd)),
+        # W S, Q S, K^T (e o Delta), M Delta. Reads W, Q, M, K^T, U^T, gamma; writes S, Delta, O.
+        "k_sweep": (ch * (6 * C * D * D + 2 * C * C * D), ch * (4 * cd + cc + 4 * C + dd + 2 * cd)),
+        # K dS, (diag(b) Q)^T dO, W^T dDelta, M^T dO. Reads M, dO, K, (diag(b) Q)^T, W, gamma;
+        # writes dS, dDelta^T.
+        "k_bwd_sweep": (ch * (6 * C * D * D + 2 * C * C * D), ch * (cc + 4 * cd + 4 * C + dd + cd)),
+        # T^T dDelta, dO S0^T, Delta dS^T, A S0^T, dO Delta^T, A Delta^T, (P o Gamma) K,
+        # (P o Gamma)^T Q, G^T K, G' K. Reads S0, dS, Delta, dO, V, dDelta^T, T^T, gamma, beta, g
+        # per value head and K^T, Q^T per key head; writes dV, dg, dbeta and dq, dk.
+        "k_bwd_grad": (ch * (6 * C * D * D + 14 * C * C * D),
+                       ch * (2 * dd + 4 * cd + cc + 12 * C + cd + 8 * C) + ck * (4 * cd)),
+    }
+    return model.get(name)
+
+
+# Whole-path algorithmic work per token at Hk=16, Hv=48, D=128 (q, k, v, g, beta, o in the
+# forward; q, k, v, g, beta, dO in and dq, dk, dv, dg, dbeta out in the backward), and the
+# bytes of one float32 state tensor per sequence.
+PATH_BYTES_PER_TOKEN = 87168
+PATH_FLOPS_PER_TOKEN = 29.36e6
 
 
 def main():
@@ -124,12 +138,32 @@ def main():
     kernels = {k: round(v[0] / v[1], 4) for k, v in sorted(trace.items(), key=lambda kv: -kv[1][0])}
     dom = max(trace.items(), key=lambda kv: kv[1][0])[0]
     avg_s = trace[dom][0] / trace[dom][1] / 1e3
-    flops = kernel_work(dom, C, D, Hk, Hv, n_chunks)
-    achieved = flops / avg_s / 1e12
-    peak = PEAK["bf16_mfma"] / 1e12
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "avg_launch_ms": round(avg_s * 1e3, 4), "operand_dtype": "bf16"}
+    flops, nbytes = kernel_model(dom, C, D, Hk, Hv, n_chunks)
+    # the binding roofline is the one whose peak takes longer for this launch's work
+    if flops / PEAK["bf16_mfma"] >= nbytes / PEAK["hbm"]:
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(flops / avg_s / 1e12, 3),
+                    "peak": PEAK["bf16_mfma"] / 1e12, "unit": "TFLOP/s",
+                    "frac": round(flops / avg_s / PEAK["bf16_mfma"], 4), "operand_dtype": "bf16"}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1),
+                    "peak": PEAK["hbm"] / 1e9, "unit": "GB/s", "frac": round(nbytes / avg_s / PEAK["hbm"], 4)}
+    roofline.update({"traffic": None, "avg_launch_ms": round(avg_s * 1e3, 4),
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                     "mfma_frac": round(flops / avg_s / PEAK["bf16_mfma"], 4),
+                     "hbm_frac": round(nbytes / avg_s / PEAK["hbm"], 4)})
+    per_kernel = {}
+    for k in kernels:
+        m = kernel_model(k, C, D, Hk, Hv, n_chunks)
+        if m:
+            t = trace[k][0] / trace[k][1] / 1e3
+            per_kernel[k] = {"ms": round(t * 1e3, 4), "TFLOP/s": round(m[0] / t / 1e12, 1),
+                             "GB/s": round(m[1] / t / 1e9, 1)}
+    state_bytes = case.N * Hv * D * D * 4
+    n_state = 3 if d["S0"] is None else 5  # S_T, dS_T, dS0 (+ S0 read twice)
+    path_bytes = PATH_BYTES_PER_TOKEN * T + n_state * state_bytes
+    path = {"bytes": path_bytes, "flops": PATH_FLOPS_PER_TOKEN * T,
+            "hbm_frac": round(path_bytes / (ms_step / 1e3) / PEAK["hbm"], 4),
+            "mfma_frac": round(PATH_FLOPS_PER_TOKEN * T / (ms_step / 1e3) / PEAK["bf16_mfma"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -156,6 +190,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_avg_ms": kernels,
+        "kernels": per_kernel,
+        "path_roofline": path,
     }
     print(json.dumps(line), flush=True)
 

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
     commit();
   }
   adj_to_lds();
-  __syncthreads();
+  lds_barrier();
   for (int c = c1 - 1; c >= c0; --c) {
     const size_t ch = ch_idx(p, c, h);
     lds_to_global_t<D, D, LDO, NT>((OT*)p.ws_dS + ch * D * D, sdSt);  // dS_C, key-major
@@ -174,19 +174,19 @@ __global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
     gemm_nt<OT, C, D, D, 1, DN, NWV, LDO, LDO>(dD, sK, sdSt);  // K dS
     dS.each([&](int, int, float& x) { x *= bn; });
     gemm_nt<OT, D, D, C, SM, SM, NWV, LCO, LCO>(dS, sQbt, sOt);  // + (diag(b) Q)^T dO~
-    __syncthreads();  // se visible
+    lds_barrier();  // se visible
     dD.each([&](int i, int, float& x) { x *= se[i]; });
     gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dD, sMt, sOt);  // + M^T dO~
     dD.each4([&](int i0, int v, f32x4& x) {
       *reinterpret_cast<o4*>(sdDt + v * LCO + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
     });
-    __syncthreads();
+    lds_barrier();
     gemm_nt<OT, D, D, C, SM, SM, NWV, LCO, LCO>(dS, sWt, sdDt);  // - W^T dDelta
     lds_to_global<D, C, LCO, NT>((OT*)p.ws_dDt + ch * D * C, sdDt);
-    __syncthreads();
+    lds_barrier();
     adj_to_lds();
     if (c - 1 >= c0) commit();
-    __syncthreads();
+    lds_barrier();
   }
   if (p.dS0) {
     float* s = p.dS0 + nh * D * D;

@@ -56,7 +56,7 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T, floa
 #pragma unroll
     for (int i = 0; i < 16; ++i) T[(o + i) * LC + o + j] = t[i];
   }
-  __syncthreads();
+  lds_barrier();
   for (int d = 1; d < NB; ++d) {
     const int npairs = NB - d;
     const int bi = w + d, bj = w;  // wave w < npairs owns block (w + d, w)
@@ -72,7 +72,7 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T, floa
 #pragma unroll
       for (int e = 0; e < 4; ++e) X[w * 320 + ((l >> 4) * 4 + e) * 20 + (l & 15)] = acc[e];
     }
-    __syncthreads();
+    lds_barrier();
     if (w < npairs) {
       f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -84,7 +84,7 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T, floa
 #pragma unroll
       for (int e = 0; e < 4; ++e) T[(bi * 16 + (l >> 4) * 4 + e) * LC + bj * 16 + (l & 15)] = -r[e];
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
     gq.template to_rows<LDO>(sQ);
     gq.template to_cols<LCO>(sVt);  // Q^T, saved for the backward
   }
-  __syncthreads();
+  lds_barrier();
   lds_to_global<D, C, LCO, NT>((OT*)p.sv_Kt + ck * D * C, sKt);
   lds_to_global<D, C, LCO, NT>((OT*)p.sv_Qt + ck * D * C, sVt);
   Tile<C, C, 1, 1, NWV> KK, QK;
@@ -139,14 +139,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
       sbeta[i] = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
       sg[i] = ok ? logf(p.g[(int64_t)(ci.t0 + i) * p.Hv + h]) : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     gv.template to_cols<LCO>(sVt);
     if (hh + 1 < p.r) gv.issue((const TI*)p.v + (int64_t)ci.t0 * p.v_rs + (h + 1) * D, p.v_rs, n);
     if (threadIdx.x < 64) {
       const float x = wave_scan_incl(threadIdx.x < C ? sg[threadIdx.x] : 0.f);
       if (threadIdx.x < C) sg[threadIdx.x] = x;
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < C; i += NT) {
       sb[i] = expf(sg[i]);
       p.sv_gam[ch * C + i] = sg[i];
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
     });
     OT* M = (OT*)p.sv_M + ch * C * C;
     QK.each([&](int i, int j, float& x) { M[i * C + j] = (OT)(i >= j ? expf(sg[i] - sg[j]) * x : 0.f); });
-    __syncthreads();
+    lds_barrier();
     invert_unit_lower<C, LCF, NWV>(sL, sT, sX);
     OT* Ttsv = (OT*)p.sv_Tt + ch * C * C;
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
       sTp[i * LCO + j] = (OT)(t * sbeta[j] * sb[j]);
       sTpp[i * LCO + j] = (OT)(t * sbeta[j]);
     }
-    __syncthreads();
+    lds_barrier();
     {
       Tile<C, D, 1, blk2(D), NWV> w;
       w.zero();
@@ -183,9 +183,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
         *reinterpret_cast<o4*>(Ut + v * C + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
       });
     }
-    __syncthreads();  // sVt free: stage (diag(b) Q)^T for the backward
+    lds_barrier();  // sVt free: stage (diag(b) Q)^T for the backward
     gq.template to_cols<LCO>(sVt, sb);
-    __syncthreads();
+    lds_barrier();
     lds_to_global<D, C, LCO, NT>((OT*)p.sv_Qbt + ch * D * C, sVt);
   }
 }
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
     commit();
   }
   state_to_lds();
-  __syncthreads();
+  lds_barrier();
   for (int c = c0; c < c1; ++c) {
     const ChunkInfo ci = p.chunks[c];
     const size_t ch = ch_idx(p, c, h);
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
     O.zero();
     gemm_nt<OT, C, D, D, 1, DN, kWaves, LDO, LDO>(WS, sW, sSt);
     gemm_nt<OT, C, D, D, 1, DN, kWaves, LDO, LDO>(O, sQ, sSt);
-    __syncthreads();  // sb, se visible
+    lds_barrier();  // sb, se visible
     {
 #pragma unroll
       for (int q = 0; q < TD::B::PER; ++q)
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
       });
       O.each([&](int i, int v, float& x) { x *= sb[i]; });
     }
-    __syncthreads();
+    lds_barrier();
     lds_to_global_t<D, C, LCO, NT>((OT*)p.sv_Dl + ch * C * D, sDt);  // Delta, row-major
     gemm_nt<OT, C, D, C, 1, DN, kWaves, LCO, LCO>(O, sM, sDt);
     {
@@ -305,10 +305,10 @@ __global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
       S.each([&](int, int, float& x) { x *= bn; });
       gemm_nt<OT, D, D, C, SM, SM, kWaves, LCO, LCO>(S, sKt, sDet);
     }
-    __syncthreads();
+    lds_barrier();
     state_to_lds();
     if (c + 1 < c1) commit();
-    __syncthreads();
+    lds_barrier();
   }
   if (p.ST) {
     float* st = p.ST + nh * D * D;
