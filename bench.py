@@ -29,26 +29,24 @@ PEAK = {"f32_mfma": 157.3e12, "bf16_mfma": 2.5e15, "hbm": 8.0e12}
 
 def kernel_model(name, C, D, Hk, Hv, n_chunks, es=2):
     """Algorithmic MFMA flops and HBM bytes of one launch of a kernel: the products it
-    forms and the tensors it must read and write, per unit of work (chunk x value head,
-    or chunk x key head), times the units of one launch. Activations are es bytes."""
-    r = Hv // Hk
+    forms and the tensors it must read and write, each counted once per unit of work
+    (chunk x value head, or chunk x key head for what the r value heads of a key head
+    share), times the units of one launch. Activations are es bytes, gates float32."""
     ch, ck = n_chunks * Hv, n_chunks * Hk  # (chunk, value head) and (chunk, key head) units
     cd, cc, dd = C * D * es, C * C * es, D * D * es
+    gates = 8 * C  # gamma and beta (or g and beta) per unit, float32
     model = {
-        # K K^T, Q K^T per key head; W = T diag(beta b) K, U = T diag(beta) V per value head.
-        # Reads K, Q, V, g, beta; writes K^T, Q^T, and per value head gamma, M, T^T, W, U^T, (diag(b) Q)^T.
-        "k_prep": (ck * (4 * C * C * D) + ch * (4 * C * C * D),
-                   ck * (4 * cd) + ch * (cd + 8 * C + 4 * C + 2 * cc + 3 * cd)),
-        # W S, Q S, K^T (e o Delta), M Delta. Reads W, Q, M, K^T, U^T, gamma; writes S, Delta, O.
-        "k_sweep": (ch * (6 * C * D * D + 2 * C * C * D), ch * (4 * cd + cc + 4 * C + dd + 2 * cd)),
-        # K dS, (diag(b) Q)^T dO, W^T dDelta, M^T dO. Reads M, dO, K, (diag(b) Q)^T, W, gamma;
-        # writes dS, dDelta^T.
-        "k_bwd_sweep": (ch * (6 * C * D * D + 2 * C * C * D), ch * (cc + 4 * cd + 4 * C + dd + cd)),
+        # K K^T and Q K^T per key head. Reads K, Q, g, beta; writes T, M and the gate record.
+        "k_prep": (ck * 4 * C * C * D, ck * 2 * cd + ch * (gates + 2 * cc + gates)),
+        # K S, Q S, T X, M Delta, K^T (e o Delta). Reads K, Q, V, T, M, gates; writes S, Delta, O.
+        "k_fwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + gates + dd + 2 * cd)),
+        # K dS, M^T dO, T^T dDelta, Q^T dO, K^T Z. Reads K, Q, dO, T, M, gates; writes dS, dDelta.
+        "k_bwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + gates + dd + cd)),
         # T^T dDelta, dO S0^T, Delta dS^T, A S0^T, dO Delta^T, A Delta^T, (P o Gamma) K,
-        # (P o Gamma)^T Q, G^T K, G' K. Reads S0, dS, Delta, dO, V, dDelta^T, T^T, gamma, beta, g
-        # per value head and K^T, Q^T per key head; writes dV, dg, dbeta and dq, dk.
+        # (P o Gamma)^T Q, G^T K, G' K. Reads S0, dS, Delta, dDelta, dO, V, T, gates, g per
+        # value head and K, Q per key head; writes dV, dg, dbeta and dq, dk.
         "k_bwd_grad": (ch * (6 * C * D * D + 14 * C * C * D),
-                       ch * (2 * dd + 4 * cd + cc + 12 * C + cd + 8 * C) + ck * (4 * cd)),
+                       ch * (2 * dd + 4 * cd + cc + gates + 4 * C + cd + 8 * C) + ck * 4 * cd),
     }
     return model.get(name)
 

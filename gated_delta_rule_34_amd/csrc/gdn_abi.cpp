@@ -50,8 +50,8 @@ gdn_status check_problem(const gdn_problem* p) {
 
 // Region sizes in bytes (each rounded up to 256 B).
 struct Regions {
-  size_t chunks, seq_chunk;      // chunk table
-  size_t oS, oW, oM, oKt, gam;   // [c][h][D][D], [c][h][C][D], [c][h][C][C], [c][kh][D][C], [c][h][C] f32
+  size_t chunks, seq_chunk;        // chunk table, first chunk per sequence
+  size_t oDD, oCD, oCC, gb;        // per (chunk, value head): [D][D], [D][C], [C][C] elements, [2][C] f32
 };
 
 Regions regions(const gdn_problem* p) {
@@ -60,57 +60,52 @@ Regions regions(const gdn_problem* p) {
   Regions r;
   r.chunks = align_up(nc * sizeof(gdn::ChunkInfo));
   r.seq_chunk = align_up(((size_t)p->N + 1) * sizeof(int));
-  r.oS = align_up(nc * Hv * D * D * es);
-  r.oW = align_up(nc * Hv * C * D * es);
-  r.oM = align_up(nc * Hv * C * C * es);
-  r.oKt = align_up(nc * (size_t)p->Hk * D * C * es);
-  r.gam = align_up(nc * Hv * C * sizeof(float));
+  r.oDD = align_up(nc * Hv * D * D * es);
+  r.oCD = align_up(nc * Hv * C * D * es);
+  r.oCC = align_up(nc * Hv * C * C * es);
+  r.gb = align_up(nc * Hv * 2 * C * sizeof(float));
   return r;
 }
 
 size_t fwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.oW;  // table, U^T
+  return r.chunks + r.seq_chunk;
 }
 
 size_t bwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.oS + r.oW;  // table, dS per chunk, dDelta^T
+  return r.chunks + r.seq_chunk + r.oDD + r.oCD;  // + dS^T and dDelta^T per chunk
 }
 
-// Saved activations: S, W, Delta, (diag(b) Q)^T, M, T^T, gamma, K^T, Q^T.
+// Saved activations: S^T, Delta^T, T, M per chunk and value head, and the gate record.
 size_t saved_bytes(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.oS + 3 * r.oW + 2 * r.oM + r.gam + 2 * r.oKt;
+  return r.oDD + r.oCD + 2 * r.oCC + r.gb;
 }
 
 void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
   char* b = static_cast<char*>(saved);
   P.sv_S = b;
-  b += r.oS;
-  P.sv_W = b;
-  b += r.oW;
-  P.sv_Dl = b;
-  b += r.oW;
-  P.sv_Qbt = b;
-  b += r.oW;
+  b += r.oDD;
+  P.sv_Dt = b;
+  b += r.oCD;
+  P.sv_T = b;
+  b += r.oCC;
   P.sv_M = b;
-  b += r.oM;
-  P.sv_Tt = b;
-  b += r.oM;
-  P.sv_gam = reinterpret_cast<float*>(b);
-  b += r.gam;
-  P.sv_Kt = b;
-  b += r.oKt;
-  P.sv_Qt = b;
+  b += r.oCC;
+  P.sv_gb = reinterpret_cast<float*>(b);
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-gdn_status check_view(const void* ptr, int64_t rs, int64_t width, int esize, int64_t T_total) {
+// Kernels address one chunk of rows with 32-bit byte offsets: chunk * rs * esize < 2^31.
+constexpr int64_t kMaxChunkSpan = (int64_t)1 << 31;
+
+gdn_status check_view(const void* ptr, int64_t rs, int64_t width, int esize, int64_t T_total, int chunk) {
   if (T_total == 0) return GDN_OK;
   if (!ptr) return GDN_EINVAL;
   if (rs < width) return GDN_EINVAL;
+  if ((int64_t)chunk * rs * esize >= kMaxChunkSpan) return GDN_EINVAL;
   if (!aligned(ptr, 16) || ((size_t)rs * esize) % 16) return GDN_EALIGN;
   return GDN_OK;
 }
@@ -168,10 +163,10 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   GDN_TRY(check_problem(p));
   const int es = p->dtype == GDN_BF16 ? 2 : 4;
   const int64_t qkw = (int64_t)p->Hk * p->Dk, vw = (int64_t)p->Hv * p->Dv;
-  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total));
-  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total));
-  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total));
-  GDN_TRY(check_view(o, o_rs, vw, es, p->T_total));
+  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(o, o_rs, vw, es, p->T_total, p->chunk));
   GDN_TRY(check_f32(g, p->T_total > 0));
   GDN_TRY(check_f32(beta, p->T_total > 0));
   GDN_TRY(check_f32(S0, false, 16));
@@ -194,7 +189,6 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   Carver cv{static_cast<char*>(workspace)};
   P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
   P.seq_chunk = cv.take<int>(r.seq_chunk);
-  P.ws_Ut = cv.take<void>(r.oW);
   const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
@@ -207,13 +201,13 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   GDN_TRY(check_problem(p));
   const int es = p->dtype == GDN_BF16 ? 2 : 4;
   const int64_t qkw = (int64_t)p->Hk * p->Dk, vw = (int64_t)p->Hv * p->Dv;
-  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total));
-  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total));
-  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total));
-  GDN_TRY(check_view(dO, dO_rs, vw, es, p->T_total));
-  GDN_TRY(check_view(dq, dq_rs, qkw, es, p->T_total));
-  GDN_TRY(check_view(dk, dk_rs, qkw, es, p->T_total));
-  GDN_TRY(check_view(dv, dv_rs, vw, es, p->T_total));
+  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(dO, dO_rs, vw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(dq, dq_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(dk, dk_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(dv, dv_rs, vw, es, p->T_total, p->chunk));
   GDN_TRY(check_f32(g, p->T_total > 0));
   GDN_TRY(check_f32(beta, p->T_total > 0));
   GDN_TRY(check_f32(dg, p->T_total > 0));
@@ -241,8 +235,8 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   Carver cv{static_cast<char*>(workspace)};
   P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
   P.seq_chunk = cv.take<int>(r.seq_chunk);
-  P.ws_dS = cv.take<void>(r.oS);
-  P.ws_dDt = cv.take<void>(r.oW);
+  P.ws_dS = cv.take<void>(r.oDD);
+  P.ws_dDt = cv.take<void>(r.oCD);
   const hipError_t e = gdn::launch_backward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }

@@ -3,423 +3,576 @@
 // Per-token form: lattice-inference gdn_backward.rs, gdn_backward steps 4a-4d (output,
 // state update, delta, retrieval), with the state adjoint dS carried in reverse time.
 // Chunk form (derived here; the pages give none), with dO~ = scale dO, e = exp(gamma_n -
-// gamma) and dS_C the adjoint flowing into the end of a chunk:
-//   dDelta = M^T dO~ + diag(e) K dS_C                     (M = Gamma o Q K^T, lower incl.)
-//   dS_0   = b_n dS_C + (diag(b) Q)^T dO~ - W^T dDelta    (carried to the previous chunk)
-//   XQ = dO~ S0^T,  XW = dDelta S0^T,  XK = Delta dS_C^T,  P = tril(dO~ Delta^T)
+// gamma), M = Gamma o Q K^T (lower incl.) and dS_C the adjoint flowing into the end of a
+// chunk:
+//   dDelta = M^T dO~ + diag(e) K dS_C
+//   dS_0   = b_n dS_C + Q^T diag(b) dO~ - K^T diag(beta b) T^T dDelta   (W^T = K^T diag(beta b) T^T)
+//   XQ = dO~ S0^T,  XK = Delta dS_C^T,  A = T^T dDelta,  Y = A S0^T,  P = tril(dO~ Delta^T)
 //   dQ     = diag(b) XQ + (P o Gamma) K
-//   dV     = diag(beta) T^T dDelta;  dK_beta_b = -T^T XW = -(T^T dDelta) S0^T
-//   dT     = dDelta (diag(beta) V)^T - XW (diag(beta b) K)^T;  dL = strictly_lower(-T^T dT T^T)
-//   dK     = (P o Gamma)^T Q + diag(e) XK + diag(beta b) dK_beta_b + G K + G^T K,
-//            G = dL o (beta_i Gamma_ij)
-//   dbeta  = rowsum(dV / beta o V) + b o rho + rowsum(dL o Gamma o K K^T),
-//            rho = rowsum(dK_beta_b o K) = -colsum(T o (XW K^T))
+//   dV     = diag(beta) A;  dL = -stril(A Delta^T)   (dT = dDelta ((I + L) Delta)^T, T (I + L) = I)
+//   dK     = (P o Gamma)^T Q + diag(e) XK - diag(beta b) Y + G K + G^T K,  G = dL o (beta_i Gamma_ij)
+//   dbeta  = rowsum(A o V) + b o rho + rowsum(dL o Gamma o K K^T),  rho = -rowsum(Y o K)
 //   dgamma = b o rowsum(Q o XQ) + beta b rho - ebar + rowsum(Gbar o Gamma) - colsum(Gbar o Gamma),
 //            ebar = e o rowsum(K o XK), Gbar o Gamma = P o M + dL o beta_i K K^T o Gamma,
 //            and the last valid row also gets b_n <S0, dS_C> + sum(ebar)
 //   dlog g = reverse cumulative sum of dgamma within the chunk;  dg = dlog g / g.
 //
 // Kernels after the chunk table:
-//  k_bwd_sweep (sequence x value head, 16 waves): the reverse chunk-serial pass; the
-//      adjoint lives in float32 MFMA accumulators; saves dS_C, dDelta and dDelta^T.
-//  k_bwd_grad  (chunk x key head, 16 waves): all remaining gradients for the r value
-//      heads of the key head, one head after the other. Every operand arrives in the
-//      layout its product reads (no transposes while staging). dq and dk of the key
-//      head are summed over its value heads in ascending order in registers and stored
-//      once: no atomics, every run is bit-identical. Row sums go through partial arrays
-//      indexed by tile column block and are added in a fixed order.
+//  k_bwd_sweep (sequence x value head, one wave per 32 adjoint columns): the reverse
+//      chunk-serial pass; dS, K dS, dDelta and T^T dDelta stay in float32 accumulators.
+//      Saves dS_C and dDelta per chunk.
+//  k_bwd_grad (chunk x key head, 8 waves): all remaining gradients for the r value heads
+//      of the key head, one head after the other, streaming the value dimension in
+//      blocks (the next block in flight while the current one is used). dq and dk of
+//      the key head are summed over its value heads in ascending order in registers and
+//      stored once: no atomics, every run is bit-identical. Row sums go through partial
+//      arrays indexed by column block and are added in a fixed order.
 #include "gdn_common.h"
-#include "gdn_mma.h"
 
 namespace gdn {
 
-constexpr int kWavesB = 16;
-constexpr int kWavesG = 8;  // k_bwd_grad
-constexpr int kThreadsG = kWavesG * 64;
-constexpr int kThreadsB = kWavesB * 64;
-
-__host__ __device__ constexpr int bblk2(int x) { return x >= 32 ? 2 : 1; }
-
-// Row sums of f(i, j, x) over an accumulator tile, added into red[column block][M].
-// Each (row block, column block) belongs to one wave, so no two waves touch the same
-// entry; the caller adds the column-block partials in order after a barrier.
-template <int M, int N, int TM, int TN, int NWV, class F>
-__device__ __forceinline__ void acc_rowsum(Tile<M, N, TM, TN, NWV>& t, F&& f, float* red) {
-  using B = Blk<M, N, TM, TN, NWV>;
-  const int w = threadIdx.x / 64, l = threadIdx.x & 63;
-#pragma unroll
-  for (int q = 0; q < B::PER; ++q) {
-    const int b = w + q * NWV;
-    if (b < B::NB) {
-      const int cb = b % B::BN, bi = (b / B::BN) * 16 * TM, bj = cb * 16 * TN;
-#pragma unroll
-      for (int x = 0; x < TM; ++x) {
-        const int i0 = bi + x * 16 + (l >> 4) * 4;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int y = 0; y < TN; ++y) {
-          const int j = bj + y * 16 + (l & 15);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += f(i0 + e, j, t.a[q][x][y][e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = row16_sum(v[e]);
-        if ((l & 15) == 0)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) red[cb * M + i0 + e] += v[e];
-      }
-    }
-  }
-}
-
-// Column sums, added into red[row block][N].
-template <int M, int N, int TM, int TN, int NWV, class F>
-__device__ __forceinline__ void acc_colsum(Tile<M, N, TM, TN, NWV>& t, F&& f, float* red) {
-  using B = Blk<M, N, TM, TN, NWV>;
-  const int w = threadIdx.x / 64, l = threadIdx.x & 63;
-#pragma unroll
-  for (int q = 0; q < B::PER; ++q) {
-    const int b = w + q * NWV;
-    if (b < B::NB) {
-      const int rb = b / B::BN, bi = rb * 16 * TM, bj = (b % B::BN) * 16 * TN;
-#pragma unroll
-      for (int y = 0; y < TN; ++y) {
-        const int j = bj + y * 16 + (l & 15);
-        float v = 0.f;
-#pragma unroll
-        for (int x = 0; x < TM; ++x)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v += f(bi + x * 16 + (l >> 4) * 4 + e, j, t.a[q][x][y][e]);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (l < 16) red[rb * N + j] += v;
-      }
-    }
-  }
+template <typename OT> __device__ __forceinline__ void store4b(OT* dst, f32x4 x) {
+  if constexpr (sizeof(OT) == 2)
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  else
+    *reinterpret_cast<f32x4*>(dst) = x;
 }
 
 // ---------------------------------------------------------------------------- sweep
-// Grid (N, Hv). Reverse chunk-serial pass over one sequence and one value head.
-template <typename TI, int C, int D>
-__global__ __launch_bounds__(kThreadsB) void k_bwd_sweep(Prob p) {
-  using OT = TI;
-  constexpr int NT = kThreadsB, NWV = kWavesB, LDO = D + 8, LCO = C + 8;
-  constexpr int SM = bblk2(D), DN = bblk2(D);
-  __shared__ __align__(16) OT sMt[C * LCO];   // M^T
-  __shared__ __align__(16) OT sOt[D * LCO];   // dO~^T
-  __shared__ __align__(16) OT sK[C * LDO];    // K
-  __shared__ __align__(16) OT sQbt[D * LCO];  // (diag(b) Q)^T
-  __shared__ __align__(16) OT sWt[D * LCO];   // -W^T
-  __shared__ __align__(16) OT sdSt[D * LDO];  // dS^T: [v][d]
-  __shared__ __align__(16) OT sdDt[D * LCO];  // dDelta^T: [v][i]
-  __shared__ float sg[C], se[C];
-  typedef OT o4 __attribute__((ext_vector_type(4)));
+template <typename TI, int C, int D> struct BwCfg {
+  static constexpr int WC = 16;  // adjoint columns per wave: two waves per SIMD at D = 128
+  static constexpr int NW = D / WC;
+  static constexpr int CT = WC / 16, DT = D / 16, RT = C / 16;
+  // One LDS buffer: K, Q, dO [C][D] and T, M [C][C], all Swz layouts.
+  static constexpr int O_K = 0, O_Q = C * D, O_O = 2 * C * D, O_T = 3 * C * D, O_M = O_T + C * C, BUF = O_M + C * C;
+};
 
-  const int n = blockIdx.x, h = blockIdx.y, kh = h / p.r;
+template <typename OT, int K, int MT, int NT, class FA, class FB>
+__device__ __forceinline__ void wave_mm_cm(f32x4 (&acc)[NT][MT], FA&& fa, FB&& fb) {
+  constexpr int KS = ks_of<OT, K>();
+  using M = Mf<OT, KS>;
+#pragma unroll
+  for (int s = 0; s < K / KS; ++s) {
+    typename M::frag b[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) b[n] = fb(n, s);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const typename M::frag a = fa(m, s);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n][m] = M::run(a, b[n], acc[n][m]);
+    }
+  }
+}
+
+// Saved rows X^T[v][j] of a wave's accumulator tiles, in RowOrd<OT, LEN> order (the same
+// writer as the forward's: fragment order stores each lane's 16-byte fragment at once).
+template <typename OT, int LEN, int CT, int NT, int NS>
+__device__ __forceinline__ void save_rows_b(OT* dst, int v0, const f32x4 (&Xc)[CT][NT],
+                                            const typename Mf<OT, ks_of<OT, LEN>()>::frag (&frag)[CT][NS]) {
+  const int l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    OT* row = dst + (size_t)(v0 + 16 * ct + r16) * LEN;
+    if constexpr (RowOrd<OT, LEN>::frag) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) *reinterpret_cast<bf16x8*>(row + 32 * s + 2 * g4) = frag[ct][s];
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) store4b(row + 16 * t + g4, Xc[ct][t]);
+    }
+  }
+}
+
+// Grid xcd_grid(N * Hk, r). Reverse chunk-serial pass over one sequence and one value head.
+template <typename TI, int C, int D>
+__global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p) {
+  using OT = TI;
+  using CF = BwCfg<TI, C, D>;
+  constexpr int NW = CF::NW, WC = CF::WC, CT = CF::CT, DT = CF::DT, RT = CF::RT;
+  constexpr int KSD = ks_of<OT, D>(), KSC = ks_of<OT, C>(), NSD = D / KSD, NSC = C / KSC;
+  using LD = Swz<OT, D>;
+  using LC = Swz<OT, C>;
+  using FragD = typename Mf<OT, KSD>::frag;
+  using FragC = typename Mf<OT, KSC>::frag;
+  __shared__ __align__(16) OT sbuf[2][CF::BUF];
+  __shared__ __align__(16) float sgb[2][2 * C];
+
+  int grp, hh;
+  if (!xcd_group(blockIdx.x, p.N * p.Hk, p.r, grp, hh)) return;
+  const int n = grp / p.Hk, kh = grp % p.Hk, h = kh * p.r + hh;
   const size_t nh = (size_t)n * p.Hv + h;
   const int c0 = p.seq_chunk[n], c1 = p.seq_chunk[n + 1];
-  using TS = Tile<D, D, SM, SM, NWV>;
-  using TD = Tile<C, D, 1, DN, NWV>;
-  TS dS;
+  int64_t sa, sb;  // rows of the sequence; chunk c starts at sa + (c - c0) C (as in the chunk table)
+  seq_bounds(p, n, sa, sb);
+  const int w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
+  const int v0 = w * WC;
+
+  TileDma<C, D, NW, OT> dmD;         // K, Q, dO
+  TileDma<C, C, NW, OT> dmC;         // T, M
+  TileDma<1, 2 * C, NW, float> dmG;  // gate record
+  dmD.init(w);
+  dmC.init(w);
+  dmG.init(w);
+  auto issue = [&](int c, int buf) {
+    const int64_t t0 = sa + (int64_t)(c - c0) * C;
+    const int len = (int)(sb - t0 < C ? sb - t0 : C);
+    const size_t ch = ch_idx(p, c, h);
+    OT* b = sbuf[buf];
+    dmD.issue(b + CF::O_K, (const OT*)p.k + t0 * p.k_rs + kh * D, p.k_rs, len, w);
+    dmD.issue(b + CF::O_Q, (const OT*)p.q + t0 * p.q_rs + kh * D, p.q_rs, len, w);
+    dmD.issue(b + CF::O_O, (const OT*)p.dO + t0 * p.dO_rs + h * D, p.dO_rs, len, w);
+    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
+    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
+    dmG.issue(sgb[buf], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+  };
+
+  // The adjoint: dS[ct][dt] holds dS[16 dt + g4 + e][v0 + 16 ct + r16].
+  f32x4 dS[CT][DT];
   if (p.dST) {
     const float* s = p.dST + nh * D * D;
-    dS.each([&](int d, int v, float& x) { x = s[d * D + v]; });
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dS[ct][dt][e] = s[(16 * dt + g4 + e) * D + v0 + 16 * ct + r16];
   } else {
-    dS.zero();
+    zero(dS);
   }
 
-  Stage<C, C, NT, OT> nM;
-  Stage<C, D, NT, TI> nO, nK;
-  Stage<D, C, NT, OT> nQb;
-  Stage<C, D, NT, OT> nW;
-  float ng = 0.f;
-  auto issue = [&](int c) {
-    const ChunkInfo ci = p.chunks[c];
+  if (c0 < c1) issue(c1 - 1, 0);
+  int buf = 0;
+  for (int c = c1 - 1; c >= c0; --c, buf ^= 1) {
+    dma_wait();
+    lds_barrier();
+    if (c - 1 >= c0) issue(c - 1, buf ^ 1);
     const size_t ch = ch_idx(p, c, h);
-    nM.issue((const OT*)p.sv_M + ch * C * C, C, C);
-    nO.issue((const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D, p.dO_rs, ci.len);
-    nK.issue((const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, ci.len);
-    nQb.issue((const OT*)p.sv_Qbt + ch * D * C, C, D);
-    nW.issue((const OT*)p.sv_W + ch * C * D, D, C);
-    if (threadIdx.x < C) ng = p.sv_gam[ch * C + threadIdx.x];
-  };
-  auto commit = [&]() {
-    nM.template to_cols<LCO>(sMt);
-    nO.template to_cols<LCO>(sOt, nullptr, p.scale);
-    nK.template to_rows_raw<LDO>(sK);
-    nQb.template to_rows_raw<LCO>(sQbt);
-    nW.template to_cols<LCO>(sWt, nullptr, -1.f);
-    if (threadIdx.x < C) sg[threadIdx.x] = ng;
-  };
-  auto adj_to_lds = [&]() {
-    dS.each4([&](int d0, int v, f32x4& x) {
-      *reinterpret_cast<o4*>(sdSt + v * LDO + d0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
-    });
-  };
-
-  if (c0 < c1) {
-    issue(c1 - 1);
-    commit();
-  }
-  adj_to_lds();
-  lds_barrier();
-  for (int c = c1 - 1; c >= c0; --c) {
-    const size_t ch = ch_idx(p, c, h);
-    lds_to_global_t<D, D, LDO, NT>((OT*)p.ws_dS + ch * D * D, sdSt);  // dS_C, key-major
-    if (threadIdx.x < C) se[threadIdx.x] = expf(sg[C - 1] - sg[threadIdx.x]);
-    const float bn = expf(sg[C - 1]);
-    if (c - 1 >= c0) issue(c - 1);
-    TD dD;
-    dD.zero();
-    gemm_nt<OT, C, D, D, 1, DN, NWV, LDO, LDO>(dD, sK, sdSt);  // K dS
-    dS.each([&](int, int, float& x) { x *= bn; });
-    gemm_nt<OT, D, D, C, SM, SM, NWV, LCO, LCO>(dS, sQbt, sOt);  // + (diag(b) Q)^T dO~
-    lds_barrier();  // se visible
-    dD.each([&](int i, int, float& x) { x *= se[i]; });
-    gemm_nt<OT, C, D, C, 1, DN, NWV, LCO, LCO>(dD, sMt, sOt);  // + M^T dO~
-    dD.each4([&](int i0, int v, f32x4& x) {
-      *reinterpret_cast<o4*>(sdDt + v * LCO + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
-    });
-    lds_barrier();
-    gemm_nt<OT, D, D, C, SM, SM, NWV, LCO, LCO>(dS, sWt, sdDt);  // - W^T dDelta
-    lds_to_global<D, C, LCO, NT>((OT*)p.ws_dDt + ch * D * C, sdDt);
-    lds_barrier();
-    adj_to_lds();
-    if (c - 1 >= c0) commit();
-    lds_barrier();
+    const OT* sK = sbuf[buf] + CF::O_K;
+    const OT* sQ = sbuf[buf] + CF::O_Q;
+    const OT* sO = sbuf[buf] + CF::O_O;
+    const OT* sT = sbuf[buf] + CF::O_T;
+    const OT* sM = sbuf[buf] + CF::O_M;
+    const float* gam = sgb[buf];  // log2 units
+    const float* bet = gam + C;
+    const float gn = gam[C - 1], bn = __builtin_amdgcn_exp2f(gn), sc = p.scale;
+    float ex[RT][4], sbx[RT][4], nbb[RT][4];  // e_i, scale b_i, -beta_i b_i
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * t + g4);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * t + g4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float b = __builtin_amdgcn_exp2f(gv[e]);
+        ex[t][e] = __builtin_amdgcn_exp2f(gn - gv[e]);
+        sbx[t][e] = sc * b;
+        nbb[t][e] = -bv[e] * b;
+      }
+    }
+    // dS_C's fragments (B operand over d) and its saved copy dS^T[v][d]
+    FragD dSb[CT][NSD];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int s = 0; s < NSD; ++s) dSb[ct][s] = from_acc<OT, KSD>(dS[ct], s, Ident{});
+    save_rows_b<OT, D, CT, DT, NSD>((OT*)p.ws_dS + ch * D * D, v0, dS, dSb);
+    // dDelta = e o (K dS) + scale M^T dO
+    f32x4 dD[CT][RT];
+    {
+      f32x4 KdS[RT][CT], MdO[RT][CT];
+      zero(KdS);
+      zero(MdO);
+      wave_mm<OT, D, RT, CT>(KdS, [&](int m, int s) { return ld_n<OT, KSD, ACC, LD>(sK, 16 * m, s); },
+                             [&](int j, int s) { return dSb[j][s]; });
+      wave_mm<OT, C, RT, CT>(MdO, [&](int m, int s) { return ld_t<OT, KSC, STD, LC>(sM, 16 * m, s); },
+                             [&](int j, int s) { return ld_t<OT, KSC, STD, LD>(sO, v0 + 16 * j, s); });
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dD[ct][t][e] = ex[t][e] * KdS[t][ct][e] + sc * MdO[t][ct][e];
+    }
+    FragC dDb[CT][NSC];  // dDelta's fragments: B operand of T^T dDelta and the saved copy
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int s = 0; s < NSC; ++s) dDb[ct][s] = from_acc<OT, KSC>(dD[ct], s, Ident{});
+    save_rows_b<OT, C, CT, RT, NSC>((OT*)p.ws_dDt + ch * D * C, v0, dD, dDb);  // dDelta^T[v][i]
+    // Z = T^T dDelta
+    f32x4 Z[CT][RT];
+    zero(Z);
+    wave_mm_cm<OT, C, RT, CT>(Z, [&](int m, int s) { return ld_t<OT, KSC, ACC, LC>(sT, 16 * m, s); },
+                              [&](int j, int s) { return dDb[j][s]; });
+    // dS <- b_n dS + Q^T (scale b o dO) - K^T (beta b o Z)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dS[ct][dt] *= bn;
+    wave_mm_cm<OT, C, DT, CT>(
+        dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sQ, 16 * m, s); },
+        [&](int j, int s) { return scale_acc<OT, KSC, RT>(ld_t<OT, KSC, ACC, LD>(sO, v0 + 16 * j, s), s, sbx); });
+    wave_mm_cm<OT, C, DT, CT>(
+        dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sK, 16 * m, s); },
+        [&](int j, int s) {
+          return from_acc<OT, KSC>(Z[j], s, [&](int t, int e, float x) { return nbb[t][e] * x; });
+        });
   }
   if (p.dS0) {
     float* s = p.dS0 + nh * D * D;
-    dS.each([&](int d, int v, float& x) { s[d * D + v] = x; });
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[(16 * dt + g4 + e) * D + v0 + 16 * ct + r16] = dS[ct][dt][e];
   }
 }
 
 // ---------------------------------------------------------------------------- grad
+// Tile ownership of an R x Cc grid of 16 x 16 tiles over NW waves (R, Cc powers of two,
+// R <= NW): wave w owns row tile w % WR and the NT column tiles from (w / WR) NT. Every
+// product with the same grid gives a wave the same tiles, so their accumulators combine
+// elementwise. cb = w / WR indexes the wave's column block in partial row sums.
+template <int R, int Cc, int NW> struct Own {
+  static_assert(R <= NW, "one row tile per wave at most");
+  static constexpr int WR = R, WCc = NW / R;
+  static constexpr int NT = Cc >= WCc ? Cc / WCc : 1;
+  __device__ __forceinline__ static bool active(int w) { return (w / WR) * NT < Cc; }
+  __device__ __forceinline__ static int m(int w) { return w % WR; }
+  __device__ __forceinline__ static int n0(int w) { return (w / WR) * NT; }
+  __device__ __forceinline__ static int cb(int w) { return w / WR; }
+};
+
 // Row-vector slots of the partial sums in k_bwd_grad.
 enum { R_EBAR = 0, R_DB1, R_RQ, R_RHO, R_DB3, R_GROW, R_GCOL, R_NSLOT };
-constexpr int kRedBlocks = 4;  // column blocks per partial-sum slot
+
+constexpr int kWavesG = 8;
+constexpr int kThreadsG = kWavesG * 64;
 
 template <typename TI, int C, int D> struct GradCfg {
   static constexpr int E = (int)sizeof(TI);
   static constexpr int BV = E == 2 ? (D >= 32 ? 32 : D) : 16;  // value columns per block
   static constexpr int NBH = D / BV;                            // blocks per head
-  static constexpr bool DBUF = NBH % 2 == 0;  // blocks alternate between two buffers
-  // One block buffer (element offsets): S0 and dS_C column blocks [D][BV] (key-major),
-  // Delta, dO, V and A = T^T dDelta column blocks [C][BV], dDelta^T row block [BV][C].
-  static constexpr int O_S0 = 0, O_DS = D * BV, O_DL = 2 * D * BV, O_DO = O_DL + C * BV, O_V = O_DO + C * BV,
-                       O_A = O_V + C * BV, O_DDT = O_A + C * BV, BUF = O_DDT + BV * C;
-  // Scratch of the second phase (padded rows of LC = C + 8): P o Gamma, its transpose,
-  // G' = dL o Gamma, and G^T = (diag(beta) G')^T.
-  static constexpr int LC = C + 8, SCR = 4 * C * LC;
-  // With two buffers the scratch shares the second one (free once the head's last block,
-  // which always sits there, is consumed); otherwise it has its own array.
-  static constexpr int BUFY = DBUF ? (BUF > SCR ? BUF : SCR) : 16;
-  static constexpr int SCRZ = DBUF ? 16 : SCR;
-  static_assert(BUF >= 2 * C * D, "dq/dk staging must fit the first buffer");
+  static constexpr int RT = C / 16;
+  static constexpr int NCB = kWavesG / RT;  // column blocks of the partial row sums
+  // One block buffer (elements): S0^T and dS^T row blocks [BV][D], Delta^T and dDelta^T
+  // row blocks [BV][C], dO and V column blocks [C][BV].
+  static constexpr int O_S0 = 0, O_DS = BV * D, O_DL = 2 * BV * D, O_DD = O_DL + BV * C, O_DO = O_DD + BV * C,
+                       O_V = O_DO + C * BV, BUF = O_V + C * BV;
+  // Scratch of the second phase: P o Gamma, G' = dL o Gamma and diag(beta) G', [C][C] each.
+  static constexpr int SCR = 3 * C * C;
+  // With an even block count the last block of every head sits in the second buffer,
+  // which is free during the second phase: the scratch shares it when it fits.
+  static constexpr bool SHARE = NBH % 2 == 0 && SCR <= BUF;
+  static constexpr int SCRZ = SHARE ? 16 : SCR;
+  static_assert(BUF >= 2 * C * D, "dq/dk staging must fit a block buffer");
 };
 
-// Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk, one head
-// after the other; dq and dk of the key head stay in registers across its value heads.
-//
-// Phase 1 streams the value dimension in blocks of BV columns (global -> LDS by direct
-// loads, the next block in flight while the current one is used) and accumulates
-//   A = T^T dDelta (per block, to LDS), dV = diag(beta) A, rowsum(A o V), <S0, dS_C>,
-//   XQ += dO S0^T,  XK += Delta dS_C^T,  Y += A S0^T,  P += dO Delta^T,  AD += A Delta^T,
-// with dO unscaled (the scale is applied afterwards). Since (I + L) Delta is exactly the
-// right factor of dT, dL = -stril(T^T dT T^T) reduces to -stril(A Delta^T) = -stril(AD),
-// and the W-path gradient of K is -diag(beta b) Y with rho = -rowsum(Y o K).
-// Phase 2 forms Zq = (P o Gamma) K, Zk = (P o Gamma)^T Q, Z1 = G' K and Z2 = G^T K on MFMA
-// and folds them into dq and dk. The row and column sums of Gbar o Gamma that the gate
-// gradient needs are row sums against Q and K of these same products:
-//   rowsum(P o M) = rowsum(Q o Zq),   colsum(P o M) = rowsum(K o Zk),
-//   rowsum(dL o Gamma o K K^T) = rowsum(K o Z1),   colsum(beta_i dL o Gamma o K K^T) = rowsum(K o Z2),
-// so neither K K^T nor M is needed here.
+// Row sums of f(i, j, x) over a wave's accumulator tiles, added into red[cb][i].
+template <int NT, class F>
+__device__ __forceinline__ void acc_rowsum(const f32x4 (&t)[NT], int m, int n0, F&& f, float* red) {
+  const int l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int y = 0; y < NT; ++y)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += f(y, e, t[y][e]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = row16_sum(v[e]);
+  if (r16 == 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[16 * m + g4 + e] += v[e];
+  (void)n0;
+}
+
+// Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk.
 template <typename TI, int C, int D>
 __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   using OT = TI;
   using CF = GradCfg<TI, C, D>;
-  constexpr int NT = kThreadsG, NWV = kWavesG, BV = CF::BV, NBH = CF::NBH;
-  constexpr int DN = bblk2(D), RS = kRedBlocks * C;
-  using LC = Swz<OT, C>;        // rows of C: K^T, Q^T, T^T, dDelta^T
-  using LB = Swz<OT, BV>;       // rows of BV: the column blocks
-  using LP = Pad<CF::LC>;       // scratch
-  using TCC = Tile<C, C, 1, 1, NWV>;
-  using TCD = Tile<C, D, 1, DN, NWV>;
-  using TCB = Tile<C, BV, 1, 1, NWV>;
-  static_assert(TCD::B::BN <= kRedBlocks && TCB::B::BN <= kRedBlocks, "partial-sum slots too small");
+  constexpr int NW = kWavesG, BV = CF::BV, NBH = CF::NBH, RT = CF::RT, NCB = CF::NCB;
+  constexpr int KSC = ks_of<OT, C>(), KSB = ks_of<OT, BV>();
+  using LD = Swz<OT, D>;
+  using LC = Swz<OT, C>;
+  using LB = Swz<OT, BV>;
+  using OD = Own<RT, D / 16, NW>;    // C x D products
+  using OC = Own<RT, C / 16, NW>;    // C x C products
+  using OB = Own<RT, BV / 16, NW>;   // C x BV products
+  using OrdD = RowOrd<OT, D>;        // storage order of the saved S^T and dS^T rows
+  using OrdC = RowOrd<OT, C>;        // storage order of the saved Delta^T and dDelta^T rows
+  constexpr int NTD = OD::NT, NTC = OC::NT, NTB = OB::NT;
+  static_assert(NTB == 1, "one tile per wave of a value block");
+  constexpr int RS = NCB * C;  // one partial-sum slot
 
-  __shared__ __align__(16) OT sKt[D * C];
-  __shared__ __align__(16) OT sQt[D * C];
-  __shared__ __align__(16) OT sTt[C * C];
-  __shared__ __align__(16) OT sX[CF::BUF];
-  __shared__ __align__(16) OT sY[CF::BUFY];
+  __shared__ __align__(16) OT sK[C * D];
+  __shared__ __align__(16) OT sQ[C * D];
+  __shared__ __align__(16) OT sT[2][C * C];
+  __shared__ __align__(16) OT sB[2][CF::BUF];  // block buffers (job j uses sB[j & 1])
   __shared__ __align__(16) OT sZ[CF::SCRZ];
+  __shared__ __align__(16) OT sAt[BV * C];
+  __shared__ __align__(16) float sgb[2][2 * C];
   __shared__ float red[R_NSLOT * RS];
   __shared__ float rowv[R_NSLOT * C];
-  __shared__ float sg[C], sb[C], se[C], sbeta[C], sgate[C], swv[NWV];
+  __shared__ float sgate[C], swv[NW];
 
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int n = ci.len;
-  const int w = threadIdx.x / 64, lane = threadIdx.x & 63;
-  const size_t ck = (size_t)c * p.Hk + kh;
-  OT* const scr = CF::DBUF ? sY : sZ;
+  const int w = wave_id(), lane = lane_id(), g4 = (lane >> 4) * 4, r16 = lane & 15;
+  OT* scr;
+  if constexpr (CF::SHARE)
+    scr = sB[1];
+  else
+    scr = sZ;
   OT* const sPG = scr;
-  OT* const sPGt = scr + C * CF::LC;
-  OT* const sGp = scr + 2 * C * CF::LC;
-  OT* const sGt = scr + 3 * C * CF::LC;
+  OT* const sGp = scr + C * C;
+  OT* const sGb = scr + 2 * C * C;
 
-  auto issue_block = [&](OT* buf, int h, int blk) {
+  const int h0 = kh * p.r;
+  TileDma<BV, D, NW, OT> dmS;   // S0^T, dS^T row blocks
+  TileDma<BV, C, NW, OT> dmB;   // Delta^T, dDelta^T row blocks
+  TileDma<C, BV, NW, OT> dmV;   // dO, V column blocks
+  TileDma<C, C, NW, OT> dmC;    // T
+  TileDma<C, D, NW, OT> dmD;    // K, Q
+  TileDma<1, 2 * C, NW, float> dmG;  // gate record
+  dmS.init(w);
+  dmB.init(w);
+  dmV.init(w);
+  dmC.init(w);
+  dmD.init(w);
+  dmG.init(w);
+  auto issue_block = [&](int j) {  // job j = (head h0 + j / NBH, block j % NBH) into sB[j % 2]
+    const int h = h0 + j / NBH, v0 = (j % NBH) * BV;
     const size_t ch = ch_idx(p, c, h);
-    const int v0 = blk * BV;
-    dma_tile<D, BV, NT>(buf + CF::O_S0, (const OT*)p.sv_S + ch * D * D + v0, D, D);
-    dma_tile<D, BV, NT>(buf + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + v0, D, D);
-    dma_tile<C, BV, NT>(buf + CF::O_DL, (const OT*)p.sv_Dl + ch * C * D + v0, D, C);
-    dma_tile<C, BV, NT>(buf + CF::O_DO, (const TI*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n);
-    dma_tile<C, BV, NT>(buf + CF::O_V, (const TI*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n);
-    dma_tile<BV, C, NT>(buf + CF::O_DDT, (const OT*)p.ws_dDt + ch * D * C + (size_t)v0 * C, C, BV);
-  };
-  float ngam = 0.f, nbeta = 0.f, ngate = 1.f;
-  auto issue_head = [&](int h) {  // T^T and the per-row gate values of value head h
-    const size_t ch = ch_idx(p, c, h);
-    dma_tile<C, C, NT>(sTt, (const OT*)p.sv_Tt + ch * C * C, C, C);
-    if (threadIdx.x < C) {
-      const int i = threadIdx.x;
-      ngam = p.sv_gam[ch * C + i];
-      nbeta = i < n ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
-      ngate = i < n ? p.g[(int64_t)(ci.t0 + i) * p.Hv + h] : 1.f;
+    OT* b = sB[j & 1];
+    dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
+    dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
+    dmB.issue(b + CF::O_DL, (const OT*)p.sv_Dt + ch * D * C + (size_t)v0 * C, C, BV, w);
+    dmB.issue(b + CF::O_DD, (const OT*)p.ws_dDt + ch * D * C + (size_t)v0 * C, C, BV, w);
+    dmV.issue(b + CF::O_DO, (const OT*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n, w);
+    dmV.issue(b + CF::O_V, (const OT*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n, w);
+    if (j % NBH == 0) {  // first block of a head: its T and gate record
+      dmC.issue(sT[(j / NBH) & 1], (const OT*)p.sv_T + ch * C * C, C, C, w);
+      dmG.issue(sgb[(j / NBH) & 1], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
     }
   };
-  const int h0 = kh * p.r;
-  dma_tile<D, C, NT>(sKt, (const OT*)p.sv_Kt + ck * D * C, C, D);
-  dma_tile<D, C, NT>(sQt, (const OT*)p.sv_Qt + ck * D * C, C, D);
-  issue_head(h0);
-  issue_block(sX, h0, 0);
+  dmD.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
+  dmD.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
+  issue_block(0);
 
-  TCD dqf, dkf;  // dq, dk of the key head, summed over its value heads in order
-  dqf.zero();
-  dkf.zero();
+  const bool aD = OD::active(w), aC = OC::active(w), aB = OB::active(w);
+  const int mt = OD::m(w);  // the wave's row tile (the same in all three grids)
+  const int nD = OD::n0(w), nC = OC::n0(w), nB = OB::n0(w);
+  const int cbD = OD::cb(w), cbC = OC::cb(w), cbB = OB::cb(w);
+  (void)cbC;
 
+  f32x4 dqf[NTD], dkf[NTD];  // dq, dk of the key head, summed over its value heads in order
+#pragma unroll
+  for (int y = 0; y < NTD; ++y) dqf[y] = dkf[y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int njobs = p.r * NBH;
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = h0 + hh;
+    const OT* sTh = sT[hh & 1];
+    const float* gam = sgb[hh & 1];  // log2 units
+    const float* bet = gam + C;
     TI* dV = (TI*)p.dv + (int64_t)ci.t0 * p.dv_rs + h * D;
-    if (threadIdx.x < C) {
-      sg[threadIdx.x] = ngam;
-      sbeta[threadIdx.x] = nbeta;
-      sgate[threadIdx.x] = ngate;
-    }
-    for (int i = threadIdx.x; i < R_NSLOT * RS; i += NT) red[i] = 0.f;
+    if (threadIdx.x < C) sgate[threadIdx.x] = threadIdx.x < n ? p.g[(int64_t)(ci.t0 + threadIdx.x) * p.Hv + h] : 1.f;
+    for (int i = threadIdx.x; i < R_NSLOT * RS; i += kThreadsG) red[i] = 0.f;
 
-    // ---- phase 1
-    TCD XQ, XK, Y;
-    TCC P, AD;
-    XQ.zero();
-    XK.zero();
-    Y.zero();
-    P.zero();
-    AD.zero();
+    // ---- phase 1: stream the value dimension
+    f32x4 XQ[NTD], XK[NTD], Y[NTD], P[NTC], AD[NTC];
+#pragma unroll
+    for (int y = 0; y < NTD; ++y) XQ[y] = XK[y] = Y[y] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int y = 0; y < NTC; ++y) P[y] = AD[y] = f32x4{0.f, 0.f, 0.f, 0.f};
     float sdot = 0.f;
-    auto block = [&](OT* cur, OT* nxt, int b) {
+    for (int b = 0; b < NBH; ++b) {
+      const int j = hh * NBH + b;
+      const OT* cur = sB[j & 1];
       dma_wait();
-      lds_barrier();  // block b (and everything issued with it) is in LDS
-      if (b == 0 && threadIdx.x < C) {
-        sb[threadIdx.x] = expf(sg[threadIdx.x]);
-        se[threadIdx.x] = expf(sg[C - 1] - sg[threadIdx.x]);
-      }
-      if (b + 1 < NBH) issue_block(nxt, h, b + 1);
+      lds_barrier();  // job j (and K, Q, T, gates with it) is in LDS
+      if (j + 1 < njobs) issue_block(j + 1);
       const int v0 = b * BV;
-      {
-        TCB A;
-        A.zero();
-        gemm_l<OT, C, BV, C, 1, 1, NWV, LC, LC>(A, sTt, cur + CF::O_DDT);
-        A.each([&](int i, int j, float& x) {
-          if (i < n) dV[(int64_t)i * p.dv_rs + v0 + j] = (TI)(sbeta[i] * x);
-          cur[CF::O_A + LB::at(i, j)] = (OT)x;
-        });
-        acc_rowsum(A, [&](int i, int j, float x) { return x * (float)cur[CF::O_V + LB::at(i, j)]; },
-                   red + R_DB1 * RS);
+      const OT* sS0 = cur + CF::O_S0;
+      const OT* sDS = cur + CF::O_DS;
+      const OT* sDL = cur + CF::O_DL;
+      const OT* sDD = cur + CF::O_DD;
+      const OT* sDO = cur + CF::O_DO;
+      const OT* sV = cur + CF::O_V;
+      if (aB) {  // A = T^T dDelta for this block; dV = beta o A; A^T to LDS; rowsum(A o V)
+        f32x4 A[1][1];
+        zero(A);
+        // dDelta^T rows are stored in RowOrd<OT, C> order: a plain 16-byte read of a fragment-order
+        // row yields the ACC-order fragment, so T^T is read in ACC order to match.
+        constexpr int ORD_DD = RowOrd<OT, C>::frag ? ACC : STD;
+        wave_mm<OT, C, 1, 1>(A, [&](int, int s) { return ld_t<OT, KSC, ORD_DD, LC>(sTh, 16 * mt, s); },
+                             [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sDD, 16 * nB, s); });
+        const f32x4 vv = ld_col4<OT, LB>(sV, 16 * mt + g4, 16 * nB);
+        float rs[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * mt + g4 + e;
+          if (i < n) dV[(int64_t)i * p.dv_rs + v0 + 16 * nB + r16] = (TI)(bet[i] * A[0][0][e]);
+          rs[e] = row16_sum(A[0][0][e] * vv[e]);
+        }
+        store4b(sAt + LC::at(16 * nB + r16, 16 * mt + g4), A[0][0]);
+        if (r16 == 0)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[R_DB1 * RS + cbB * C + 16 * mt + g4 + e] += rs[e];
       }
       {
         using V = Vec16<OT>;
-        for (int idx = threadIdx.x; idx < D * BV / V::N; idx += NT) {  // same layout: index-wise product
-          const typename V::type a = reinterpret_cast<const typename V::type*>(cur + CF::O_S0)[idx];
-          const typename V::type d = reinterpret_cast<const typename V::type*>(cur + CF::O_DS)[idx];
+        for (int idx = threadIdx.x; idx < D * BV / V::N; idx += kThreadsG) {  // same layout: index-wise product
+          const typename V::type a = reinterpret_cast<const typename V::type*>(sS0)[idx];
+          const typename V::type d = reinterpret_cast<const typename V::type*>(sDS)[idx];
 #pragma unroll
           for (int e = 0; e < V::N; ++e) sdot += (float)a[e] * (float)d[e];
         }
       }
-      lds_barrier();  // A visible
-      gemm_l<OT, C, D, BV, 1, DN, NWV, LB, LB>(XQ, cur + CF::O_DO, cur + CF::O_S0);
-      gemm_l<OT, C, D, BV, 1, DN, NWV, LB, LB>(XK, cur + CF::O_DL, cur + CF::O_DS);
-      gemm_l<OT, C, D, BV, 1, DN, NWV, LB, LB>(Y, cur + CF::O_A, cur + CF::O_S0);
-      gemm_l<OT, C, C, BV, 1, 1, NWV, LB, LB>(P, cur + CF::O_DO, cur + CF::O_DL);
-      gemm_l<OT, C, C, BV, 1, 1, NWV, LB, LB>(AD, cur + CF::O_A, cur + CF::O_DL);
-    };
-    if constexpr (CF::DBUF) {
-      for (int b = 0; b < NBH; b += 2) {
-        block(sX, sY, b);
-        block(sY, sX, b + 1);
+      lds_barrier();  // A^T visible
+      if (aD) {
+        f32x4 XY[2][NTD];  // dO S0^T and A S0^T share the S0 fragments
+#pragma unroll
+        for (int y = 0; y < NTD; ++y) {
+          XY[0][y] = XQ[y];
+          XY[1][y] = Y[y];
+        }
+        wave_mm<OT, BV, 2, NTD>(XY,
+                                [&](int m, int s) {
+                                  return m == 0 ? ld_n<OT, KSB, STD, LB>(sDO, 16 * mt, s)
+                                                : ld_t<OT, KSB, STD, LC>(sAt, 16 * mt, s);
+                                },
+                                [&](int y, int s) { return ld_t<OT, KSB, STD, LD, OrdD>(sS0, 16 * (nD + y), s); });
+        f32x4 XKa[1][NTD];
+#pragma unroll
+        for (int y = 0; y < NTD; ++y) XKa[0][y] = XK[y];
+        wave_mm<OT, BV, 1, NTD>(XKa, [&](int, int s) { return ld_t<OT, KSB, STD, LC, OrdC>(sDL, 16 * mt, s); },
+                                [&](int y, int s) { return ld_t<OT, KSB, STD, LD, OrdD>(sDS, 16 * (nD + y), s); });
+#pragma unroll
+        for (int y = 0; y < NTD; ++y) {
+          XQ[y] = XY[0][y];
+          Y[y] = XY[1][y];
+          XK[y] = XKa[0][y];
+        }
       }
-    } else {
-      block(sX, sX, 0);
-    }
-    lds_barrier();  // the last block and T^T are consumed
-    const bool more = hh + 1 < p.r;
-    if (more) {
-      issue_head(h + 1);
-      issue_block(sX, h + 1, 0);
+      if (aC) {
+        f32x4 PA[2][NTC];  // dO Delta^T and A Delta^T share the Delta fragments
+#pragma unroll
+        for (int y = 0; y < NTC; ++y) {
+          PA[0][y] = P[y];
+          PA[1][y] = AD[y];
+        }
+        wave_mm<OT, BV, 2, NTC>(PA,
+                                [&](int m, int s) {
+                                  return m == 0 ? ld_n<OT, KSB, STD, LB>(sDO, 16 * mt, s)
+                                                : ld_t<OT, KSB, STD, LC>(sAt, 16 * mt, s);
+                                },
+                                [&](int y, int s) { return ld_t<OT, KSB, STD, LC, OrdC>(sDL, 16 * (nC + y), s); });
+#pragma unroll
+        for (int y = 0; y < NTC; ++y) {
+          P[y] = PA[0][y];
+          AD[y] = PA[1][y];
+        }
+      }
+      lds_barrier();  // sAt consumed before the next block rewrites it
     }
 
     // ---- phase 2
-    const float sc = p.scale;
-    P.each([&](int i, int j, float& x) {
-      const float pg = i >= j ? sc * x * expf(sg[i] - sg[j]) : 0.f;
-      sPG[LP::at(i, j)] = (OT)pg;
-      sPGt[LP::at(j, i)] = (OT)pg;
-    });
-    AD.each([&](int i, int j, float& x) {  // dL = -stril(AD); G' = dL o Gamma
-      const float gp = i > j ? -x * expf(sg[i] - sg[j]) : 0.f;
-      sGp[LP::at(i, j)] = (OT)gp;
-      sGt[LP::at(j, i)] = (OT)(sbeta[i] * gp);
-    });
-    acc_rowsum(XK, [&](int i, int d, float x) { return se[i] * x * (float)sKt[LC::at(d, i)]; }, red + R_EBAR * RS);
-    dkf.each_with(XK, [&](int i, int, float& a, float& x) { a += se[i] * x; });
-    acc_rowsum(XQ, [&](int i, int d, float x) { return sc * x * (float)sQt[LC::at(d, i)]; }, red + R_RQ * RS);
-    dqf.each_with(XQ, [&](int i, int, float& a, float& x) { a += sc * sb[i] * x; });
-    acc_rowsum(Y, [&](int i, int d, float x) { return -x * (float)sKt[LC::at(d, i)]; }, red + R_RHO * RS);
-    dkf.each_with(Y, [&](int i, int, float& a, float& y) { a -= sbeta[i] * sb[i] * y; });
+    const float sc = p.scale, gn = gam[C - 1];
+    if (aC) {
+#pragma unroll
+      for (int y = 0; y < NTC; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * mt + g4 + e, jj = 16 * (nC + y) + r16;
+          const float gd = __builtin_amdgcn_exp2f(gam[i] - gam[jj]);
+          const float pg = i >= jj ? sc * P[y][e] * gd : 0.f;
+          const float gp = i > jj ? -AD[y][e] * gd : 0.f;
+          sPG[LC::at(i, jj)] = (OT)pg;
+          sGp[LC::at(i, jj)] = (OT)gp;
+          sGb[LC::at(i, jj)] = (OT)(bet[i] * gp);
+        }
+    }
+    float bx[4], ex[4], bb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * mt + g4 + e;
+      bx[e] = __builtin_amdgcn_exp2f(gam[i]);
+      ex[e] = __builtin_amdgcn_exp2f(gn - gam[i]);
+      bb[e] = bet[i];
+    }
+    if (aD) {
+      f32x4 Kc[NTD], Qc[NTD];  // K and Q at this wave's accumulator positions
+#pragma unroll
+      for (int y = 0; y < NTD; ++y) {
+        Kc[y] = ld_col4<OT, LD>(sK, 16 * mt + g4, 16 * (nD + y));
+        Qc[y] = ld_col4<OT, LD>(sQ, 16 * mt + g4, 16 * (nD + y));
+      }
+      acc_rowsum<NTD>(XK, mt, nD, [&](int y, int e, float x) { return ex[e] * x * Kc[y][e]; },
+                      red + R_EBAR * RS + cbD * C);
+      acc_rowsum<NTD>(XQ, mt, nD, [&](int y, int e, float x) { return sc * x * Qc[y][e]; },
+                      red + R_RQ * RS + cbD * C);
+      acc_rowsum<NTD>(Y, mt, nD, [&](int y, int e, float x) { return -x * Kc[y][e]; }, red + R_RHO * RS + cbD * C);
+#pragma unroll
+      for (int y = 0; y < NTD; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dkf[y][e] += ex[e] * XK[y][e] - bb[e] * bx[e] * Y[y][e];
+          dqf[y][e] += sc * bx[e] * XQ[y][e];
+        }
+    }
     sdot = wave_sum(sdot);
     if (lane == 0) swv[w] = sdot;
     lds_barrier();  // scratch written
-    {
-      TCD Z;
-      Z.zero();
-      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sPG, sKt);  // (P o Gamma) K
-      acc_rowsum(Z, [&](int i, int d, float x) { return x * (float)sQt[LC::at(d, i)]; }, red + R_GROW * RS);
-      dqf.each_with(Z, [&](int, int, float& a, float& z) { a += z; });
-    }
-    {
-      TCD Z;
-      Z.zero();
-      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sPGt, sQt);  // (P o Gamma)^T Q
-      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sGt, sKt);   // + G^T K
-      acc_rowsum(Z, [&](int i, int d, float x) { return x * (float)sKt[LC::at(d, i)]; }, red + R_GCOL * RS);
-      dkf.each_with(Z, [&](int, int, float& a, float& z) { a += z; });
-    }
-    {
-      TCD Z;
-      Z.zero();
-      gemm_l<OT, C, D, C, 1, DN, NWV, LP, LC>(Z, sGp, sKt);  // G' K
-      acc_rowsum(Z, [&](int i, int d, float x) { return x * (float)sKt[LC::at(d, i)]; }, red + R_DB3 * RS);
-      dkf.each_with(Z, [&](int i, int, float& a, float& z) { a += sbeta[i] * z; });
+    if (aD) {
+      f32x4 Kc[NTD], Qc[NTD];
+#pragma unroll
+      for (int y = 0; y < NTD; ++y) {
+        Kc[y] = ld_col4<OT, LD>(sK, 16 * mt + g4, 16 * (nD + y));
+        Qc[y] = ld_col4<OT, LD>(sQ, 16 * mt + g4, 16 * (nD + y));
+      }
+      auto fK = [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sK, 16 * (nD + y), s); };
+      {  // (P o Gamma) K
+        f32x4 Z[1][NTD];
+        zero(Z);
+        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sPG, 16 * mt, s); }, fK);
+        acc_rowsum<NTD>(Z[0], mt, nD, [&](int y, int e, float x) { return x * Qc[y][e]; },
+                        red + R_GROW * RS + cbD * C);
+#pragma unroll
+        for (int y = 0; y < NTD; ++y) dqf[y] += Z[0][y];
+      }
+      {  // (P o Gamma)^T Q + G^T K
+        f32x4 Z[1][NTD];
+        zero(Z);
+        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sPG, 16 * mt, s); },
+                               [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sQ, 16 * (nD + y), s); });
+        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sGb, 16 * mt, s); }, fK);
+        acc_rowsum<NTD>(Z[0], mt, nD, [&](int y, int e, float x) { return x * Kc[y][e]; },
+                        red + R_GCOL * RS + cbD * C);
+#pragma unroll
+        for (int y = 0; y < NTD; ++y) dkf[y] += Z[0][y];
+      }
+      {  // G' K
+        f32x4 Z[1][NTD];
+        zero(Z);
+        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sGp, 16 * mt, s); }, fK);
+        acc_rowsum<NTD>(Z[0], mt, nD, [&](int y, int e, float x) { return x * Kc[y][e]; },
+                        red + R_DB3 * RS + cbD * C);
+#pragma unroll
+        for (int y = 0; y < NTD; ++y)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dkf[y][e] += bb[e] * Z[0][y][e];
+      }
     }
     lds_barrier();
     if (threadIdx.x < C) {
       const int i = threadIdx.x;
       for (int s = 0; s < R_NSLOT; ++s) {
         float a = 0.f;
-        for (int b = 0; b < kRedBlocks; ++b) a += red[s * RS + b * C + i];
+        for (int b = 0; b < NCB; ++b) a += red[s * RS + b * C + i];
         rowv[s * C + i] = a;
       }
     }
@@ -430,20 +583,21 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const float ebar = ok ? rowv[R_EBAR * C + i] : 0.f;
       const float rho = ok ? rowv[R_RHO * C + i] : 0.f;
       const float db3 = ok ? rowv[R_DB3 * C + i] : 0.f;
+      const float bi = ok ? __builtin_amdgcn_exp2f(gam[i]) : 0.f, be = ok ? bet[i] : 0.f;
       float dgam = 0.f;
       if (ok)
-        dgam = sb[i] * rowv[R_RQ * C + i] + sbeta[i] * sb[i] * rho - ebar + rowv[R_GROW * C + i] +
-               sbeta[i] * db3 - rowv[R_GCOL * C + i];
+        dgam = bi * rowv[R_RQ * C + i] + be * bi * rho - ebar + rowv[R_GROW * C + i] + be * db3 -
+               rowv[R_GCOL * C + i];
       const float ebsum = wave_sum(ebar);
       if (i == n - 1) {
         float st = 0.f;
-        for (int k = 0; k < NWV; ++k) st += swv[k];
-        dgam += expf(sg[C - 1]) * st + ebsum;
+        for (int k = 0; k < NW; ++k) st += swv[k];
+        dgam += __builtin_amdgcn_exp2f(gn) * st + ebsum;
       }
       const float dlg = wave_rscan_incl(dgam);
       if (i < n) {
         const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
-        p.dbeta[row] = rowv[R_DB1 * C + i] + sb[i] * rho + db3;
+        p.dbeta[row] = rowv[R_DB1 * C + i] + bi * rho + db3;
         p.dg[row] = dlg / sgate[i];
       }
     }
@@ -451,15 +605,23 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   }
   // dq, dk of the key head: rows through LDS (the first block buffer), 16-byte stores
   {
-    TI* st = (TI*)sX;
-    dqf.each([&](int i, int d, float& x) { st[i * D + d] = (TI)x; });
-    dkf.each([&](int i, int d, float& x) { st[(C + i) * D + d] = (TI)x; });
+    TI* st = (TI*)sB[0];
+    if (aD) {
+#pragma unroll
+      for (int y = 0; y < NTD; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * mt + g4 + e, d = 16 * (nD + y) + r16;
+          st[i * D + d] = (TI)dqf[y][e];
+          st[(C + i) * D + d] = (TI)dkf[y][e];
+        }
+    }
     lds_barrier();
     using V = Vec16<TI>;
     constexpr int VPR = D / V::N;
     TI* dq = (TI*)p.dq + (int64_t)ci.t0 * p.dq_rs + kh * D;
     TI* dk = (TI*)p.dk + (int64_t)ci.t0 * p.dk_rs + kh * D;
-    for (int idx = threadIdx.x; idx < 2 * C * VPR; idx += NT) {
+    for (int idx = threadIdx.x; idx < 2 * C * VPR; idx += kThreadsG) {
       const int r = idx / VPR, cc = (idx % VPR) * V::N;
       const int i = r % C;
       if (i < n) {
@@ -472,8 +634,11 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
 
 template <typename TI, int C, int D>
 static hipError_t bwd_seq(const Prob& p, hipStream_t s) {
+  using CF = BwCfg<TI, C, D>;
   traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
-  if (p.N > 0) traced("k_bwd_sweep", s, [&] { k_bwd_sweep<TI, C, D><<<dim3(p.N, p.Hv), kThreadsB, 0, s>>>(p); });
+  if (p.N > 0)
+    traced("k_bwd_sweep", s,
+           [&] { k_bwd_sweep<TI, C, D><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });
   if (p.nc_max > 0)
     traced("k_bwd_grad", s, [&] { k_bwd_grad<TI, C, D><<<dim3(p.nc_max, p.Hk), kThreadsG, 0, s>>>(p); });
   return hipGetLastError();

@@ -1,7 +1,7 @@
 // gdn_common.h -- chunk table shared by the forward and backward launch sequences.
 #pragma once
 #include "gdn_internal.h"
-#include "gdn_mma.h"
+#include "gdn_frag.h"
 
 namespace gdn {
 
@@ -61,6 +61,18 @@ __device__ __forceinline__ void seq_bounds(const Prob& p, int n, int64_t& a, int
     b = a + p.T;
   }
 }
+
+// Workgroup b of a grid of xcd_grid(G, r) workgroups, as member mem of group grp, where a
+// group is r units that share a key head. Workgroups are dispatched to the 8 XCDs
+// round-robin, so the members of a group land on one XCD and share its L2. Returns false
+// for the padding workgroups of the last round.
+__device__ __forceinline__ bool xcd_group(int b, int G, int r, int& grp, int& mem) {
+  const int x = b & 7, s = b >> 3;
+  grp = (s / r) * 8 + x;
+  mem = s % r;
+  return grp < G;
+}
+__host__ __device__ constexpr int xcd_grid(int G, int r) { return (G + 7) / 8 * 8 * r; }
 
 // One workgroup: chunk table and per-sequence first-chunk offsets.
 template <int C>

@@ -5,31 +5,37 @@
 // chunk of n <= C tokens starting from state S:
 //   gamma = cumsum(log g),  b = exp(gamma),  Gamma_rs = exp(gamma_r - gamma_s) [r >= s]
 //   L = strictly_lower(diag(beta) (Gamma o K K^T)),  T = (I + L)^-1
-//   W = T diag(beta b) K,  U = T diag(beta) V,  Delta = U - W S   (Delta_r = delta_r)
-//   O = scale (diag(b) Q S + (Gamma o Q K^T) Delta)
-//   S_next = b_n S + K^T diag(exp(gamma_n - gamma)) Delta
+//   Delta = T diag(beta) (V - diag(b) K S)       (Delta_r = delta_r of the recurrence)
+//   O = scale (diag(b) Q S + M Delta),  M = Gamma o Q K^T (lower incl. diagonal)
+//   S_next = b_n S + K^T diag(e) Delta,  e = exp(gamma_n - gamma)
 // Rows past the end of a partial chunk carry k = q = v = beta = 0 and log g = 0.
 //
 // Two kernels after the chunk table:
-//  k_prep  (chunk x key head, 8 waves): K K^T and Q K^T once for the r value heads of the
-//          key head; per value head gamma, the blocked inverse T, W, U and
-//          M = Gamma o Q K^T. Everything the serial pass and the backward need is written
-//          once, in the storage type, in the layout its consumer reads.
-//  k_sweep (sequence x value head, 8 waves): the chunk-serial pass. The state lives in
-//          float32 MFMA accumulators; per chunk it forms Delta = U - W S, the output
-//          O = diag(b) Q S + M Delta, and S <- b_n S + K^T (e o Delta), while the next
-//          chunk's operands are loaded into registers.
+//  k_prep (chunk x key head, 4 waves): K K^T and Q K^T once for the r value heads of the
+//      key head; per value head the gate record (gamma in log2 units, so that every decay
+//      factor is one native exp2, and beta), M and the blocked inverse
+//      T, each written once in the storage type. Nothing else is materialised: the sweep
+//      forms W S as T diag(beta b) (K S) and U as T diag(beta) V itself.
+//  k_fwd_sweep (sequence x value head, one wave per 32 state columns): the chunk-serial
+//      pass. Columns of S never mix, so each wave owns a column slice of the state in
+//      float32 MFMA accumulators and K S, Delta and O never leave its registers: the
+//      accumulator of one product is the operand of the next (ACC order). K, Q, V, T, M
+//      and the gate record of the next chunk stream into a second LDS buffer by direct
+//      loads while the current chunk is computed.
 #include "gdn_common.h"
-#include "gdn_mma.h"
 
 namespace gdn {
 
-constexpr int kWaves = 8;              // k_sweep
-constexpr int kThreads = kWaves * 64;
-constexpr int kPrepWaves = 16;         // k_prep
+constexpr int kPrepWaves = 4;
 constexpr int kPrepThreads = kPrepWaves * 64;
 
-__host__ __device__ constexpr int blk2(int x) { return x >= 32 ? 2 : 1; }
+// Four accumulator values as consecutive elements of type OT (8 or 16 bytes).
+template <typename OT> __device__ __forceinline__ void store4(OT* dst, f32x4 x) {
+  if constexpr (sizeof(OT) == 2)
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  else
+    *reinterpret_cast<f32x4*>(dst) = x;
+}
 
 // T := (I + L)^-1 for strictly lower triangular L (float32 LDS, row stride LC).
 // Diagonal 16 x 16 blocks by forward substitution, one column per lane, then the
@@ -38,6 +44,7 @@ __host__ __device__ constexpr int blk2(int x) { return x >= 32 ? 2 : 1; }
 template <int C, int LC, int NWV>
 __device__ __forceinline__ void invert_unit_lower(const float* L, float* T, float* X) {
   constexpr int NB = C / 16;
+  static_assert(NWV >= NB, "one wave per diagonal block");
   const int w = threadIdx.x / 64, l = threadIdx.x & 63;
   for (int idx = threadIdx.x; idx < C * C; idx += NWV * 64) {
     const int i = idx / C, j = idx % C;
@@ -92,235 +99,333 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T, floa
 template <typename TI, int C, int D>
 __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   using OT = TI;
-  constexpr int NT = kPrepThreads, NWV = kPrepWaves, LDO = D + 8, LCO = C + 8, LCF = C + 4;
-  __shared__ __align__(16) OT sK[C * LDO];
-  __shared__ __align__(16) OT sQ[C * LDO];
-  __shared__ __align__(16) OT sKt[D * LCO];
-  __shared__ __align__(16) OT sVt[D * LCO];  // V^T of each value head
-  __shared__ __align__(16) float sL[C * LCF];
-  __shared__ __align__(16) float sT[C * LCF];
-  __shared__ __align__(16) OT sTp[C * LCO];   // T diag(beta b)
-  __shared__ __align__(16) OT sTpp[C * LCO];  // T diag(beta)
-  __shared__ __align__(16) float sX[3 * 320];
-  __shared__ float sg[C], sb[C], sbeta[C];
-  typedef OT o4 __attribute__((ext_vector_type(4)));
+  using LD = Swz<OT, D>;
+  constexpr int NW = kPrepWaves, NT = kPrepThreads, LCF = C + 4, RT = C / 16;
+  constexpr int KSD = ks_of<OT, D>();
+  // K and Q (direct loads) for the Gram products; afterwards the same bytes hold L, T,
+  // the inverse's scratch and the staging tile of M.
+  constexpr int KQ_BYTES = 2 * C * D * (int)sizeof(OT);
+  constexpr int INV_BYTES = (2 * C * LCF + 3 * 320) * 4 + C * C * (int)sizeof(OT);
+  __shared__ __align__(16) char smem[KQ_BYTES > INV_BYTES ? KQ_BYTES : INV_BYTES];
+  __shared__ float sg[C], sbeta[C];
+  OT* const sK = reinterpret_cast<OT*>(smem);
+  OT* const sQ = sK + C * D;
+  float* const sL = reinterpret_cast<float*>(smem);
+  float* const sT = sL + C * LCF;
+  float* const sX = sT + C * LCF;
+  OT* const sM = reinterpret_cast<OT*>(sX + 3 * 320);
+
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
-  const int n = ci.len;
-  const size_t ck = (size_t)c * p.Hk + kh;
-
-  Stage<C, D, NT, TI> gq;  // Q stays in registers: (diag(b) Q)^T is written per value head
+  const int n = ci.len, w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
   {
-    Stage<C, D, NT, TI> gk;
-    gk.issue((const TI*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n);
-    gq.issue((const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n);
-    gk.template to_rows<LDO>(sK);
-    gk.template to_cols<LCO>(sKt);
-    gq.template to_rows<LDO>(sQ);
-    gq.template to_cols<LCO>(sVt);  // Q^T, saved for the backward
+    TileDma<C, D, NW, OT> dm;
+    dm.init(w);
+    dm.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
+    dm.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
   }
+  dma_wait();
   lds_barrier();
-  lds_to_global<D, C, LCO, NT>((OT*)p.sv_Kt + ck * D * C, sKt);
-  lds_to_global<D, C, LCO, NT>((OT*)p.sv_Qt + ck * D * C, sVt);
-  Tile<C, C, 1, 1, NWV> KK, QK;
-  KK.zero();
-  QK.zero();
-  gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(KK, sK, sK);
-  gemm_nt<OT, C, C, D, 1, 1, NWV, LDO, LDO>(QK, sQ, sK);
-
-  Stage<C, D, NT, TI> gv;
-  gv.issue((const TI*)p.v + (int64_t)ci.t0 * p.v_rs + (kh * p.r) * D, p.v_rs, n);
+  // K K^T and Q K^T: wave w < C / 16 owns row tile w and every column tile.
+  const bool rw = w < RT;
+  f32x4 KK[1][RT], QK[1][RT];
+  zero(KK);
+  zero(QK);
+  if (rw) {
+    auto fb = [&](int j, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * j, s); };
+    wave_mm<OT, D, 1, RT>(KK, [&](int, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * w, s); }, fb);
+    wave_mm<OT, D, 1, RT>(QK, [&](int, int s) { return ld_n<OT, KSD, STD, LD>(sQ, 16 * w, s); }, fb);
+  }
+  lds_barrier();  // K and Q consumed
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = kh * p.r + hh;
     const size_t ch = ch_idx(p, c, h);
-    for (int i = threadIdx.x; i < C; i += NT) {
-      const bool ok = i < n;
-      sbeta[i] = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
-      sg[i] = ok ? logf(p.g[(int64_t)(ci.t0 + i) * p.Hv + h]) : 0.f;
-    }
-    lds_barrier();
-    gv.template to_cols<LCO>(sVt);
-    if (hh + 1 < p.r) gv.issue((const TI*)p.v + (int64_t)ci.t0 * p.v_rs + (h + 1) * D, p.v_rs, n);
     if (threadIdx.x < 64) {
-      const float x = wave_scan_incl(threadIdx.x < C ? sg[threadIdx.x] : 0.f);
-      if (threadIdx.x < C) sg[threadIdx.x] = x;
+      const int i = threadIdx.x;
+      const bool ok = i < n && i < C;
+      const float lg = ok ? __builtin_amdgcn_logf(p.g[(int64_t)(ci.t0 + i) * p.Hv + h]) : 0.f;  // log2 g
+      const float be = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
+      const float gam = wave_scan_incl(i < C ? lg : 0.f);
+      if (i < C) {
+        sg[i] = gam;
+        sbeta[i] = be;
+        p.sv_gb[ch * 2 * C + i] = gam;
+        p.sv_gb[ch * 2 * C + C + i] = be;
+      }
     }
     lds_barrier();
-    for (int i = threadIdx.x; i < C; i += NT) {
-      sb[i] = expf(sg[i]);
-      p.sv_gam[ch * C + i] = sg[i];
-    }
-    KK.each([&](int i, int j, float& x) {
-      sL[i * LCF + j] = i > j ? sbeta[i] * expf(sg[i] - sg[j]) * x : 0.f;
-    });
-    OT* M = (OT*)p.sv_M + ch * C * C;
-    QK.each([&](int i, int j, float& x) { M[i * C + j] = (OT)(i >= j ? expf(sg[i] - sg[j]) * x : 0.f); });
-    lds_barrier();
-    invert_unit_lower<C, LCF, NWV>(sL, sT, sX);
-    OT* Ttsv = (OT*)p.sv_Tt + ch * C * C;
-    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
-      const int i = idx / C, j = idx % C;
-      const float t = sT[i * LCF + j];
-      Ttsv[idx] = (OT)sT[j * LCF + i];
-      sTp[i * LCO + j] = (OT)(t * sbeta[j] * sb[j]);
-      sTpp[i * LCO + j] = (OT)(t * sbeta[j]);
+    if (rw) {
+#pragma unroll
+      for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * w + g4 + e, jj = 16 * j + r16;
+          const float gd = __builtin_amdgcn_exp2f(sg[i] - sg[jj]);
+          sL[i * LCF + jj] = i > jj ? sbeta[i] * gd * KK[0][j][e] : 0.f;
+          sM[i * C + jj] = (OT)(i >= jj && i < n ? gd * QK[0][j][e] : 0.f);
+        }
     }
     lds_barrier();
     {
-      Tile<C, D, 1, blk2(D), NWV> w;
-      w.zero();
-      gemm_nt<OT, C, D, C, 1, blk2(D), NWV, LCO, LCO>(w, sTp, sKt);
-      OT* W = (OT*)p.sv_W + ch * C * D;
-      w.each([&](int i, int d, float& x) { W[i * D + d] = (OT)x; });
+      using V = Vec16<OT>;
+      typename V::type* dst = reinterpret_cast<typename V::type*>((OT*)p.sv_M + ch * C * C);
+      const typename V::type* src = reinterpret_cast<const typename V::type*>(sM);
+      for (int idx = threadIdx.x; idx < C * C / V::N; idx += NT) dst[idx] = src[idx];
     }
+    invert_unit_lower<C, LCF, NW>(sL, sT, sX);
     {
-      Tile<C, D, 1, blk2(D), NWV> u;
-      u.zero();
-      gemm_nt<OT, C, D, C, 1, blk2(D), NWV, LCO, LCO>(u, sTpp, sVt);
-      OT* Ut = (OT*)p.ws_Ut + ch * D * C;
-      u.each4([&](int i0, int v, f32x4& x) {
-        *reinterpret_cast<o4*>(Ut + v * C + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
-      });
+      OT* dst = (OT*)p.sv_T + ch * C * C;
+      for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
+        const int i = idx / (C / 4), j0 = (idx % (C / 4)) * 4;
+        store4(dst + i * C + j0, *reinterpret_cast<const f32x4*>(sT + i * LCF + j0));
+      }
     }
-    lds_barrier();  // sVt free: stage (diag(b) Q)^T for the backward
-    gq.template to_cols<LCO>(sVt, sb);
-    lds_barrier();
-    lds_to_global<D, C, LCO, NT>((OT*)p.sv_Qbt + ch * D * C, sVt);
+    lds_barrier();  // sL, sT, sM free for the next head
   }
 }
 
-// Grid (N, Hv). Chunk-serial pass over one sequence and one value head.
-template <typename TI, int C, int D>
-__global__ __launch_bounds__(kThreads) void k_sweep(Prob p) {
-  using OT = TI;
-  constexpr int NT = kThreads, LDO = D + 8, LCO = C + 8;
-  constexpr int SM = blk2(D), DN = blk2(D);
-  __shared__ __align__(16) OT sW[C * LDO];
-  __shared__ __align__(16) OT sQ[C * LDO];
-  __shared__ __align__(16) OT sM[C * LCO];
-  __shared__ __align__(16) OT sKt[D * LCO];
-  __shared__ __align__(16) OT sSt[D * LDO];   // S^T: [v][d]
-  __shared__ __align__(16) OT sDt[D * LCO];   // Delta^T: [v][i]
-  __shared__ __align__(16) OT sDet[D * LCO];  // (e o Delta)^T
-  __shared__ float sg[C], sb[C], se[C];
-  typedef OT o4 __attribute__((ext_vector_type(4)));
+// ---------------------------------------------------------------------------- sweep
+template <typename TI, int C, int D> struct SwCfg {
+  static constexpr int WC = 16;       // state columns per wave: two waves per SIMD at D = 128
+  static constexpr int NW = D / WC;   // waves: one workgroup holds every column of a head
+  static constexpr int CT = WC / 16, DT = D / 16, RT = C / 16;
+  static constexpr int CE = 16 / (int)sizeof(TI);  // elements per 16-byte chunk
+  static constexpr int LSO = D + CE;               // row stride of the output staging tile
+  // One LDS buffer: K, Q, V [C][D] and T, M [C][C], all Swz layouts.
+  static constexpr int O_K = 0, O_Q = C * D, O_V = 2 * C * D, O_T = 3 * C * D, O_M = O_T + C * C, BUF = O_M + C * C;
+};
 
-  const int n = blockIdx.x, h = blockIdx.y, kh = h / p.r;
+// acc[n][m] += sum_k A(m, k) B(k, n): wave_mm with the accumulator tiles stored
+// column-tile major (the layout from_acc reads when the result feeds a later product).
+template <typename OT, int K, int MT, int NT, class FA, class FB>
+__device__ __forceinline__ void wave_mm_cm(f32x4 (&acc)[NT][MT], FA&& fa, FB&& fb) {
+  constexpr int KS = ks_of<OT, K>();
+  using M = Mf<OT, KS>;
+#pragma unroll
+  for (int s = 0; s < K / KS; ++s) {
+    typename M::frag b[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) b[n] = fb(n, s);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const typename M::frag a = fa(m, s);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n][m] = M::run(a, b[n], acc[n][m]);
+    }
+  }
+}
+
+// One saved row segment per lane and column tile: the transposed tile X^T[v][j] of a
+// wave's accumulators Xc[ct][t] (rows j = 16 t + g4 + e of column v = v0 + 16 ct + r16),
+// into rows of LEN elements in RowOrd<OT, LEN> order. In fragment order every lane stores
+// its 16-byte MFMA fragment (frag[ct][s], ACC order over j) with one instruction.
+template <typename OT, int LEN, int CT, int NT, int NS>
+__device__ __forceinline__ void save_rows(OT* dst, int v0, const f32x4 (&Xc)[CT][NT],
+                                          const typename Mf<OT, ks_of<OT, LEN>()>::frag (&frag)[CT][NS]) {
+  const int l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    OT* row = dst + (size_t)(v0 + 16 * ct + r16) * LEN;
+    if constexpr (RowOrd<OT, LEN>::frag) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) *reinterpret_cast<bf16x8*>(row + 32 * s + 2 * g4) = frag[ct][s];
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) store4(row + 16 * t + g4, Xc[ct][t]);
+    }
+  }
+}
+
+// Wave-local ordering of LDS writes before reads by other lanes of the same wave.
+__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Grid xcd_grid(N * Hk, r): one workgroup per (sequence, value head); the r value heads
+// of a key head run on one XCD (they read the same K and Q).
+template <typename TI, int C, int D>
+__global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p) {
+  using OT = TI;
+  using CF = SwCfg<TI, C, D>;
+  constexpr int NW = CF::NW, WC = CF::WC, CT = CF::CT, DT = CF::DT, RT = CF::RT, CE = CF::CE;
+  constexpr int KSD = ks_of<OT, D>(), KSC = ks_of<OT, C>(), NSD = D / KSD, NSC = C / KSC;
+  using LD = Swz<OT, D>;
+  using LC = Swz<OT, C>;
+  using FragD = typename Mf<OT, KSD>::frag;
+  using FragC = typename Mf<OT, KSC>::frag;
+  __shared__ __align__(16) OT sbuf[2][CF::BUF];
+  __shared__ __align__(16) float sgb[2][2 * C];
+  __shared__ __align__(16) OT stg[C * CF::LSO];  // the chunk's output rows, all D columns
+
+  int grp, hh;
+  if (!xcd_group(blockIdx.x, p.N * p.Hk, p.r, grp, hh)) return;
+  const int n = grp / p.Hk, kh = grp % p.Hk, h = kh * p.r + hh;
   const size_t nh = (size_t)n * p.Hv + h;
   const int c0 = p.seq_chunk[n], c1 = p.seq_chunk[n + 1];
+  int64_t sa, sb;  // rows of the sequence; chunk c starts at sa + (c - c0) C (as in the chunk table)
+  seq_bounds(p, n, sa, sb);
+  const int w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
+  const int v0 = w * WC;  // first state column of this wave
 
-  using TS = Tile<D, D, SM, SM, kWaves>;
-  using TD = Tile<C, D, 1, DN, kWaves>;
-  TS S;
+  TileDma<C, D, NW, OT> dmD;         // K, Q, V
+  TileDma<C, C, NW, OT> dmC;         // T, M
+  TileDma<1, 2 * C, NW, float> dmG;  // gate record
+  dmD.init(w);
+  dmC.init(w);
+  dmG.init(w);
+  auto issue = [&](int c, int buf) {
+    const int64_t t0 = sa + (int64_t)(c - c0) * C;
+    const int len = (int)(sb - t0 < C ? sb - t0 : C);
+    const size_t ch = ch_idx(p, c, h);
+    OT* b = sbuf[buf];
+    dmD.issue(b + CF::O_K, (const OT*)p.k + t0 * p.k_rs + kh * D, p.k_rs, len, w);
+    dmD.issue(b + CF::O_Q, (const OT*)p.q + t0 * p.q_rs + kh * D, p.q_rs, len, w);
+    dmD.issue(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
+    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
+    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
+    dmG.issue(sgb[buf], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+  };
+
+  // The state: S[ct][dt] holds S[16 dt + g4 + e][v0 + 16 ct + r16].
+  f32x4 S[CT][DT];
   if (p.S0) {
     const float* s0 = p.S0 + nh * D * D;
-    S.each([&](int d, int v, float& x) { x = s0[d * D + v]; });
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[ct][dt][e] = s0[(16 * dt + g4 + e) * D + v0 + 16 * ct + r16];
   } else {
-    S.zero();
+    zero(S);
   }
 
-  Stage<C, D, NT, OT> nW;
-  Stage<C, D, NT, TI> nQ;
-  Stage<C, C, NT, OT> nM;
-  Stage<D, C, NT, OT> nKt;
-  float ng = 0.f;
-  auto issue = [&](int c) {
-    const ChunkInfo ci = p.chunks[c];
-    const size_t ch = ch_idx(p, c, h), ck = (size_t)c * p.Hk + kh;
-    nW.issue((const OT*)p.sv_W + ch * C * D, D, C);
-    nQ.issue((const TI*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, ci.len);
-    nM.issue((const OT*)p.sv_M + ch * C * C, C, C);
-    nKt.issue((const OT*)p.sv_Kt + ck * D * C, C, D);
-    if (threadIdx.x < C) ng = p.sv_gam[ch * C + threadIdx.x];
-  };
-  auto commit = [&]() {
-    nW.template to_rows<LDO>(sW);
-    nQ.template to_rows<LDO>(sQ);
-    nM.template to_rows<LCO>(sM);
-    nKt.template to_rows<LCO>(sKt);
-    if (threadIdx.x < C) sg[threadIdx.x] = ng;
-  };
-  auto state_to_lds = [&]() {
-    S.each4([&](int d0, int v, f32x4& x) {
-      *reinterpret_cast<o4*>(sSt + v * LDO + d0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
-    });
-  };
-
-  if (c0 < c1) {
-    issue(c0);
-    commit();
-  }
-  state_to_lds();
-  lds_barrier();
-  for (int c = c0; c < c1; ++c) {
-    const ChunkInfo ci = p.chunks[c];
+  if (c0 < c1) issue(c0, 0);
+  int buf = 0;
+  for (int c = c0; c < c1; ++c, buf ^= 1) {
+    dma_wait();
+    lds_barrier();  // chunk c is in sbuf[buf]; every wave is done with sbuf[buf ^ 1] and stg
+    if (c + 1 < c1) issue(c + 1, buf ^ 1);
+    const int64_t t0 = sa + (int64_t)(c - c0) * C;
+    const int len = (int)(sb - t0 < C ? sb - t0 : C);
     const size_t ch = ch_idx(p, c, h);
-    if (threadIdx.x < C) {
-      sb[threadIdx.x] = expf(sg[threadIdx.x]);
-      se[threadIdx.x] = expf(sg[C - 1] - sg[threadIdx.x]);
-    }
-    if (c + 1 < c1) issue(c + 1);
-    TD U;  // U of this chunk, in the accumulator layout of Delta
-    {
-      const OT* Ut = (const OT*)p.ws_Ut + ch * D * C;
-      U.each4([&](int i0, int v, f32x4& x) {
-        const o4 u = *reinterpret_cast<const o4*>(Ut + v * C + i0);
-        x = f32x4{(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
-      });
-    }
-    // the chunk's start state, saved for the backward (key-major, from its LDS copy)
-    lds_to_global_t<D, D, LDO, NT>((OT*)p.sv_S + ch * D * D, sSt);
-    TD WS, O;
-    WS.zero();
-    O.zero();
-    gemm_nt<OT, C, D, D, 1, DN, kWaves, LDO, LDO>(WS, sW, sSt);
-    gemm_nt<OT, C, D, D, 1, DN, kWaves, LDO, LDO>(O, sQ, sSt);
-    lds_barrier();  // sb, se visible
-    {
+    const OT* sK = sbuf[buf] + CF::O_K;
+    const OT* sQ = sbuf[buf] + CF::O_Q;
+    const OT* sV = sbuf[buf] + CF::O_V;
+    const OT* sT = sbuf[buf] + CF::O_T;
+    const OT* sM = sbuf[buf] + CF::O_M;
+    const float* gam = sgb[buf];  // log2 units
+    const float* bet = gam + C;
+    // decay factors of this lane's accumulator rows i = 16 t + g4 + e
+    const float gn = gam[C - 1], bn = __builtin_amdgcn_exp2f(gn);
+    float bx[RT][4], ex[RT][4];
 #pragma unroll
-      for (int q = 0; q < TD::B::PER; ++q)
+    for (int t = 0; t < RT; ++t) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * t + g4);
 #pragma unroll
-        for (int y = 0; y < DN; ++y) U.a[q][0][y] -= WS.a[q][0][y];
-      U.each4([&](int i0, int v, f32x4& x) {
-        *reinterpret_cast<o4*>(sDt + v * LCO + i0) = o4{(OT)x[0], (OT)x[1], (OT)x[2], (OT)x[3]};
-        *reinterpret_cast<o4*>(sDet + v * LCO + i0) =
-            o4{(OT)(x[0] * se[i0]), (OT)(x[1] * se[i0 + 1]), (OT)(x[2] * se[i0 + 2]), (OT)(x[3] * se[i0 + 3])};
-      });
-      O.each([&](int i, int v, float& x) { x *= sb[i]; });
+      for (int e = 0; e < 4; ++e) {
+        bx[t][e] = __builtin_amdgcn_exp2f(gv[e]);
+        ex[t][e] = __builtin_amdgcn_exp2f(gn - gv[e]);
+      }
     }
-    lds_barrier();
-    lds_to_global_t<D, C, LCO, NT>((OT*)p.sv_Dl + ch * C * D, sDt);  // Delta, row-major
-    gemm_nt<OT, C, D, C, 1, DN, kWaves, LCO, LCO>(O, sM, sDt);
+    // the state's MFMA fragments (B operand over d), shared by K S, Q S and the saved copy
+    FragD Sb[CT][NSD];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int s = 0; s < NSD; ++s) Sb[ct][s] = from_acc<OT, KSD>(S[ct], s, Ident{});
+    save_rows<OT, D, CT, DT, NSD>((OT*)p.sv_S + ch * D * D, v0, S, Sb);  // S^T[v][d] at the chunk start
+    // X = beta o (V - b o K S), then Delta = T X
+    f32x4 X[CT][RT];
     {
-      TI* o = (TI*)p.o + (int64_t)ci.t0 * p.o_rs + h * D;
-      const int len = ci.len;
+      f32x4 KS[RT][CT];
+      zero(KS);
+      wave_mm<OT, D, RT, CT>(KS, [&](int m, int s) { return ld_n<OT, KSD, ACC, LD>(sK, 16 * m, s); },
+                             [&](int j, int s) { return Sb[j][s]; });
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 16 * t + g4);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const f32x4 vv = ld_col4<OT, LD>(sV, 16 * t + g4, v0 + 16 * ct);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) X[ct][t][e] = bb[e] * (vv[e] - bx[t][e] * KS[t][ct][e]);
+        }
+      }
+    }
+    f32x4 Dl[CT][RT];
+    zero(Dl);
+    wave_mm_cm<OT, C, RT, CT>(Dl, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sT, 16 * m, s); },
+                              [&](int j, int s) { return from_acc<OT, KSC>(X[j], s, Ident{}); });
+    FragC Db[CT][NSC];  // Delta's fragments: B operand of M Delta and the saved copy
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int s = 0; s < NSC; ++s) Db[ct][s] = from_acc<OT, KSC>(Dl[ct], s, Ident{});
+    save_rows<OT, C, CT, RT, NSC>((OT*)p.sv_Dt + ch * D * C, v0, Dl, Db);  // Delta^T[v][i]
+    {  // O = b o Q S + M Delta, staged as rows for the whole workgroup
+      f32x4 O[RT][CT];
+      zero(O);
+      wave_mm<OT, D, RT, CT>(O, [&](int m, int s) { return ld_n<OT, KSD, ACC, LD>(sQ, 16 * m, s); },
+                             [&](int j, int s) { return Sb[j][s]; });
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[t][ct][e] *= bx[t][e];
+      wave_mm<OT, C, RT, CT>(O, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sM, 16 * m, s); },
+                             [&](int j, int s) { return Db[j][s]; });
       const float sc = p.scale;
-      O.each([&](int i, int v, float& x) {
-        if (i < len) o[(int64_t)i * p.o_rs + v] = (TI)(sc * x);
-      });
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)(sc * O[t][ct][e]);
     }
-    {
-      const float bn = sb[C - 1];
-      S.each([&](int, int, float& x) { x *= bn; });
-      gemm_nt<OT, D, D, C, SM, SM, kWaves, LCO, LCO>(S, sKt, sDet);
+    lds_barrier();  // the chunk's output rows are staged
+    {  // full output rows, 16-byte stores spread over every wave
+      using V = Vec16<OT>;
+      constexpr int VPR = D / CE;
+      TI* o = (TI*)p.o + t0 * p.o_rs + h * D;
+#pragma unroll
+      for (int idx = threadIdx.x; idx < C * VPR; idx += NW * 64) {
+        const int i = idx / VPR, q = idx % VPR;
+        if (i < len)
+          *reinterpret_cast<typename V::type*>(o + (int64_t)i * p.o_rs + q * CE) =
+              *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
+      }
     }
-    lds_barrier();
-    state_to_lds();
-    if (c + 1 < c1) commit();
-    lds_barrier();
+    // S <- b_n S + K^T (e o Delta)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) S[ct][dt] *= bn;
+    wave_mm_cm<OT, C, DT, CT>(
+        S, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sK, 16 * m, s); },
+        [&](int j, int s) {
+          return from_acc<OT, KSC>(Dl[j], s, [&](int t, int e, float x) { return ex[t][e] * x; });
+        });
   }
   if (p.ST) {
     float* st = p.ST + nh * D * D;
-    S.each([&](int d, int v, float& x) { st[d * D + v] = x; });
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[(16 * dt + g4 + e) * D + v0 + 16 * ct + r16] = S[ct][dt][e];
   }
 }
 
 template <typename TI, int C, int D>
 static hipError_t fwd_seq(const Prob& p, hipStream_t s) {
+  using CF = SwCfg<TI, C, D>;
   traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
   if (p.nc_max > 0) traced("k_prep", s, [&] { k_prep<TI, C, D><<<dim3(p.nc_max, p.Hk), kPrepThreads, 0, s>>>(p); });
-  if (p.N > 0) traced("k_sweep", s, [&] { k_sweep<TI, C, D><<<dim3(p.N, p.Hv), kThreads, 0, s>>>(p); });
+  if (p.N > 0)
+    traced("k_fwd_sweep", s,
+           [&] { k_fwd_sweep<TI, C, D><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });
   return hipGetLastError();
 }
 
@@ -329,10 +434,14 @@ static hipError_t fwd_d(const Prob& p, hipStream_t s) {
   switch (p.D) {
     case 16: return fwd_seq<TI, C, 16>(p, s);
     case 32: return fwd_seq<TI, C, 32>(p, s);
-    case 64: return fwd_seq<TI, C, 64>(p, s);
-    case 128:
+    case 64:
       if constexpr (sizeof(TI) == 4 && C == 64)
         return hipErrorInvalidValue;  // rejected on the host (LDS)
+      else
+        return fwd_seq<TI, C, 64>(p, s);
+    case 128:
+      if constexpr (sizeof(TI) == 4 && C == 64)
+        return hipErrorInvalidValue;
       else
         return fwd_seq<TI, C, 128>(p, s);
   }

@@ -44,22 +44,16 @@ struct Prob {
   ChunkInfo* chunks;  // [nc_max]
   int* seq_chunk;     // [N + 1] first chunk of each sequence
 
-  // Saved activations written by the forward for the backward (element type = the
-  // problem's storage type OT unless noted), per chunk c and value head h / key head kh:
-  void* sv_S;    // [c][h][D][D]  state at the start of the chunk, key-major
-  void* sv_W;    // [c][h][C][D]  W, row-major
-  void* sv_Dl;   // [c][h][C][D]  Delta, row-major
-  void* sv_M;    // [c][h][C][C]  Gamma o Q K^T (lower incl. diagonal), row-major
-  void* sv_Tt;   // [c][h][C][C]  T^T, T = (I + L)^-1
-  float* sv_gam; // [c][h][C]     float32
-  void* sv_Kt;   // [c][kh][D][C] K^T
-  void* sv_Qbt;  // [c][h][D][C]  (diag(b) Q)^T
-  void* sv_Qt;   // [c][kh][D][C] Q^T
-  // forward workspace
-  void* ws_Ut;   // [c][h][D][C]  U^T
-  // backward workspace
-  void* ws_dS;   // [c][h][D][D]  state adjoint at the end of the chunk, key-major
-  void* ws_dDt;  // [c][h][D][C]  dDelta^T
+  // Saved activations written by the forward for the backward, per chunk c and value
+  // head h (element type = the problem's storage type OT unless noted):
+  void* sv_S;    // [c][h][D][D]  state at the start of the chunk, transposed: S^T[v][d]
+  void* sv_Dt;   // [c][h][D][C]  Delta^T[v][i]
+  void* sv_T;    // [c][h][C][C]  T = (I + L)^-1, row-major
+  void* sv_M;    // [c][h][C][C]  M = Gamma o Q K^T (lower incl. diagonal), row-major
+  float* sv_gb;  // [c][h][2][C]  float32: gamma (cumulative log g), beta (0 past the end)
+  // workspace
+  void* ws_dS;   // [c][h][D][D]  state adjoint flowing into the end of the chunk, dS^T[v][d]
+  void* ws_dDt;  // [c][h][D][C]  dDelta^T[v][i]
 };
 
 // Benchmark tracing (gdn_trace.cpp): runs launch(ctx), bracketed by HIP events on s
