@@ -19,9 +19,9 @@
 //
 // Kernels after the chunk table:
 //  k_bwd_sweep (sequence x value head, one wave per 32 adjoint columns): the reverse
-//      chunk-serial pass; dS, K dS, dDelta and T^T dDelta stay in float32 accumulators.
-//      Saves dS_C and dDelta per chunk.
-//  k_bwd_grad (chunk x key head, 8 waves): all remaining gradients for the r value heads
+//      chunk-serial pass; dS, K dS, dDelta and A = T^T dDelta stay in float32 accumulators.
+//      Writes dV = diag(beta) A (staged as full rows) and saves dS_C and A per chunk.
+//  k_bwd_grad (chunk x key head, 8 waves): the remaining gradients for the r value heads
 //      of the key head, one head after the other, streaming the value dimension in
 //      blocks (the next block in flight while the current one is used). dq and dk of
 //      the key head are summed over its value heads in ascending order in registers and
@@ -43,6 +43,8 @@ template <typename TI, int C, int D> struct BwCfg {
   static constexpr int WC = 16;  // adjoint columns per wave: two waves per SIMD at D = 128
   static constexpr int NW = D / WC;
   static constexpr int CT = WC / 16, DT = D / 16, RT = C / 16;
+  static constexpr int CE = 16 / (int)sizeof(TI);  // elements per 16-byte chunk
+  static constexpr int LSO = D + CE;               // row stride of the dV staging tile
   // One LDS buffer: K, Q, dO [C][D] and T, M [C][C], all Swz layouts.
   static constexpr int O_K = 0, O_Q = C * D, O_O = 2 * C * D, O_T = 3 * C * D, O_M = O_T + C * C, BUF = O_M + C * C;
 };
@@ -89,7 +91,7 @@ template <typename TI, int C, int D>
 __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p) {
   using OT = TI;
   using CF = BwCfg<TI, C, D>;
-  constexpr int NW = CF::NW, WC = CF::WC, CT = CF::CT, DT = CF::DT, RT = CF::RT;
+  constexpr int NW = CF::NW, WC = CF::WC, CT = CF::CT, DT = CF::DT, RT = CF::RT, CE = CF::CE;
   constexpr int KSD = ks_of<OT, D>(), KSC = ks_of<OT, C>(), NSD = D / KSD, NSC = C / KSC;
   using LD = Swz<OT, D>;
   using LC = Swz<OT, C>;
@@ -97,6 +99,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
   using FragC = typename Mf<OT, KSC>::frag;
   __shared__ __align__(16) OT sbuf[2][CF::BUF];
   __shared__ __align__(16) float sgb[2][2 * C];
+  __shared__ __align__(16) OT stg[C * CF::LSO];  // the chunk's dV rows, all D columns
 
   int grp, hh;
   if (!xcd_group(blockIdx.x, p.N * p.Hk, p.r, grp, hh)) return;
@@ -145,8 +148,10 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
   int buf = 0;
   for (int c = c1 - 1; c >= c0; --c, buf ^= 1) {
     dma_wait();
-    lds_barrier();
+    lds_barrier();  // chunk c is in sbuf[buf]; every wave is done with sbuf[buf ^ 1] and stg
     if (c - 1 >= c0) issue(c - 1, buf ^ 1);
+    const int64_t t0 = sa + (int64_t)(c - c0) * C;
+    const int len = (int)(sb - t0 < C ? sb - t0 : C);
     const size_t ch = ch_idx(p, c, h);
     const OT* sK = sbuf[buf] + CF::O_K;
     const OT* sQ = sbuf[buf] + CF::O_Q;
@@ -193,17 +198,45 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
 #pragma unroll
           for (int e = 0; e < 4; ++e) dD[ct][t][e] = ex[t][e] * KdS[t][ct][e] + sc * MdO[t][ct][e];
     }
-    FragC dDb[CT][NSC];  // dDelta's fragments: B operand of T^T dDelta and the saved copy
+    FragC dDb[CT][NSC];  // dDelta's fragments: B operand of T^T dDelta
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int s = 0; s < NSC; ++s) dDb[ct][s] = from_acc<OT, KSC>(dD[ct], s, Ident{});
-    save_rows_b<OT, C, CT, RT, NSC>((OT*)p.ws_dDt + ch * D * C, v0, dD, dDb);  // dDelta^T[v][i]
-    // Z = T^T dDelta
+    // A = T^T dDelta: the gradient kernel's A (saved as A^T[v][i]) and dV = diag(beta) A
     f32x4 Z[CT][RT];
     zero(Z);
     wave_mm_cm<OT, C, RT, CT>(Z, [&](int m, int s) { return ld_t<OT, KSC, ACC, LC>(sT, 16 * m, s); },
                               [&](int j, int s) { return dDb[j][s]; });
+    {
+      FragC Ab[CT][NSC];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s = 0; s < NSC; ++s) Ab[ct][s] = from_acc<OT, KSC>(Z[ct], s, Ident{});
+      save_rows_b<OT, C, CT, RT, NSC>((OT*)p.ws_At + ch * D * C, v0, Z, Ab);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * t + g4);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)(bv[e] * Z[ct][t][e]);
+      }
+    }
+    lds_barrier();  // the chunk's dV rows are staged
+    {  // full dV rows, 16-byte stores spread over every wave
+      using V = Vec16<OT>;
+      constexpr int VPR = D / CE;
+      TI* dv = (TI*)p.dv + t0 * p.dv_rs + h * D;
+#pragma unroll
+      for (int idx = threadIdx.x; idx < C * VPR; idx += NW * 64) {
+        const int i = idx / VPR, q = idx % VPR;
+        if (i < len)
+          *reinterpret_cast<typename V::type*>(dv + (int64_t)i * p.dv_rs + q * CE) =
+              *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
+      }
+    }
     // dS <- b_n dS + Q^T (scale b o dO) - K^T (beta b o Z)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -244,8 +277,8 @@ template <int R, int Cc, int NW> struct Own {
   __device__ __forceinline__ static int cb(int w) { return w / WR; }
 };
 
-// Row-vector slots of the partial sums in k_bwd_grad.
-enum { R_EBAR = 0, R_DB1, R_RQ, R_RHO, R_DB3, R_GROW, R_GCOL, R_NSLOT };
+// Row-vector slots of the partial sums in k_bwd_grad (column sums have their own array).
+enum { R_EBAR = 0, R_DB1, R_RQ, R_RHO, R_DB3, R_GROW, R_NSLOT };
 
 constexpr int kWavesG = 8;
 constexpr int kThreadsG = kWavesG * 64;
@@ -256,22 +289,18 @@ template <typename TI, int C, int D> struct GradCfg {
   static constexpr int NBH = D / BV;                            // blocks per head
   static constexpr int RT = C / 16;
   static constexpr int NCB = kWavesG / RT;  // column blocks of the partial row sums
-  // One block buffer (elements): S0^T and dS^T row blocks [BV][D], Delta^T and dDelta^T
-  // row blocks [BV][C], dO and V column blocks [C][BV].
-  static constexpr int O_S0 = 0, O_DS = BV * D, O_DL = 2 * BV * D, O_DD = O_DL + BV * C, O_DO = O_DD + BV * C,
+  // One block buffer (elements): S0^T and dS^T row blocks [BV][D], Delta^T and A^T row
+  // blocks [BV][C], dO and V column blocks [C][BV].
+  static constexpr int O_S0 = 0, O_DS = BV * D, O_DL = 2 * BV * D, O_AT = O_DL + BV * C, O_DO = O_AT + BV * C,
                        O_V = O_DO + C * BV, BUF = O_V + C * BV;
-  // Scratch of the second phase: P o Gamma, G' = dL o Gamma and diag(beta) G', [C][C] each.
-  static constexpr int SCR = 3 * C * C;
-  // With an even block count the last block of every head sits in the second buffer,
-  // which is free during the second phase: the scratch shares it when it fits.
-  static constexpr bool SHARE = NBH % 2 == 0 && SCR <= BUF;
-  static constexpr int SCRZ = SHARE ? 16 : SCR;
+  static_assert(2 * BUF >= 2 * C * C, "the head-summed C x C matrices must fit the block buffers");
   static_assert(BUF >= 2 * C * D, "dq/dk staging must fit a block buffer");
 };
 
-// Row sums of f(i, j, x) over a wave's accumulator tiles, added into red[cb][i].
+// Row sums of f(y, e, x) over a wave's accumulator tiles (one row tile, NT column tiles),
+// added into red[16 m + 4 g + e].
 template <int NT, class F>
-__device__ __forceinline__ void acc_rowsum(const f32x4 (&t)[NT], int m, int n0, F&& f, float* red) {
+__device__ __forceinline__ void acc_rowsum(const f32x4 (&t)[NT], int m, F&& f, float* red) {
   const int l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -283,64 +312,68 @@ __device__ __forceinline__ void acc_rowsum(const f32x4 (&t)[NT], int m, int n0, 
   if (r16 == 0)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[16 * m + g4 + e] += v[e];
-  (void)n0;
 }
 
+__device__ __forceinline__ void lds_wave_fence_b() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk.
+//
+// Phase 1 streams the value dimension in blocks of BV columns (direct loads, the next
+// block in flight while the current one is used; one workgroup barrier per block).
+// A = T^T dDelta comes from the reverse sweep, which formed it anyway and already wrote
+// dV = diag(beta) A. Per block:
+//   rowsum(A o V), <S0, dS_C>,
+//   XQ += dO S0^T,  XK += Delta dS_C^T,  Y += A S0^T,  P += dO Delta^T,  AD += A Delta^T,
+// with dO unscaled (the scale is applied afterwards). Since (I + L) Delta is exactly the
+// right factor of dT, dL = -stril(T^T dT T^T) reduces to -stril(A Delta^T) = -stril(AD),
+// and the W-path gradient of K is -diag(beta b) Y with rho = -rowsum(Y o K).
+// Per head, the rest is elementwise on the wave's tiles: PG = P o Gamma (scaled),
+// G' = -stril(AD) o Gamma, Gb = diag(beta) G', and the gate sums
+//   rowsum(P o M) = rowsum(PG o Q K^T),  colsum(P o M) = colsum(PG o Q K^T),
+//   rowsum(dL o Gamma o K K^T) = rowsum(G' o K K^T),  colsum(beta_i dL o Gamma o K K^T) = colsum(Gb o K K^T),
+// with Q K^T and K K^T formed once per key head. The products with K and Q are linear in
+// PG and Gb and dq, dk sum over the value heads, so they run once per key head on the
+// head sums: dq += (sum PG) K,  dk += (sum PG)^T Q + ((sum Gb) + (sum Gb)^T) K.
 template <typename TI, int C, int D>
 __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   using OT = TI;
   using CF = GradCfg<TI, C, D>;
   constexpr int NW = kWavesG, BV = CF::BV, NBH = CF::NBH, RT = CF::RT, NCB = CF::NCB;
-  constexpr int KSC = ks_of<OT, C>(), KSB = ks_of<OT, BV>();
+  constexpr int KSC = ks_of<OT, C>(), KSB = ks_of<OT, BV>(), KSD = ks_of<OT, D>();
+  constexpr int CE = 16 / (int)sizeof(OT);
   using LD = Swz<OT, D>;
   using LC = Swz<OT, C>;
   using LB = Swz<OT, BV>;
   using OD = Own<RT, D / 16, NW>;    // C x D products
   using OC = Own<RT, C / 16, NW>;    // C x C products
-  using OB = Own<RT, BV / 16, NW>;   // C x BV products
   using OrdD = RowOrd<OT, D>;        // storage order of the saved S^T and dS^T rows
-  using OrdC = RowOrd<OT, C>;        // storage order of the saved Delta^T and dDelta^T rows
-  constexpr int NTD = OD::NT, NTC = OC::NT, NTB = OB::NT;
-  static_assert(NTB == 1, "one tile per wave of a value block");
+  using OrdC = RowOrd<OT, C>;        // storage order of the saved Delta^T and A^T rows
+  constexpr int NTD = OD::NT, NTC = OC::NT, NTB = BV / 16;
   constexpr int RS = NCB * C;  // one partial-sum slot
 
   __shared__ __align__(16) OT sK[C * D];
   __shared__ __align__(16) OT sQ[C * D];
-  __shared__ __align__(16) OT sT[2][C * C];
   __shared__ __align__(16) OT sB[2][CF::BUF];  // block buffers (job j uses sB[j & 1])
-  __shared__ __align__(16) OT sZ[CF::SCRZ];
-  __shared__ __align__(16) OT sAt[BV * C];
   __shared__ __align__(16) float sgb[2][2 * C];
-  __shared__ float red[R_NSLOT * RS];
-  __shared__ float rowv[R_NSLOT * C];
-  __shared__ float sgate[C], swv[NW];
+  __shared__ float red[2][R_NSLOT * RS];
+  __shared__ float redc[2][RT * C];  // column sums of PG o QK^T + Gb o KK^T per row tile
+  __shared__ float sgate[2][C], swv[2][NW];
 
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int n = ci.len;
   const int w = wave_id(), lane = lane_id(), g4 = (lane >> 4) * 4, r16 = lane & 15;
-  OT* scr;
-  if constexpr (CF::SHARE)
-    scr = sB[1];
-  else
-    scr = sZ;
-  OT* const sPG = scr;
-  OT* const sGp = scr + C * C;
-  OT* const sGb = scr + 2 * C * C;
 
   const int h0 = kh * p.r;
   TileDma<BV, D, NW, OT> dmS;   // S0^T, dS^T row blocks
-  TileDma<BV, C, NW, OT> dmB;   // Delta^T, dDelta^T row blocks
+  TileDma<BV, C, NW, OT> dmB;   // Delta^T, A^T row blocks
   TileDma<C, BV, NW, OT> dmV;   // dO, V column blocks
-  TileDma<C, C, NW, OT> dmC;    // T
   TileDma<C, D, NW, OT> dmD;    // K, Q
   TileDma<1, 2 * C, NW, float> dmG;  // gate record
   dmS.init(w);
   dmB.init(w);
   dmV.init(w);
-  dmC.init(w);
   dmD.init(w);
   dmG.init(w);
   auto issue_block = [&](int j) {  // job j = (head h0 + j / NBH, block j % NBH) into sB[j % 2]
@@ -350,37 +383,39 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
     dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
     dmB.issue(b + CF::O_DL, (const OT*)p.sv_Dt + ch * D * C + (size_t)v0 * C, C, BV, w);
-    dmB.issue(b + CF::O_DD, (const OT*)p.ws_dDt + ch * D * C + (size_t)v0 * C, C, BV, w);
+    dmB.issue(b + CF::O_AT, (const OT*)p.ws_At + ch * D * C + (size_t)v0 * C, C, BV, w);
     dmV.issue(b + CF::O_DO, (const OT*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n, w);
     dmV.issue(b + CF::O_V, (const OT*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n, w);
-    if (j % NBH == 0) {  // first block of a head: its T and gate record
-      dmC.issue(sT[(j / NBH) & 1], (const OT*)p.sv_T + ch * C * C, C, C, w);
+    if (j % NBH == 0)  // first block of a head: its gate record
       dmG.issue(sgb[(j / NBH) & 1], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
-    }
   };
   dmD.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
   dmD.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
   issue_block(0);
 
-  const bool aD = OD::active(w), aC = OC::active(w), aB = OB::active(w);
-  const int mt = OD::m(w);  // the wave's row tile (the same in all three grids)
-  const int nD = OD::n0(w), nC = OC::n0(w), nB = OB::n0(w);
-  const int cbD = OD::cb(w), cbC = OC::cb(w), cbB = OB::cb(w);
-  (void)cbC;
+  const bool aD = OD::active(w), aC = OC::active(w);
+  const int mt = OD::m(w);  // the wave's row tile (the same in every grid)
+  const int nD = OD::n0(w), nC = OC::n0(w), cbD = OD::cb(w), cbC = OC::cb(w);
+  const int cbA = w / RT;   // the waves sharing row tile mt split the block's columns of rowsum(A o V)
+  constexpr int FIN = NW - 1;  // the wave that finishes each head's per-row gate gradients
 
   f32x4 dqf[NTD], dkf[NTD];  // dq, dk of the key head, summed over its value heads in order
 #pragma unroll
   for (int y = 0; y < NTD; ++y) dqf[y] = dkf[y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 QKt[NTC], KKt[NTC], PGs[NTC], Gbs[NTC];  // Q K^T, K K^T, sum PG, sum Gb on the C x C tiles
+#pragma unroll
+  for (int y = 0; y < NTC; ++y) QKt[y] = KKt[y] = PGs[y] = Gbs[y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int njobs = p.r * NBH;
   for (int hh = 0; hh < p.r; ++hh) {
-    const int h = h0 + hh;
-    const OT* sTh = sT[hh & 1];
-    const float* gam = sgb[hh & 1];  // log2 units
+    const int h = h0 + hh, par = hh & 1;
+    const float* gam = sgb[par];  // log2 units
     const float* bet = gam + C;
-    TI* dV = (TI*)p.dv + (int64_t)ci.t0 * p.dv_rs + h * D;
-    if (threadIdx.x < C) sgate[threadIdx.x] = threadIdx.x < n ? p.g[(int64_t)(ci.t0 + threadIdx.x) * p.Hv + h] : 1.f;
-    for (int i = threadIdx.x; i < R_NSLOT * RS; i += kThreadsG) red[i] = 0.f;
+    float* redh = red[par];
+    float* redch = redc[par];
+    if (threadIdx.x < C) sgate[par][threadIdx.x] = threadIdx.x < n ? p.g[(int64_t)(ci.t0 + threadIdx.x) * p.Hv + h] : 1.f;
+    for (int i = threadIdx.x; i < R_NSLOT * RS; i += kThreadsG) redh[i] = 0.f;
+    for (int i = threadIdx.x; i < RT * C; i += kThreadsG) redch[i] = 0.f;
 
     // ---- phase 1: stream the value dimension
     f32x4 XQ[NTD], XK[NTD], Y[NTD], P[NTC], AD[NTC];
@@ -393,35 +428,53 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const int j = hh * NBH + b;
       const OT* cur = sB[j & 1];
       dma_wait();
-      lds_barrier();  // job j (and K, Q, T, gates with it) is in LDS
+      lds_barrier();  // job j (and K, Q, T, gates with it) is in LDS; every wave is done with job j - 1
       if (j + 1 < njobs) issue_block(j + 1);
-      const int v0 = b * BV;
+      if (j == 0 && aC) {  // Q K^T and K K^T of the key head on this wave's C x C tiles
+        f32x4 G2[2][NTC];
+#pragma unroll
+        for (int y = 0; y < NTC; ++y) G2[0][y] = G2[1][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+        wave_mm<OT, D, 2, NTC>(G2, [&](int m, int s) { return ld_n<OT, KSD, STD, LD>(m == 0 ? sQ : sK, 16 * mt, s); },
+                               [&](int y, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * (nC + y), s); });
+#pragma unroll
+        for (int y = 0; y < NTC; ++y) {
+          QKt[y] = G2[0][y];
+          KKt[y] = G2[1][y];
+        }
+      }
       const OT* sS0 = cur + CF::O_S0;
       const OT* sDS = cur + CF::O_DS;
       const OT* sDL = cur + CF::O_DL;
-      const OT* sDD = cur + CF::O_DD;
+      const OT* sAt = cur + CF::O_AT;
       const OT* sDO = cur + CF::O_DO;
       const OT* sV = cur + CF::O_V;
-      if (aB) {  // A = T^T dDelta for this block; dV = beta o A; A^T to LDS; rowsum(A o V)
-        f32x4 A[1][1];
-        zero(A);
-        // dDelta^T rows are stored in RowOrd<OT, C> order: a plain 16-byte read of a fragment-order
-        // row yields the ACC-order fragment, so T^T is read in ACC order to match.
-        constexpr int ORD_DD = RowOrd<OT, C>::frag ? ACC : STD;
-        wave_mm<OT, C, 1, 1>(A, [&](int, int s) { return ld_t<OT, KSC, ORD_DD, LC>(sTh, 16 * mt, s); },
-                             [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sDD, 16 * nB, s); });
-        const f32x4 vv = ld_col4<OT, LB>(sV, 16 * mt + g4, 16 * nB);
-        float rs[4];
+      {  // rowsum(A o V): the waves of row tile mt take the block's column tiles in turn
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        bool any = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * mt + g4 + e;
-          if (i < n) dV[(int64_t)i * p.dv_rs + v0 + 16 * nB + r16] = (TI)(bet[i] * A[0][0][e]);
-          rs[e] = row16_sum(A[0][0][e] * vv[e]);
+        for (int y = 0; y < NTB; ++y)
+          if (y % NCB == cbA) {
+            any = true;
+            const f32x4 vv = ld_col4<OT, LB>(sV, 16 * mt + g4, 16 * y);
+            // A^T[v][16 mt + g4 .. + 3] (a run of four in the row's storage order)
+            const OT* ar = sAt + LC::at(16 * y + r16, OrdC::pos(16 * mt + g4));
+            f32x4 av;
+            if constexpr (sizeof(OT) == 2) {
+              const bf16x4 x = *reinterpret_cast<const bf16x4*>(ar);
+              av = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+            } else {
+              av = *reinterpret_cast<const f32x4*>(ar);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rs[e] += av[e] * vv[e];
+          }
+        if (any) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rs[e] = row16_sum(rs[e]);
+          if (r16 == 0)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) redh[R_DB1 * RS + cbA * C + 16 * mt + g4 + e] += rs[e];
         }
-        store4b(sAt + LC::at(16 * nB + r16, 16 * mt + g4), A[0][0]);
-        if (r16 == 0)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) red[R_DB1 * RS + cbB * C + 16 * mt + g4 + e] += rs[e];
       }
       {
         using V = Vec16<OT>;
@@ -432,7 +485,6 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           for (int e = 0; e < V::N; ++e) sdot += (float)a[e] * (float)d[e];
         }
       }
-      lds_barrier();  // A^T visible
       if (aD) {
         f32x4 XY[2][NTD];  // dO S0^T and A S0^T share the S0 fragments
 #pragma unroll
@@ -443,7 +495,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         wave_mm<OT, BV, 2, NTD>(XY,
                                 [&](int m, int s) {
                                   return m == 0 ? ld_n<OT, KSB, STD, LB>(sDO, 16 * mt, s)
-                                                : ld_t<OT, KSB, STD, LC>(sAt, 16 * mt, s);
+                                                : ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * mt, s);
                                 },
                                 [&](int y, int s) { return ld_t<OT, KSB, STD, LD, OrdD>(sS0, 16 * (nD + y), s); });
         f32x4 XKa[1][NTD];
@@ -468,7 +520,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         wave_mm<OT, BV, 2, NTC>(PA,
                                 [&](int m, int s) {
                                   return m == 0 ? ld_n<OT, KSB, STD, LB>(sDO, 16 * mt, s)
-                                                : ld_t<OT, KSB, STD, LC>(sAt, 16 * mt, s);
+                                                : ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * mt, s);
                                 },
                                 [&](int y, int s) { return ld_t<OT, KSB, STD, LC, OrdC>(sDL, 16 * (nC + y), s); });
 #pragma unroll
@@ -477,25 +529,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           AD[y] = PA[1][y];
         }
       }
-      lds_barrier();  // sAt consumed before the next block rewrites it
     }
 
-    // ---- phase 2
+    // ---- phase 2 of the head: elementwise on the wave's tiles
     const float sc = p.scale, gn = gam[C - 1];
-    if (aC) {
-#pragma unroll
-      for (int y = 0; y < NTC; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * mt + g4 + e, jj = 16 * (nC + y) + r16;
-          const float gd = __builtin_amdgcn_exp2f(gam[i] - gam[jj]);
-          const float pg = i >= jj ? sc * P[y][e] * gd : 0.f;
-          const float gp = i > jj ? -AD[y][e] * gd : 0.f;
-          sPG[LC::at(i, jj)] = (OT)pg;
-          sGp[LC::at(i, jj)] = (OT)gp;
-          sGb[LC::at(i, jj)] = (OT)(bet[i] * gp);
-        }
-    }
     float bx[4], ex[4], bb[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -504,6 +541,41 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       ex[e] = __builtin_amdgcn_exp2f(gn - gam[i]);
       bb[e] = bet[i];
     }
+    if (aC) {
+      float grow[4] = {0.f, 0.f, 0.f, 0.f}, db3[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int y = 0; y < NTC; ++y) {
+        float col = 0.f;
+        const int jj = 16 * (nC + y) + r16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * mt + g4 + e;
+          const float gd = __builtin_amdgcn_exp2f(gam[i] - gam[jj]);
+          const float pg = i >= jj ? sc * P[y][e] * gd : 0.f;
+          const float gp = i > jj ? -AD[y][e] * gd : 0.f;
+          const float gb = bb[e] * gp;
+          PGs[y][e] += pg;
+          Gbs[y][e] += gb;
+          grow[e] += pg * QKt[y][e];
+          db3[e] += gp * KKt[y][e];
+          col += pg * QKt[y][e] + gb * KKt[y][e];
+        }
+        col += __shfl_xor(col, 16);
+        col += __shfl_xor(col, 32);
+        if (lane < 16) redch[mt * C + jj] += col;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        grow[e] = row16_sum(grow[e]);
+        db3[e] = row16_sum(db3[e]);
+      }
+      if (r16 == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          redh[R_GROW * RS + cbC * C + 16 * mt + g4 + e] += grow[e];
+          redh[R_DB3 * RS + cbC * C + 16 * mt + g4 + e] += db3[e];
+        }
+    }
     if (aD) {
       f32x4 Kc[NTD], Qc[NTD];  // K and Q at this wave's accumulator positions
 #pragma unroll
@@ -511,11 +583,9 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         Kc[y] = ld_col4<OT, LD>(sK, 16 * mt + g4, 16 * (nD + y));
         Qc[y] = ld_col4<OT, LD>(sQ, 16 * mt + g4, 16 * (nD + y));
       }
-      acc_rowsum<NTD>(XK, mt, nD, [&](int y, int e, float x) { return ex[e] * x * Kc[y][e]; },
-                      red + R_EBAR * RS + cbD * C);
-      acc_rowsum<NTD>(XQ, mt, nD, [&](int y, int e, float x) { return sc * x * Qc[y][e]; },
-                      red + R_RQ * RS + cbD * C);
-      acc_rowsum<NTD>(Y, mt, nD, [&](int y, int e, float x) { return -x * Kc[y][e]; }, red + R_RHO * RS + cbD * C);
+      acc_rowsum<NTD>(XK, mt, [&](int y, int e, float x) { return ex[e] * x * Kc[y][e]; }, redh + R_EBAR * RS + cbD * C);
+      acc_rowsum<NTD>(XQ, mt, [&](int y, int e, float x) { return sc * x * Qc[y][e]; }, redh + R_RQ * RS + cbD * C);
+      acc_rowsum<NTD>(Y, mt, [&](int y, int e, float x) { return -x * Kc[y][e]; }, redh + R_RHO * RS + cbD * C);
 #pragma unroll
       for (int y = 0; y < NTD; ++y)
 #pragma unroll
@@ -525,84 +595,74 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         }
     }
     sdot = wave_sum(sdot);
-    if (lane == 0) swv[w] = sdot;
-    lds_barrier();  // scratch written
-    if (aD) {
-      f32x4 Kc[NTD], Qc[NTD];
-#pragma unroll
-      for (int y = 0; y < NTD; ++y) {
-        Kc[y] = ld_col4<OT, LD>(sK, 16 * mt + g4, 16 * (nD + y));
-        Qc[y] = ld_col4<OT, LD>(sQ, 16 * mt + g4, 16 * (nD + y));
-      }
-      auto fK = [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sK, 16 * (nD + y), s); };
-      {  // (P o Gamma) K
-        f32x4 Z[1][NTD];
-        zero(Z);
-        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sPG, 16 * mt, s); }, fK);
-        acc_rowsum<NTD>(Z[0], mt, nD, [&](int y, int e, float x) { return x * Qc[y][e]; },
-                        red + R_GROW * RS + cbD * C);
-#pragma unroll
-        for (int y = 0; y < NTD; ++y) dqf[y] += Z[0][y];
-      }
-      {  // (P o Gamma)^T Q + G^T K
-        f32x4 Z[1][NTD];
-        zero(Z);
-        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sPG, 16 * mt, s); },
-                               [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sQ, 16 * (nD + y), s); });
-        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sGb, 16 * mt, s); }, fK);
-        acc_rowsum<NTD>(Z[0], mt, nD, [&](int y, int e, float x) { return x * Kc[y][e]; },
-                        red + R_GCOL * RS + cbD * C);
-#pragma unroll
-        for (int y = 0; y < NTD; ++y) dkf[y] += Z[0][y];
-      }
-      {  // G' K
-        f32x4 Z[1][NTD];
-        zero(Z);
-        wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sGp, 16 * mt, s); }, fK);
-        acc_rowsum<NTD>(Z[0], mt, nD, [&](int y, int e, float x) { return x * Kc[y][e]; },
-                        red + R_DB3 * RS + cbD * C);
-#pragma unroll
-        for (int y = 0; y < NTD; ++y)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dkf[y][e] += bb[e] * Z[0][y][e];
-      }
-    }
-    lds_barrier();
-    if (threadIdx.x < C) {
-      const int i = threadIdx.x;
-      for (int s = 0; s < R_NSLOT; ++s) {
-        float a = 0.f;
-        for (int b = 0; b < NCB; ++b) a += red[s * RS + b * C + i];
-        rowv[s * C + i] = a;
-      }
-    }
-    lds_barrier();
-    if (threadIdx.x < 64) {
-      const int i = threadIdx.x;
+    if (lane == 0) swv[par][w] = sdot;
+    lds_barrier();  // the head's partial sums are complete
+    if (w == FIN) {  // per-row gate gradients of head h (the other waves move on)
+      const int i = lane;
       const bool ok = i < C;
-      const float ebar = ok ? rowv[R_EBAR * C + i] : 0.f;
-      const float rho = ok ? rowv[R_RHO * C + i] : 0.f;
-      const float db3 = ok ? rowv[R_DB3 * C + i] : 0.f;
+      float rv[R_NSLOT], gcol = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < R_NSLOT; ++sl) {
+        float a = 0.f;
+        if (ok)
+          for (int b = 0; b < NCB; ++b) a += redh[sl * RS + b * C + i];
+        rv[sl] = a;
+      }
+      if (ok)
+        for (int m = 0; m < RT; ++m) gcol += redch[m * C + i];
       const float bi = ok ? __builtin_amdgcn_exp2f(gam[i]) : 0.f, be = ok ? bet[i] : 0.f;
       float dgam = 0.f;
-      if (ok)
-        dgam = bi * rowv[R_RQ * C + i] + be * bi * rho - ebar + rowv[R_GROW * C + i] + be * db3 -
-               rowv[R_GCOL * C + i];
-      const float ebsum = wave_sum(ebar);
+      if (ok) dgam = bi * rv[R_RQ] + be * bi * rv[R_RHO] - rv[R_EBAR] + rv[R_GROW] + be * rv[R_DB3] - gcol;
+      const float ebsum = wave_sum(rv[R_EBAR]);
       if (i == n - 1) {
         float st = 0.f;
-        for (int k = 0; k < NW; ++k) st += swv[k];
+        for (int k = 0; k < NW; ++k) st += swv[par][k];
         dgam += __builtin_amdgcn_exp2f(gn) * st + ebsum;
       }
       const float dlg = wave_rscan_incl(dgam);
       if (i < n) {
         const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
-        p.dbeta[row] = rowv[R_DB1 * C + i] + bi * rho + db3;
-        p.dg[row] = dlg / sgate[i];
+        p.dbeta[row] = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
+        p.dg[row] = dlg / sgate[par][i];
       }
     }
-    lds_barrier();
   }
+
+  // ---- the key head's products with K and Q on the head sums
+  OT* const sPGs = sB[0];         // sum PG    [C][C]
+  OT* const sGbs = sB[0] + C * C;  // sum Gb   [C][C]
+  if (aC) {
+#pragma unroll
+    for (int y = 0; y < NTC; ++y)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * mt + g4 + e, jj = 16 * (nC + y) + r16;
+        sPGs[LC::at(i, jj)] = (OT)PGs[y][e];
+        sGbs[LC::at(i, jj)] = (OT)Gbs[y][e];
+      }
+  }
+  lds_barrier();
+  if (aD) {
+    auto fK = [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sK, 16 * (nD + y), s); };
+    {  // dq += (sum PG) K
+      f32x4 Z[1][NTD];
+      zero(Z);
+      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sPGs, 16 * mt, s); }, fK);
+#pragma unroll
+      for (int y = 0; y < NTD; ++y) dqf[y] += Z[0][y];
+    }
+    {  // dk += (sum PG)^T Q + (sum Gb)^T K + (sum Gb) K
+      f32x4 Z[1][NTD];
+      zero(Z);
+      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sPGs, 16 * mt, s); },
+                             [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sQ, 16 * (nD + y), s); });
+      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sGbs, 16 * mt, s); }, fK);
+      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sGbs, 16 * mt, s); }, fK);
+#pragma unroll
+      for (int y = 0; y < NTD; ++y) dkf[y] += Z[0][y];
+    }
+  }
+  lds_barrier();
   // dq, dk of the key head: rows through LDS (the first block buffer), 16-byte stores
   {
     TI* st = (TI*)sB[0];

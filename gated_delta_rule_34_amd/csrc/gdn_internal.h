@@ -53,7 +53,7 @@ struct Prob {
   float* sv_gb;  // [c][h][2][C]  float32: gamma (cumulative log g), beta (0 past the end)
   // workspace
   void* ws_dS;   // [c][h][D][D]  state adjoint flowing into the end of the chunk, dS^T[v][d]
-  void* ws_dDt;  // [c][h][D][C]  dDelta^T[v][i]
+  void* ws_At;   // [c][h][D][C]  A^T[v][i], A = T^T dDelta
 };
 
 // Benchmark tracing (gdn_trace.cpp): runs launch(ctx), bracketed by HIP events on s
