@@ -9,14 +9,25 @@ states) + gdn_bwd over the whole batch; inputs are resident in HBM before timing
 
 Prints one JSON line. ``roofline`` covers the kernel with the largest share of the
 step, timed live with HIP events recorded by the library around each launch on the
-launch stream; ``cpu_baseline`` times the float64 oracle on one of the four sequences
-(all 48 heads), fwd + bwd, on the host cores.
+launch stream; its ``traffic`` is the measured HBM bytes per launch from the committed
+counter summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+reads for a plain copy of known size), or null when the kernels changed since those
+counters were taken. ``cpu_baseline`` times the float64 oracle on the whole batch (all
+four sequences, all 48 heads), fwd + bwd, on the host cores, repeated to at least 10 s.
+
+Counter runs: ``--pmc-calib`` first copies a buffer of known size (the calibration
+dispatch); ``--summarize-pmc FETCH_DIR WRITE_DIR`` turns the two rocprofv3 result
+directories into the committed summary.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +36,92 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN fwd+bwd tokens/s @Hk16/Hv48/D128 T=4096; % MFMA / HBM roofline"
 PEAK = {"f32_mfma": 157.3e12, "bf16_mfma": 2.5e15, "hbm": 8.0e12}
+WORKLOAD_TAG = "B4_T4096_Hk16_Hv48_D128_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"gdn_kernels_{WORKLOAD_TAG}_hbm_traffic.md")
+CALIB_BYTES = 3 << 27  # the calibration copy reads and writes 384 MiB
+
+
+def source_hash():
+    """Hash of the HIP sources and headers: counter summaries are valid for this code only."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_34_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _kernel_key(name):
+    m = re.search(r"gdn(?:::|\d+)(k_\w+?)(?:I|<|\()", name)
+    return m.group(1) if m else None
+
+
+def _read_counters(d, counter):
+    """[(dispatch id, kernel name, value)] of one counter from a rocprofv3 result directory."""
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(out)
+
+
+def summarize_pmc(fetch_dir, write_dir, out_path, command):
+    """Write the traffic summary: per gdn kernel the average FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch) and the calibrated HBM bytes, with the copy-kernel scale factors."""
+    fetch, write = _read_counters(fetch_dir, "FETCH_SIZE"), _read_counters(write_dir, "WRITE_SIZE")
+
+    def calib(rows):
+        # the calibration copy is the first non-gdn dispatch that reads (or writes) ~CALIB_BYTES
+        for did, name, v in rows:
+            if _kernel_key(name) is None and 0.5 * CALIB_BYTES < v * 1024 < 2.0 * CALIB_BYTES:
+                return did, v
+        raise SystemExit("calibration copy not found (run the counter passes with --pmc-calib)")
+
+    (fd, fv), (wd, wv) = calib(fetch), calib(write)
+    f_scale, w_scale = CALIB_BYTES / (fv * 1024), CALIB_BYTES / (wv * 1024)
+    agg = {}
+    for rows, key in ((fetch, "fetch_kib"), (write, "write_kib")):
+        for _, name, v in rows:
+            k = _kernel_key(name)
+            if k:
+                agg.setdefault(k, {}).setdefault(key, []).append(v)
+    summary = {"source_hash": source_hash(), "calib_bytes": CALIB_BYTES, "fetch_scale": round(f_scale, 4),
+               "write_scale": round(w_scale, 4), "kernels": {}}
+    lines = [f"# HBM traffic per launch: gdn kernels, 4 x 4096 tokens, Hk=16, Hv=48, D=128, bf16, chunk 64", "",
+             "Two rocprofv3 counter passes of the same bench command (one counter each); REPO is the repository root:",
+             "", "```", command, "```", "",
+             f"Calibration: a plain copy of {CALIB_BYTES >> 20} MiB (torch `copy_`, the first large non-gdn dispatch) "
+             f"reads FETCH_SIZE = {fv:.0f} KiB (dispatch {fd}) and WRITE_SIZE = {wv:.0f} KiB (dispatch {wd}); "
+             f"scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write) turn counter KiB into bytes.", "",
+             "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
+             "|---|---|---|---|---|"]
+    for k in sorted(agg):
+        fk = sum(agg[k].get("fetch_kib", [0])) / max(1, len(agg[k].get("fetch_kib", [])))
+        wk = sum(agg[k].get("write_kib", [0])) / max(1, len(agg[k].get("write_kib", [])))
+        total = fk * 1024 * f_scale + wk * 1024 * w_scale
+        summary["kernels"][k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "bytes": int(total)}
+        lines.append(f"| {k} | {len(agg[k].get('fetch_kib', []))} | {fk:.0f} | {wk:.0f} | {total / 1e6:.1f} MB |")
+    lines += ["", "Machine-readable (bench.py reads it; valid while the kernel sources hash to `source_hash`):", "",
+              "```json", json.dumps(summary, indent=1), "```", ""]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def measured_traffic(kernel):
+    """Calibrated HBM bytes per launch of `kernel` from the committed summary, or None when
+    there is none or the sources changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        blob = json.loads(text[text.index("```json") + 7: text.rindex("```")])
+    except (OSError, ValueError):
+        return None
+    if blob.get("source_hash") != source_hash():
+        return None
+    k = blob.get("kernels", {}).get(kernel)
+    return k["bytes"] if k else None
 
 
 def kernel_model(name, C, D, Hk, Hv, n_chunks, es=2):
@@ -40,13 +137,15 @@ def kernel_model(name, C, D, Hk, Hv, n_chunks, es=2):
         "k_prep": (ck * 4 * C * C * D, ck * 2 * cd + ch * (gates + 2 * cc + gates)),
         # K S, Q S, T X, M Delta, K^T (e o Delta). Reads K, Q, V, T, M, gates; writes S, Delta, O.
         "k_fwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + gates + dd + 2 * cd)),
-        # K dS, M^T dO, T^T dDelta, Q^T dO, K^T Z. Reads K, Q, dO, T, M, gates; writes dS, dDelta.
-        "k_bwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + gates + dd + cd)),
-        # T^T dDelta, dO S0^T, Delta dS^T, A S0^T, dO Delta^T, A Delta^T, (P o Gamma) K,
-        # (P o Gamma)^T Q, G^T K, G' K. Reads S0, dS, Delta, dDelta, dO, V, T, gates, g per
-        # value head and K, Q per key head; writes dV, dg, dbeta and dq, dk.
-        "k_bwd_grad": (ch * (6 * C * D * D + 14 * C * C * D),
-                       ch * (2 * dd + 4 * cd + cc + gates + 4 * C + cd + 8 * C) + ck * 4 * cd),
+        # K dS, M^T dO, T^T dDelta, Q^T dO, K^T (nb o A). Reads K, Q, dO, T, M, gates; writes dS,
+        # A^T (A = T^T dDelta) and dV.
+        "k_bwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + gates + dd + 2 * cd)),
+        # Per value head dO S0^T, Delta dS^T, A S0^T, dO Delta^T, A Delta^T; per key head Q K^T,
+        # K K^T and the three products that fold the head sums into dq and dk. Reads S0, dS,
+        # Delta, A^T, dO, V, gates and g per value head, K and Q per key head; writes dg, dbeta
+        # per value head and dq, dk per key head.
+        "k_bwd_grad": (ch * (6 * C * D * D + 4 * C * C * D) + ck * 10 * C * C * D,
+                       ch * (2 * dd + 4 * cd + gates + 4 * C + 8 * C) + ck * 4 * cd),
     }
     return model.get(name)
 
@@ -64,7 +163,15 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-calib", action="store_true",
+                    help="first copy a buffer of known size (the counter calibration dispatch)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic summary from two rocprofv3 counter result directories")
+    ap.add_argument("--pmc-command", default="", help="command line recorded in the traffic summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], TRAFFIC_FILE, args.pmc_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
@@ -78,6 +185,14 @@ def main():
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gdn_gpu import problem, to_device
     from synth import config_case
+
+    if args.pmc_calib:  # a plain copy of known size, for the FETCH_SIZE / WRITE_SIZE scale factors
+        src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     case = config_case(3)
     d = to_device(case)
@@ -145,7 +260,7 @@ def main():
     else:
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1),
                     "peak": PEAK["hbm"] / 1e9, "unit": "GB/s", "frac": round(nbytes / avg_s / PEAK["hbm"], 4)}
-    roofline.update({"traffic": None, "avg_launch_ms": round(avg_s * 1e3, 4),
+    roofline.update({"traffic": measured_traffic(dom), "avg_launch_ms": round(avg_s * 1e3, 4),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_frac": round(flops / avg_s / PEAK["bf16_mfma"], 4),
                      "hbm_frac": round(nbytes / avg_s / PEAK["hbm"], 4)})
@@ -170,12 +285,17 @@ def main():
         oracle.build()
         nthreads = min(oracle.default_threads(), 16)
         t0 = time.perf_counter()
-        oracle.run_case(case, backward=True, seqs=[0], nthreads=nthreads)
-        dt = time.perf_counter() - t0
-        cpu = {"value": round(case.lens[0] / dt, 2), "unit": "tokens/s", "cores": min(nthreads, Hk),
+        reps = 0
+        while True:  # the whole batch, repeated until at least 10 s of host work
+            oracle.run_case(case, backward=True, nthreads=nthreads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or reps >= 8:
+                break
+        cpu = {"value": round(reps * T / dt, 2), "unit": "tokens/s", "cores": min(nthreads, case.N * Hk),
                "kind": "oracle",
-               "sample": f"sequence 0 of 4 ({case.lens[0]} tokens, all {Hv} value heads), fwd+bwd, float64; "
-                         f"{dt:.1f} s"}
+               "sample": f"the whole batch ({case.N} x {case.lens[0]} tokens, all {Hv} value heads) x {reps}, "
+                         f"fwd+bwd, float64; {dt:.1f} s"}
 
     line = {
         "metric": METRIC, "value": round(T / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
