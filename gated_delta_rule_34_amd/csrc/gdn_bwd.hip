@@ -293,7 +293,8 @@ template <typename TI, int C, int D> struct GradCfg {
   // blocks [BV][C], dO and V column blocks [C][BV].
   static constexpr int O_S0 = 0, O_DS = BV * D, O_DL = 2 * BV * D, O_AT = O_DL + BV * C, O_DO = O_AT + BV * C,
                        O_V = O_DO + C * BV, BUF = O_V + C * BV;
-  static_assert(2 * BUF >= 2 * C * C, "the head-summed C x C matrices must fit the block buffers");
+  static constexpr int NBUF = 3;  // block buffers: two blocks in flight
+  static_assert(NBUF * BUF >= 2 * C * C, "the head-summed C x C matrices must fit the block buffers");
   static_assert(BUF >= 2 * C * D, "dq/dk staging must fit a block buffer");
 };
 
@@ -318,8 +319,8 @@ __device__ __forceinline__ void lds_wave_fence_b() { asm volatile("s_waitcnt lgk
 
 // Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk.
 //
-// Phase 1 streams the value dimension in blocks of BV columns (direct loads, the next
-// block in flight while the current one is used; one workgroup barrier per block).
+// Phase 1 streams the value dimension in blocks of BV columns (direct loads, the next two
+// blocks in flight while the current one is used; one workgroup barrier per block).
 // A = T^T dDelta comes from the reverse sweep, which formed it anyway and already wrote
 // dV = diag(beta) A. Per block:
 //   rowsum(A o V), <S0, dS_C>,
@@ -353,11 +354,11 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
 
   __shared__ __align__(16) OT sK[C * D];
   __shared__ __align__(16) OT sQ[C * D];
-  __shared__ __align__(16) OT sB[2][CF::BUF];  // block buffers (job j uses sB[j & 1])
-  __shared__ __align__(16) float sgb[2][2 * C];
+  __shared__ __align__(16) OT sB[CF::NBUF][CF::BUF];  // block buffers (job j uses sB[j % NBUF])
+  __shared__ __align__(16) float sgb[3][2 * C];        // gate records (head hh uses sgb[hh % 3])
   __shared__ float red[2][R_NSLOT * RS];
   __shared__ float redc[2][RT * C];  // column sums of PG o QK^T + Gb o KK^T per row tile
-  __shared__ float sgate[2][C], swv[2][NW];
+  __shared__ float swv[2][NW];
 
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
@@ -366,37 +367,60 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   const int w = wave_id(), lane = lane_id(), g4 = (lane >> 4) * 4, r16 = lane & 15;
 
   const int h0 = kh * p.r;
-  TileDma<BV, D, NW, OT> dmS;   // S0^T, dS^T row blocks
-  TileDma<BV, C, NW, OT> dmB;   // Delta^T, A^T row blocks
-  TileDma<C, BV, NW, OT> dmV;   // dO, V column blocks
+  constexpr int NH = NW / 2;  // the two halves of the waves load different tensors of a block
+  TileDma<BV, D, NW, OT> dmS;   // S0^T, dS^T row blocks (every wave)
+  TileDma<BV, C, NH, OT> dmB;   // Delta^T (first half) or A^T (second half) row blocks
+  TileDma<C, BV, NH, OT> dmV;   // dO (first half) or V (second half) column blocks
   TileDma<C, D, NW, OT> dmD;    // K, Q
   TileDma<1, 2 * C, NW, float> dmG;  // gate record
+  const int wh = w % NH;
   dmS.init(w);
-  dmB.init(w);
-  dmV.init(w);
+  dmB.init(wh);
+  dmV.init(wh);
   dmD.init(w);
   dmG.init(w);
-  auto issue_block = [&](int j) {  // job j = (head h0 + j / NBH, block j % NBH) into sB[j % 2]
+  // Job j = (head h0 + j / NBH, block j % NBH) goes into sB[j % NBUF]; the first block of a
+  // head also brings the head's gate record. A job's loads are issued in four parts spread
+  // over the step two jobs earlier, so that no wave stalls long on a full memory queue.
+  auto issue_part = [&](int j, int part) {
     const int h = h0 + j / NBH, v0 = (j % NBH) * BV;
     const size_t ch = ch_idx(p, c, h);
-    OT* b = sB[j & 1];
-    dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
-    dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
-    dmB.issue(b + CF::O_DL, (const OT*)p.sv_Dt + ch * D * C + (size_t)v0 * C, C, BV, w);
-    dmB.issue(b + CF::O_AT, (const OT*)p.ws_At + ch * D * C + (size_t)v0 * C, C, BV, w);
-    dmV.issue(b + CF::O_DO, (const OT*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n, w);
-    dmV.issue(b + CF::O_V, (const OT*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n, w);
-    if (j % NBH == 0)  // first block of a head: its gate record
-      dmG.issue(sgb[(j / NBH) & 1], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+    OT* b = sB[j % CF::NBUF];
+    if (part == 0) {
+      dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
+      if (j % NBH == 0) dmG.issue(sgb[(j / NBH) % 3], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+    } else if (part == 1) {
+      dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
+    } else if (part == 2) {
+      if (w < NH)
+        dmB.issue(b + CF::O_DL, (const OT*)p.sv_Dt + ch * D * C + (size_t)v0 * C, C, BV, wh);
+      else
+        dmB.issue(b + CF::O_AT, (const OT*)p.ws_At + ch * D * C + (size_t)v0 * C, C, BV, wh);
+    } else {
+      if (w < NH)
+        dmV.issue(b + CF::O_DO, (const OT*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n, wh);
+      else
+        dmV.issue(b + CF::O_V, (const OT*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n, wh);
+    }
+  };
+  auto issue_block = [&](int j) {
+    for (int part = 0; part < 4; ++part) issue_part(j, part);
+  };
+  // This wave's load instructions of job j.
+  auto job_loads = [&](int j) {
+    return 2 * dmS.count(w) + dmB.count(wh) + dmV.count(wh) + (j % NBH == 0 ? dmG.count(w) : 0);
   };
   dmD.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
   dmD.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
   issue_block(0);
+  if (1 < p.r * NBH) issue_block(1);
 
   const bool aD = OD::active(w), aC = OC::active(w);
   const int mt = OD::m(w);  // the wave's row tile (the same in every grid)
   const int nD = OD::n0(w), nC = OC::n0(w), cbD = OD::cb(w), cbC = OC::cb(w);
-  const int cbA = w / RT;   // the waves sharing row tile mt split the block's columns of rowsum(A o V)
+  // rowsum(A o V) is the diagonal of A V^T: the wave holding the diagonal C x C tile of its
+  // row tile accumulates that tile of A V^T (one MFMA per block) and reads the diagonal.
+  const bool dgw = aC && nC <= mt && mt < nC + NTC;
   constexpr int FIN = NW - 1;  // the wave that finishes each head's per-row gate gradients
 
   f32x4 dqf[NTD], dkf[NTD];  // dq, dk of the key head, summed over its value heads in order
@@ -409,16 +433,15 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   const int njobs = p.r * NBH;
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = h0 + hh, par = hh & 1;
-    const float* gam = sgb[par];  // log2 units
+    const float* gam = sgb[hh % 3];  // log2 units
     const float* bet = gam + C;
     float* redh = red[par];
     float* redch = redc[par];
-    if (threadIdx.x < C) sgate[par][threadIdx.x] = threadIdx.x < n ? p.g[(int64_t)(ci.t0 + threadIdx.x) * p.Hv + h] : 1.f;
     for (int i = threadIdx.x; i < R_NSLOT * RS; i += kThreadsG) redh[i] = 0.f;
     for (int i = threadIdx.x; i < RT * C; i += kThreadsG) redch[i] = 0.f;
 
     // ---- phase 1: stream the value dimension
-    f32x4 XQ[NTD], XK[NTD], Y[NTD], P[NTC], AD[NTC];
+    f32x4 XQ[NTD], XK[NTD], Y[NTD], P[NTC], AD[NTC], AV[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
     for (int y = 0; y < NTD; ++y) XQ[y] = XK[y] = Y[y] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -426,10 +449,11 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     float sdot = 0.f;
     for (int b = 0; b < NBH; ++b) {
       const int j = hh * NBH + b;
-      const OT* cur = sB[j & 1];
-      dma_wait();
-      lds_barrier();  // job j (and K, Q, T, gates with it) is in LDS; every wave is done with job j - 1
-      if (j + 1 < njobs) issue_block(j + 1);
+      const OT* cur = sB[j % CF::NBUF];
+      dma_wait_keep(j + 1 < njobs ? job_loads(j + 1) : 0);  // job j's loads (and all before) are done
+      lds_barrier();  // job j (and K, Q, gates with it) is in LDS; every wave is done with job j - 1
+      const bool nxt2 = j + 2 < njobs;
+      if (nxt2) issue_part(j + 2, 0);
       if (j == 0 && aC) {  // Q K^T and K K^T of the key head on this wave's C x C tiles
         f32x4 G2[2][NTC];
 #pragma unroll
@@ -448,34 +472,6 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const OT* sAt = cur + CF::O_AT;
       const OT* sDO = cur + CF::O_DO;
       const OT* sV = cur + CF::O_V;
-      {  // rowsum(A o V): the waves of row tile mt take the block's column tiles in turn
-        float rs[4] = {0.f, 0.f, 0.f, 0.f};
-        bool any = false;
-#pragma unroll
-        for (int y = 0; y < NTB; ++y)
-          if (y % NCB == cbA) {
-            any = true;
-            const f32x4 vv = ld_col4<OT, LB>(sV, 16 * mt + g4, 16 * y);
-            // A^T[v][16 mt + g4 .. + 3] (a run of four in the row's storage order)
-            const OT* ar = sAt + LC::at(16 * y + r16, OrdC::pos(16 * mt + g4));
-            f32x4 av;
-            if constexpr (sizeof(OT) == 2) {
-              const bf16x4 x = *reinterpret_cast<const bf16x4*>(ar);
-              av = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-            } else {
-              av = *reinterpret_cast<const f32x4*>(ar);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rs[e] += av[e] * vv[e];
-          }
-        if (any) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rs[e] = row16_sum(rs[e]);
-          if (r16 == 0)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) redh[R_DB1 * RS + cbA * C + 16 * mt + g4 + e] += rs[e];
-        }
-      }
       {
         using V = Vec16<OT>;
         for (int idx = threadIdx.x; idx < D * BV / V::N; idx += kThreadsG) {  // same layout: index-wise product
@@ -485,6 +481,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           for (int e = 0; e < V::N; ++e) sdot += (float)a[e] * (float)d[e];
         }
       }
+      if (nxt2) issue_part(j + 2, 1);  // every wave issues every part (the wait counts rely on it)
       if (aD) {
         f32x4 XY[2][NTD];  // dO S0^T and A S0^T share the S0 fragments
 #pragma unroll
@@ -510,6 +507,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           XK[y] = XKa[0][y];
         }
       }
+      if (nxt2) issue_part(j + 2, 2);
       if (aC) {
         f32x4 PA[2][NTC];  // dO Delta^T and A Delta^T share the Delta fragments
 #pragma unroll
@@ -529,6 +527,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           AD[y] = PA[1][y];
         }
       }
+      if (nxt2) issue_part(j + 2, 3);
+      if (dgw)  // A V^T on the diagonal tile of row tile mt
+        wave_mm<OT, BV, 1, 1>(AV, [&](int, int s) { return ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * mt, s); },
+                              [&](int, int s) { return ld_n<OT, KSB, STD, LB>(sV, 16 * mt, s); });
     }
 
     // ---- phase 2 of the head: elementwise on the wave's tiles
@@ -540,6 +542,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       bx[e] = __builtin_amdgcn_exp2f(gam[i]);
       ex[e] = __builtin_amdgcn_exp2f(gn - gam[i]);
       bb[e] = bet[i];
+    }
+    if (dgw) {  // lane (g, r) holds (A V^T)[4 g + e][r]: the diagonal is e = r - 4 g
+      const int e = r16 - g4;
+      if (e >= 0 && e < 4) redh[R_DB1 * RS + 16 * mt + r16] = AV[0][0][e];
     }
     if (aC) {
       float grow[4] = {0.f, 0.f, 0.f, 0.f}, db3[4] = {0.f, 0.f, 0.f, 0.f};
@@ -623,7 +629,8 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       if (i < n) {
         const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
         p.dbeta[row] = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
-        p.dg[row] = dlg / sgate[par][i];
+        // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
+        p.dg[row] = dlg * __builtin_amdgcn_exp2f((i > 0 ? gam[i - 1] : 0.f) - gam[i]);
       }
     }
   }

@@ -302,6 +302,13 @@ template <int R, int Cn, int NW, typename T> struct TileDma {
       cof[u] = (uint32_t)(c * 16);
     }
   }
+  // Instructions wave w issues per tile (wave-uniform).
+  __device__ __forceinline__ static int count(int w) {
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) n += (u * NW + w) * 64 < TOT ? 1 : 0;
+    return n;
+  }
   __device__ __forceinline__ void issue(T* lds, const T* src, int64_t rs, int nvalid, int w) const {
     const uint32_t rsb = (uint32_t)(rs * (int64_t)sizeof(T));
     const i32x4 rsrc = buf_rsrc(src, (uint32_t)nvalid * rsb);
@@ -319,6 +326,20 @@ template <int R, int Cn, int NW, typename T> struct TileDma {
 // Wait until this wave's outstanding vector-memory operations (loads into LDS included)
 // have completed: s_waitcnt vmcnt(0), other counters left alone.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most n of this wave's vector-memory operations are outstanding. They
+// complete in issue order, so this waits for everything issued before the last n. n must
+// be wave-uniform; above 15 it waits as for 15 (an earlier point, never a later one).
+__device__ __forceinline__ void dma_wait_keep(int n) {
+#define GDN_VMCNT(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | k); break;
+  switch (n < 15 ? n : 15) {
+    GDN_VMCNT(0) GDN_VMCNT(1) GDN_VMCNT(2) GDN_VMCNT(3) GDN_VMCNT(4) GDN_VMCNT(5) GDN_VMCNT(6) GDN_VMCNT(7)
+    GDN_VMCNT(8) GDN_VMCNT(9) GDN_VMCNT(10) GDN_VMCNT(11) GDN_VMCNT(12) GDN_VMCNT(13) GDN_VMCNT(14)
+    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15); break;
+  }
+#undef GDN_VMCNT
+}
 
 // Workgroup barrier that orders LDS accesses only: it does not wait for the wave's
 // outstanding global memory operations, so loads into LDS stay in flight across it.
