@@ -299,7 +299,7 @@ template <typename TI, int C, int D> struct GradCfg {
 };
 
 // Row sums of f(y, e, x) over a wave's accumulator tiles (one row tile, NT column tiles),
-// added into red[16 m + 4 g + e].
+// stored to red[16 m + 4 g + e] (each wave owns its slots: no read-modify-write).
 template <int NT, class F>
 __device__ __forceinline__ void acc_rowsum(const f32x4 (&t)[NT], int m, F&& f, float* red) {
   const int l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
@@ -312,7 +312,7 @@ __device__ __forceinline__ void acc_rowsum(const f32x4 (&t)[NT], int m, F&& f, f
   for (int e = 0; e < 4; ++e) v[e] = row16_sum(v[e]);
   if (r16 == 0)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[16 * m + g4 + e] += v[e];
+    for (int e = 0; e < 4; ++e) red[16 * m + g4 + e] = v[e];
 }
 
 __device__ __forceinline__ void lds_wave_fence_b() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         }
         col += __shfl_xor(col, 16);
         col += __shfl_xor(col, 32);
-        if (lane < 16) redch[mt * C + jj] += col;
+        if (lane < 16) redch[mt * C + jj] = col;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -578,8 +578,8 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       if (r16 == 0)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          redh[R_GROW * RS + cbC * C + 16 * mt + g4 + e] += grow[e];
-          redh[R_DB3 * RS + cbC * C + 16 * mt + g4 + e] += db3[e];
+          redh[R_GROW * RS + cbC * C + 16 * mt + g4 + e] = grow[e];
+          redh[R_DB3 * RS + cbC * C + 16 * mt + g4 + e] = db3[e];
         }
     }
     if (aD) {

@@ -7,42 +7,45 @@ namespace gdn {
 
 constexpr int NTHREADS = 256;  // threads of the chunk-table kernel
 
-// Wave-level scans and sums over 64 lanes (fixed combination order: deterministic).
-__device__ __forceinline__ float wave_scan_incl(float x) {  // sum of lanes 0..l
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float t = __shfl_up(x, off);
-    if (l >= off) x += t;
-  }
-  return x;
-}
-__device__ __forceinline__ float wave_rscan_incl(float x) {  // sum of lanes l..63
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float t = __shfl_down(x, off);
-    if (l + off < 64) x += t;
-  }
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+// DPP move of x (lanes whose source is outside the row, or whose row is masked off, get 0).
+template <int CTRL, int ROWS = 0xF> __device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
 }
 
 // Sum over the 16 lanes of a DPP row (lanes 16k .. 16k + 15), returned in every lane of
 // the row: pair and quad swaps, then the half-row and row mirrors (no LDS traffic).
-template <int CTRL> __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
   x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
   x += dpp<0x141>(x);  // row_half_mirror
   x += dpp<0x140>(x);  // row_mirror
   return x;
+}
+
+// Wave-level scans and sums over 64 lanes, in DPP steps (fixed combination order, so the
+// results are deterministic).
+__device__ __forceinline__ float wave_scan_incl(float x) {  // sum of lanes 0..l
+  x += dpp<0x111>(x);       // row_shr:1
+  x += dpp<0x112>(x);       // row_shr:2
+  x += dpp<0x114>(x);       // row_shr:4
+  x += dpp<0x118>(x);       // row_shr:8: inclusive sums within each row of 16
+  x += dpp<0x142, 0xA>(x);  // row_bcast:15 -> rows 1 and 3 add the total of the row before
+  x += dpp<0x143, 0xC>(x);  // row_bcast:31 -> rows 2 and 3 add the total of rows 0 and 1
+  return x;
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+__device__ __forceinline__ float wave_sum(float x) { return lane_value(wave_scan_incl(x), 63); }
+__device__ __forceinline__ float wave_rscan_incl(float x) {  // sum of lanes l..63
+  x += dpp<0x101>(x);  // row_shl:1
+  x += dpp<0x102>(x);  // row_shl:2
+  x += dpp<0x104>(x);  // row_shl:4
+  x += dpp<0x108>(x);  // row_shl:8: sums of lanes l.. end of row
+  const float t1 = lane_value(x, 16), t2 = lane_value(x, 32), t3 = lane_value(x, 48);
+  const float t23 = t2 + t3, t123 = t1 + t23;
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row == 0 ? t123 : row == 1 ? t23 : row == 2 ? t3 : 0.f);
 }
 
 __device__ __forceinline__ size_t ch_idx(const Prob& p, int c, int h) { return (size_t)c * p.Hv + h; }
