@@ -77,7 +77,7 @@ size_t bwd_ws(const gdn_problem* p) {
   return r.chunks + r.seq_chunk + r.oDD + r.oCD;  // + dS^T and A^T per chunk
 }
 
-// Saved activations: S^T, Delta^T, T, M per chunk and value head, and the gate record.
+// Saved activations: S^T, Delta, T, M per chunk and value head, and the gate record.
 size_t saved_bytes(const gdn_problem* p) {
   const Regions r = regions(p);
   return r.oDD + r.oCD + 2 * r.oCC + r.gb;
@@ -87,7 +87,7 @@ void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
   char* b = static_cast<char*>(saved);
   P.sv_S = b;
   b += r.oDD;
-  P.sv_Dt = b;
+  P.sv_D = b;
   b += r.oCD;
   P.sv_T = b;
   b += r.oCC;

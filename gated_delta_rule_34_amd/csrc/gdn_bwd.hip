@@ -263,18 +263,22 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
 }
 
 // ---------------------------------------------------------------------------- grad
-// Tile ownership of an R x Cc grid of 16 x 16 tiles over NW waves (R, Cc powers of two,
-// R <= NW): wave w owns row tile w % WR and the NT column tiles from (w / WR) NT. Every
-// product with the same grid gives a wave the same tiles, so their accumulators combine
-// elementwise. cb = w / WR indexes the wave's column block in partial row sums.
-template <int R, int Cc, int NW> struct Own {
-  static_assert(R <= NW, "one row tile per wave at most");
-  static constexpr int WR = R, WCc = NW / R;
-  static constexpr int NT = Cc >= WCc ? Cc / WCc : 1;
-  __device__ __forceinline__ static bool active(int w) { return (w / WR) * NT < Cc; }
-  __device__ __forceinline__ static int m(int w) { return w % WR; }
-  __device__ __forceinline__ static int n0(int w) { return (w / WR) * NT; }
-  __device__ __forceinline__ static int cb(int w) { return w / WR; }
+// Wave tiling of the C x D products (RT x DT tiles of 16 x 16) and of the C x C products
+// (RT x RT tiles) over NW waves. Wave w owns row block rb = w % WRB (MT row tiles) and
+// column block cb = w / WRB: NT of the D tiles and NTC of the C tiles. The C x C tiles of a
+// wave lie in its own row tiles, so both kinds of product share the wave's A fragments, and
+// with MT = 2 every fragment read from LDS feeds at least two MFMAs.
+template <int RT, int DT, int NW> struct Part {
+  static constexpr int MT = (RT >= 2 && RT * DT >= 2 * NW) ? 2 : 1;
+  static constexpr int WRB = RT / MT;
+  static_assert(WRB <= NW && NW % WRB == 0, "row blocks must divide the waves");
+  static constexpr int WCB = NW / WRB;
+  static constexpr int NT = DT >= WCB ? DT / WCB : 1;
+  static constexpr int NTC = RT >= WCB ? RT / WCB : 1;
+  __device__ __forceinline__ static int rb(int w) { return w % WRB; }
+  __device__ __forceinline__ static int cb(int w) { return w / WRB; }
+  __device__ __forceinline__ static bool activeD(int w) { return cb(w) * NT < DT; }
+  __device__ __forceinline__ static bool activeC(int w) { return cb(w) * NTC < RT; }
 };
 
 // Row-vector slots of the partial sums in k_bwd_grad (column sums have their own array).
@@ -284,18 +288,26 @@ constexpr int kWavesG = 8;
 constexpr int kThreadsG = kWavesG * 64;
 
 template <typename TI, int C, int D> struct GradCfg {
-  static constexpr int E = (int)sizeof(TI);
-  static constexpr int BV = E == 2 ? (D >= 32 ? 32 : D) : 16;  // value columns per block
-  static constexpr int NBH = D / BV;                            // blocks per head
-  static constexpr int RT = C / 16;
-  static constexpr int NCB = kWavesG / RT;  // column blocks of the partial row sums
-  // One block buffer (elements): S0^T and dS^T row blocks [BV][D], Delta^T and A^T row
-  // blocks [BV][C], dO and V column blocks [C][BV].
-  static constexpr int O_S0 = 0, O_DS = BV * D, O_DL = 2 * BV * D, O_AT = O_DL + BV * C, O_DO = O_AT + BV * C,
-                       O_V = O_DO + C * BV, BUF = O_V + C * BV;
+  static constexpr int BV = grad_block<TI, D>();  // value columns per block
+  static constexpr int NBH = D / BV;              // blocks per head
+  static constexpr int PB = NBH >= 2 ? 2 : 1;     // blocks per pair (dO and V are loaded by pairs)
+  static constexpr int RT = C / 16, DT = D / 16;
+  using PT = Part<RT, DT, kWavesG>;
+  static constexpr int NCB = PT::WCB;  // column blocks of the partial row sums
+  // One block buffer (elements): S0^T and dS^T row blocks [BV][D], the A^T row block
+  // [BV][C] and the Delta block [C][BV] (all contiguous in memory).
+  static constexpr int O_S0 = 0, O_DS = BV * D, O_AT = 2 * BV * D, O_DL = O_AT + BV * C, BUF = O_DL + C * BV;
   static constexpr int NBUF = 3;  // block buffers: two blocks in flight
-  static_assert(NBUF * BUF >= 2 * C * C, "the head-summed C x C matrices must fit the block buffers");
-  static_assert(BUF >= 2 * C * D, "dq/dk staging must fit a block buffer");
+  // One pair buffer: the dO and V column blocks [C][PB BV] of a pair of blocks. dO and V
+  // are row views with long strides; a pair makes each row segment a whole 128-byte line.
+  // With one block per pair, a pair is issued in the step two blocks before its own, so
+  // three pair buffers are needed; with two, in the step of the previous pair's first block.
+  static constexpr int PW = PB * BV, O_DO = 0, O_V = C * PW, PBUF = 2 * C * PW, NPBUF = PB == 1 ? 3 : 2;
+  // Block and pair buffers are one LDS array; after the last block it holds the head-summed
+  // C x C matrices and then the dq, dk rows.
+  static constexpr int O_P = NBUF * BUF, SMEM = O_P + NPBUF * PBUF;
+  static_assert(SMEM >= 2 * C * C && SMEM >= 2 * C * D, "end-phase scratch must fit the buffers");
+  static_assert(NBH % PB == 0, "pairs do not straddle heads");
 };
 
 // Row sums of f(y, e, x) over a wave's accumulator tiles (one row tile, NT column tiles),
@@ -315,46 +327,68 @@ __device__ __forceinline__ void acc_rowsum(const f32x4 (&t)[NT], int m, F&& f, f
     for (int e = 0; e < 4; ++e) red[16 * m + g4 + e] = v[e];
 }
 
-__device__ __forceinline__ void lds_wave_fence_b() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ float pick4(f32x4 v, int e) { return e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : v[3]; }
+
+// Elements c .. c + 3 of row r of an LDS tile (c % 4 == 0: one 8- or 16-byte read).
+template <typename OT, class L> __device__ __forceinline__ f32x4 ld_row4(const OT* X, int r, int c) {
+  if constexpr (sizeof(OT) == 2) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(X + L::at(r, c));
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  } else {
+    return *reinterpret_cast<const f32x4*>(X + L::at(r, c));
+  }
+}
+
+// Sum over the four lanes l % 16 + {0, 16, 32, 48} (the four row groups of an accumulator).
+__device__ __forceinline__ float group4_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
 
 // Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk.
 //
 // Phase 1 streams the value dimension in blocks of BV columns (direct loads, the next two
 // blocks in flight while the current one is used; one workgroup barrier per block).
 // A = T^T dDelta comes from the reverse sweep, which formed it anyway and already wrote
-// dV = diag(beta) A. Per block:
-//   rowsum(A o V), <S0, dS_C>,
-//   XQ += dO S0^T,  XK += Delta dS_C^T,  Y += A S0^T,  P += dO Delta^T,  AD += A Delta^T,
-// with dO unscaled (the scale is applied afterwards). Since (I + L) Delta is exactly the
-// right factor of dT, dL = -stril(T^T dT T^T) reduces to -stril(A Delta^T) = -stril(AD),
-// and the W-path gradient of K is -diag(beta b) Y with rho = -rowsum(Y o K).
+// dV = diag(beta) A. Per block, with dO unscaled (the scale is applied afterwards):
+//   XQ^T += S0 dO^T,  Y^T += S0 A^T,  XK^T += dS_C Delta^T  (kept transposed, D x C, so that
+//   their row sums over d are sums within a lane),  P += dO Delta^T,  AD += A Delta^T,
+//   A V^T on the diagonal tiles (its diagonal is rowsum(A o V)), and S0 dS_C^T on the
+//   diagonal D tiles (its trace is <S0, dS_C>).
+// Since (I + L) Delta is exactly the right factor of dT, dL = -stril(T^T dT T^T) reduces to
+// -stril(A Delta^T) = -stril(AD), and the W-path gradient of K is -diag(beta b) Y with
+// rho = -rowsum(Y o K).
 // Per head, the rest is elementwise on the wave's tiles: PG = P o Gamma (scaled),
 // G' = -stril(AD) o Gamma, Gb = diag(beta) G', and the gate sums
 //   rowsum(P o M) = rowsum(PG o Q K^T),  colsum(P o M) = colsum(PG o Q K^T),
 //   rowsum(dL o Gamma o K K^T) = rowsum(G' o K K^T),  colsum(beta_i dL o Gamma o K K^T) = colsum(Gb o K K^T),
 // with Q K^T and K K^T formed once per key head. The products with K and Q are linear in
 // PG and Gb and dq, dk sum over the value heads, so they run once per key head on the
-// head sums: dq += (sum PG) K,  dk += (sum PG)^T Q + ((sum Gb) + (sum Gb)^T) K.
+// head sums: dq^T += K^T (sum PG)^T,  dk^T += Q^T (sum PG) + K^T ((sum Gb) + (sum Gb)^T).
 template <typename TI, int C, int D>
 __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   using OT = TI;
   using CF = GradCfg<TI, C, D>;
+  using PT = typename CF::PT;
   constexpr int NW = kWavesG, BV = CF::BV, NBH = CF::NBH, RT = CF::RT, NCB = CF::NCB;
+  constexpr int MT = PT::MT, NT = PT::NT, NTC = PT::NTC;
   constexpr int KSC = ks_of<OT, C>(), KSB = ks_of<OT, BV>(), KSD = ks_of<OT, D>();
-  constexpr int CE = 16 / (int)sizeof(OT);
+  using M = Mf<OT, KSB>;
+  using FragB = typename M::frag;
   using LD = Swz<OT, D>;
   using LC = Swz<OT, C>;
   using LB = Swz<OT, BV>;
-  using OD = Own<RT, D / 16, NW>;    // C x D products
-  using OC = Own<RT, C / 16, NW>;    // C x C products
-  using OrdD = RowOrd<OT, D>;        // storage order of the saved S^T and dS^T rows
-  using OrdC = RowOrd<OT, C>;        // storage order of the saved Delta^T and A^T rows
-  constexpr int NTD = OD::NT, NTC = OC::NT, NTB = BV / 16;
+  using LP = Swz<OT, CF::PW>;
+  using OrdD = RowOrd<OT, D>;  // storage order of the saved S^T and dS^T rows
+  using OrdC = RowOrd<OT, C>;  // storage order of the saved A^T rows
   constexpr int RS = NCB * C;  // one partial-sum slot
 
   __shared__ __align__(16) OT sK[C * D];
   __shared__ __align__(16) OT sQ[C * D];
-  __shared__ __align__(16) OT sB[CF::NBUF][CF::BUF];  // block buffers (job j uses sB[j % NBUF])
+  // block buffers (job j uses block buffer j % NBUF), then pair buffers (pair q uses q % NPBUF)
+  __shared__ __align__(16) OT smem[CF::SMEM];
+  auto sB = [&](int i) { return smem + i * CF::BUF; };
+  auto sP = [&](int i) { return smem + CF::O_P + i * CF::PBUF; };
   __shared__ __align__(16) float sgb[3][2 * C];        // gate records (head hh uses sgb[hh % 3])
   __shared__ float red[2][R_NSLOT * RS];
   __shared__ float redc[2][RT * C];  // column sums of PG o QK^T + Gb o KK^T per row tile
@@ -367,70 +401,98 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   const int w = wave_id(), lane = lane_id(), g4 = (lane >> 4) * 4, r16 = lane & 15;
 
   const int h0 = kh * p.r;
-  constexpr int NH = NW / 2;  // the two halves of the waves load different tensors of a block
+  constexpr int NH = NW / 2;  // the two halves of the waves load different tensors
+  constexpr int PB = CF::PB, PW = CF::PW;
   TileDma<BV, D, NW, OT> dmS;   // S0^T, dS^T row blocks (every wave)
-  TileDma<BV, C, NH, OT> dmB;   // Delta^T (first half) or A^T (second half) row blocks
-  TileDma<C, BV, NH, OT> dmV;   // dO (first half) or V (second half) column blocks
+  TileDma<BV, C, NH, OT> dmA;   // A^T row block (first half)
+  TileDma<C, BV, NH, OT> dmL;   // Delta block (second half)
+  TileDma<C, PW, NH, OT> dmP;   // dO (first half) or V (second half) for a pair of blocks
   TileDma<C, D, NW, OT> dmD;    // K, Q
   TileDma<1, 2 * C, NW, float> dmG;  // gate record
   const int wh = w % NH;
   dmS.init(w);
-  dmB.init(wh);
-  dmV.init(wh);
+  dmA.init(wh);
+  dmL.init(wh);
+  dmP.init(wh);
   dmD.init(w);
   dmG.init(w);
+  const int njobs = p.r * NBH, npairs = njobs / PB;
   // Job j = (head h0 + j / NBH, block j % NBH) goes into sB[j % NBUF]; the first block of a
-  // head also brings the head's gate record. A job's loads are issued in four parts spread
-  // over the step two jobs earlier, so that no wave stalls long on a full memory queue.
+  // head also brings the head's gate record. Job j's loads are issued in the step of job
+  // j - 2, in parts spread over the step (a long run of loads would stall the issuing wave).
+  // Pair q (the dO and V columns of jobs q PB .. q PB + PB - 1) goes into sP[q % NPBUF] and
+  // is issued after that step's job loads in the step of job (q - 1) PB (PB = 2) or q - 2
+  // (PB = 1). Before the first step: job 0, pair 0, job 1 (and pair 1 when PB = 1).
   auto issue_part = [&](int j, int part) {
-    const int h = h0 + j / NBH, v0 = (j % NBH) * BV;
+    const int h = h0 + j / NBH, blk = j % NBH, v0 = blk * BV;
     const size_t ch = ch_idx(p, c, h);
-    OT* b = sB[j % CF::NBUF];
+    OT* b = sB(j % CF::NBUF);
     if (part == 0) {
       dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
-      if (j % NBH == 0) dmG.issue(sgb[(j / NBH) % 3], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+      if (blk == 0) dmG.issue(sgb[(j / NBH) % 3], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
     } else if (part == 1) {
       dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
-    } else if (part == 2) {
-      if (w < NH)
-        dmB.issue(b + CF::O_DL, (const OT*)p.sv_Dt + ch * D * C + (size_t)v0 * C, C, BV, wh);
-      else
-        dmB.issue(b + CF::O_AT, (const OT*)p.ws_At + ch * D * C + (size_t)v0 * C, C, BV, wh);
     } else {
       if (w < NH)
-        dmV.issue(b + CF::O_DO, (const OT*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n, wh);
+        dmA.issue(b + CF::O_AT, (const OT*)p.ws_At + ch * D * C + (size_t)v0 * C, C, BV, wh);
       else
-        dmV.issue(b + CF::O_V, (const OT*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n, wh);
+        dmL.issue(b + CF::O_DL, (const OT*)p.sv_D + ch * C * D + (size_t)blk * C * BV, BV, n, wh);
     }
   };
-  auto issue_block = [&](int j) {
-    for (int part = 0; part < 4; ++part) issue_part(j, part);
+  auto issue_job = [&](int j) {
+    for (int part = 0; part < 3; ++part) issue_part(j, part);
   };
-  // This wave's load instructions of job j.
+  auto issue_pair = [&](int q) {
+    const int h = h0 + (q * PB) / NBH, v0 = ((q * PB) % NBH) * BV;
+    OT* b = sP(q % CF::NPBUF);
+    if (w < NH)
+      dmP.issue(b + CF::O_DO, (const OT*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n, wh);
+    else
+      dmP.issue(b + CF::O_V, (const OT*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n, wh);
+  };
+  // This wave's load instructions of job j, of a pair, and of the step of job j.
   auto job_loads = [&](int j) {
-    return 2 * dmS.count(w) + dmB.count(wh) + dmV.count(wh) + (j % NBH == 0 ? dmG.count(w) : 0);
+    return j < njobs ? 2 * dmS.count(w) + (w < NH ? dmA.count(wh) : dmL.count(wh)) + (j % NBH == 0 ? dmG.count(w) : 0) : 0;
+  };
+  const int pair_loads = dmP.count(wh);
+  auto step_loads = [&](int j) {  // issued in the step of job j: job j + 2 and, maybe, a pair
+    const int q = PB == 1 ? j + 2 : j / PB + 1;
+    return job_loads(j + 2) + ((j % PB == 0 && q < npairs) ? pair_loads : 0);
   };
   dmD.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
   dmD.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
-  issue_block(0);
-  if (1 < p.r * NBH) issue_block(1);
+  issue_job(0);
+  issue_pair(0);
+  if (1 < njobs) {
+    issue_job(1);
+    if (PB == 1) issue_pair(1);
+  }
 
-  const bool aD = OD::active(w), aC = OC::active(w);
-  const int mt = OD::m(w);  // the wave's row tile (the same in every grid)
-  const int nD = OD::n0(w), nC = OC::n0(w), cbD = OD::cb(w), cbC = OC::cb(w);
-  // rowsum(A o V) is the diagonal of A V^T: the wave holding the diagonal C x C tile of its
-  // row tile accumulates that tile of A V^T (one MFMA per block) and reads the diagonal.
-  const bool dgw = aC && nC <= mt && mt < nC + NTC;
+  const bool aD = PT::activeD(w), aC = PT::activeC(w);
+  const int rb = PT::rb(w), cb = PT::cb(w);
+  const int m0 = rb * MT, nD = cb * NT, nC = cb * NTC;  // first row tile, first D tile, first C tile
+  // The wave's diagonal C x C tile (row tile m0 + dmi = column tile nC + dyc), if it has one.
+  int dmi = -1;
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int yc = 0; yc < NTC; ++yc)
+      if (m0 + mi == nC + yc) dmi = mi;
+  const bool dgw = aC && dmi >= 0;
   constexpr int FIN = NW - 1;  // the wave that finishes each head's per-row gate gradients
 
-  f32x4 dqf[NTD], dkf[NTD];  // dq, dk of the key head, summed over its value heads in order
-#pragma unroll
-  for (int y = 0; y < NTD; ++y) dqf[y] = dkf[y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 QKt[NTC], KKt[NTC], PGs[NTC], Gbs[NTC];  // Q K^T, K K^T, sum PG, sum Gb on the C x C tiles
-#pragma unroll
-  for (int y = 0; y < NTC; ++y) QKt[y] = KKt[y] = PGs[y] = Gbs[y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // dq^T, dk^T of the key head on the wave's D x C tiles [y][mi], summed over its value
+  // heads in order: lane (g, r) element e holds row i = 16 (m0 + mi) + r, column
+  // d = 16 (nD + y) + 4 g + e.
+  f32x4 dqt[NT][MT], dkt[NT][MT];
+  zero(dqt);
+  zero(dkt);
+  f32x4 QKt[MT][NTC], KKt[MT][NTC], PGs[MT][NTC], Gbs[MT][NTC];  // Q K^T, K K^T, sum PG, sum Gb
+  zero(QKt);
+  zero(KKt);
+  zero(PGs);
+  zero(Gbs);
 
-  const int njobs = p.r * NBH;
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = h0 + hh, par = hh & 1;
     const float* gam = sgb[hh % 3];  // log2 units
@@ -441,164 +503,187 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     for (int i = threadIdx.x; i < RT * C; i += kThreadsG) redch[i] = 0.f;
 
     // ---- phase 1: stream the value dimension
-    f32x4 XQ[NTD], XK[NTD], Y[NTD], P[NTC], AD[NTC], AV[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
-#pragma unroll
-    for (int y = 0; y < NTD; ++y) XQ[y] = XK[y] = Y[y] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int y = 0; y < NTC; ++y) P[y] = AD[y] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float sdot = 0.f;
+    f32x4 XQt[NT][MT], XKt[NT][MT], Yt[NT][MT], P[MT][NTC], AD[MT][NTC];
+    f32x4 AV = {0.f, 0.f, 0.f, 0.f}, SD = {0.f, 0.f, 0.f, 0.f};
+    zero(XQt);
+    zero(XKt);
+    zero(Yt);
+    zero(P);
+    zero(AD);
     for (int b = 0; b < NBH; ++b) {
       const int j = hh * NBH + b;
-      const OT* cur = sB[j % CF::NBUF];
-      dma_wait_keep(j + 1 < njobs ? job_loads(j + 1) : 0);  // job j's loads (and all before) are done
+      const OT* cur = sB(j % CF::NBUF);
+      const OT* curp = sP((j / PB) % CF::NPBUF);
+      const int sp = (j % PB) * (BV / KSB);  // this block's first contraction step within the pair
+      // Job j and its pair are done once at most the loads issued after them are outstanding:
+      // job 1 before the first step, else the previous step's loads.
+      dma_wait_keep(j == 0 ? job_loads(1) + (PB == 1 && 1 < npairs ? pair_loads : 0) : step_loads(j - 1));
       lds_barrier();  // job j (and K, Q, gates with it) is in LDS; every wave is done with job j - 1
-      const bool nxt2 = j + 2 < njobs;
-      if (nxt2) issue_part(j + 2, 0);
+      const bool nxt2 = j + 2 < njobs;  // every wave issues every part (the wait counts rely on it)
+      if (nxt2) {
+        issue_part(j + 2, 0);
+        issue_part(j + 2, 1);
+      }
       if (j == 0 && aC) {  // Q K^T and K K^T of the key head on this wave's C x C tiles
-        f32x4 G2[2][NTC];
+        f32x4 G2[2 * MT][NTC];
+        zero(G2);
+        wave_mm<OT, D, 2 * MT, NTC>(
+            G2, [&](int m, int s) { return ld_n<OT, KSD, STD, LD>(m < MT ? sQ : sK, 16 * (m0 + m % MT), s); },
+            [&](int yc, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * (nC + yc), s); });
 #pragma unroll
-        for (int y = 0; y < NTC; ++y) G2[0][y] = G2[1][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-        wave_mm<OT, D, 2, NTC>(G2, [&](int m, int s) { return ld_n<OT, KSD, STD, LD>(m == 0 ? sQ : sK, 16 * mt, s); },
-                               [&](int y, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * (nC + y), s); });
+        for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-        for (int y = 0; y < NTC; ++y) {
-          QKt[y] = G2[0][y];
-          KKt[y] = G2[1][y];
-        }
+          for (int yc = 0; yc < NTC; ++yc) {
+            QKt[mi][yc] = G2[mi][yc];
+            KKt[mi][yc] = G2[MT + mi][yc];
+          }
       }
       const OT* sS0 = cur + CF::O_S0;
       const OT* sDS = cur + CF::O_DS;
-      const OT* sDL = cur + CF::O_DL;
       const OT* sAt = cur + CF::O_AT;
-      const OT* sDO = cur + CF::O_DO;
-      const OT* sV = cur + CF::O_V;
-      {
-        using V = Vec16<OT>;
-        for (int idx = threadIdx.x; idx < D * BV / V::N; idx += kThreadsG) {  // same layout: index-wise product
-          const typename V::type a = reinterpret_cast<const typename V::type*>(sS0)[idx];
-          const typename V::type d = reinterpret_cast<const typename V::type*>(sDS)[idx];
+      const OT* sDL = cur + CF::O_DL;
+      const OT* sDO = curp + CF::O_DO;
+      const OT* sV = curp + CF::O_V;
 #pragma unroll
-          for (int e = 0; e < V::N; ++e) sdot += (float)a[e] * (float)d[e];
+      for (int s = 0; s < BV / KSB; ++s) {
+        FragB fo[MT], fa[MT];  // dO and A rows of the wave's row tiles (A operands)
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+          fo[mi] = ld_n<OT, KSB, STD, LP>(sDO, 16 * (m0 + mi), sp + s);
+          fa[mi] = ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * (m0 + mi), s);
+        }
+        if (aD) {
+          FragB fs[NT], fds[NT], fd[MT];
+#pragma unroll
+          for (int y = 0; y < NT; ++y) {
+            fs[y] = ld_t<OT, KSB, STD, LD, OrdD>(sS0, 16 * (nD + y), s);
+            fds[y] = ld_t<OT, KSB, STD, LD, OrdD>(sDS, 16 * (nD + y), s);
+          }
+#pragma unroll
+          for (int mi = 0; mi < MT; ++mi) fd[mi] = ld_n<OT, KSB, STD, LB>(sDL, 16 * (m0 + mi), s);
+#pragma unroll
+          for (int y = 0; y < NT; ++y)
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+              XQt[y][mi] = M::run(fs[y], fo[mi], XQt[y][mi]);
+              Yt[y][mi] = M::run(fs[y], fa[mi], Yt[y][mi]);
+              XKt[y][mi] = M::run(fds[y], fd[mi], XKt[y][mi]);
+            }
+          if (rb == 0)  // S0 dS_C^T on the diagonal D tiles (the waves of row block 0 cover every d)
+#pragma unroll
+            for (int y = 0; y < NT; ++y) SD = M::run(fs[y], fds[y], SD);
+        }
+        if (s == 0) {
+          if (nxt2) issue_part(j + 2, 2);
+          const int q = PB == 1 ? j + 2 : j / PB + 1;
+          if (j % PB == 0 && q < npairs) issue_pair(q);
+        }
+        if (aC) {
+          FragB fb[NTC];  // Delta rows of the wave's C tiles (B operands over v)
+#pragma unroll
+          for (int yc = 0; yc < NTC; ++yc) fb[yc] = ld_n<OT, KSB, STD, LB>(sDL, 16 * (nC + yc), s);
+#pragma unroll
+          for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int yc = 0; yc < NTC; ++yc) {
+              P[mi][yc] = M::run(fo[mi], fb[yc], P[mi][yc]);
+              AD[mi][yc] = M::run(fa[mi], fb[yc], AD[mi][yc]);
+            }
+          if (dgw) {  // A V^T on the diagonal tile
+            FragB fad = fa[0];
+#pragma unroll
+            for (int mi = 1; mi < MT; ++mi)
+              if (dmi == mi) fad = fa[mi];
+            AV = M::run(fad, ld_n<OT, KSB, STD, LP>(sV, 16 * (m0 + dmi), sp + s), AV);
+          }
         }
       }
-      if (nxt2) issue_part(j + 2, 1);  // every wave issues every part (the wait counts rely on it)
-      if (aD) {
-        f32x4 XY[2][NTD];  // dO S0^T and A S0^T share the S0 fragments
-#pragma unroll
-        for (int y = 0; y < NTD; ++y) {
-          XY[0][y] = XQ[y];
-          XY[1][y] = Y[y];
-        }
-        wave_mm<OT, BV, 2, NTD>(XY,
-                                [&](int m, int s) {
-                                  return m == 0 ? ld_n<OT, KSB, STD, LB>(sDO, 16 * mt, s)
-                                                : ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * mt, s);
-                                },
-                                [&](int y, int s) { return ld_t<OT, KSB, STD, LD, OrdD>(sS0, 16 * (nD + y), s); });
-        f32x4 XKa[1][NTD];
-#pragma unroll
-        for (int y = 0; y < NTD; ++y) XKa[0][y] = XK[y];
-        wave_mm<OT, BV, 1, NTD>(XKa, [&](int, int s) { return ld_t<OT, KSB, STD, LC, OrdC>(sDL, 16 * mt, s); },
-                                [&](int y, int s) { return ld_t<OT, KSB, STD, LD, OrdD>(sDS, 16 * (nD + y), s); });
-#pragma unroll
-        for (int y = 0; y < NTD; ++y) {
-          XQ[y] = XY[0][y];
-          Y[y] = XY[1][y];
-          XK[y] = XKa[0][y];
-        }
-      }
-      if (nxt2) issue_part(j + 2, 2);
-      if (aC) {
-        f32x4 PA[2][NTC];  // dO Delta^T and A Delta^T share the Delta fragments
-#pragma unroll
-        for (int y = 0; y < NTC; ++y) {
-          PA[0][y] = P[y];
-          PA[1][y] = AD[y];
-        }
-        wave_mm<OT, BV, 2, NTC>(PA,
-                                [&](int m, int s) {
-                                  return m == 0 ? ld_n<OT, KSB, STD, LB>(sDO, 16 * mt, s)
-                                                : ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * mt, s);
-                                },
-                                [&](int y, int s) { return ld_t<OT, KSB, STD, LC, OrdC>(sDL, 16 * (nC + y), s); });
-#pragma unroll
-        for (int y = 0; y < NTC; ++y) {
-          P[y] = PA[0][y];
-          AD[y] = PA[1][y];
-        }
-      }
-      if (nxt2) issue_part(j + 2, 3);
-      if (dgw)  // A V^T on the diagonal tile of row tile mt
-        wave_mm<OT, BV, 1, 1>(AV, [&](int, int s) { return ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * mt, s); },
-                              [&](int, int s) { return ld_n<OT, KSB, STD, LB>(sV, 16 * mt, s); });
     }
 
     // ---- phase 2 of the head: elementwise on the wave's tiles
     const float sc = p.scale, gn = gam[C - 1];
-    float bx[4], ex[4], bb[4];
+    float bb[MT][4];  // beta of the rows 16 (m0 + mi) + 4 g + e of the C x C tiles
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * mt + g4 + e;
-      bx[e] = __builtin_amdgcn_exp2f(gam[i]);
-      ex[e] = __builtin_amdgcn_exp2f(gn - gam[i]);
-      bb[e] = bet[i];
-    }
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bb[mi][e] = bet[16 * (m0 + mi) + g4 + e];
     if (dgw) {  // lane (g, r) holds (A V^T)[4 g + e][r]: the diagonal is e = r - 4 g
       const int e = r16 - g4;
-      if (e >= 0 && e < 4) redh[R_DB1 * RS + 16 * mt + r16] = AV[0][0][e];
+      if (e >= 0 && e < 4) redh[R_DB1 * RS + 16 * (m0 + dmi) + r16] = pick4(AV, e);
     }
     if (aC) {
-      float grow[4] = {0.f, 0.f, 0.f, 0.f}, db3[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int y = 0; y < NTC; ++y) {
-        float col = 0.f;
-        const int jj = 16 * (nC + y) + r16;
+      for (int mi = 0; mi < MT; ++mi) {
+        float grow[4] = {0.f, 0.f, 0.f, 0.f}, db3[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int yc = 0; yc < NTC; ++yc) {
+          float col = 0.f;
+          const int jj = 16 * (nC + yc) + r16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * (m0 + mi) + g4 + e;
+            const float gd = __builtin_amdgcn_exp2f(gam[i] - gam[jj]);
+            const float pg = i >= jj ? sc * P[mi][yc][e] * gd : 0.f;
+            const float gp = i > jj ? -AD[mi][yc][e] * gd : 0.f;
+            const float gb = bb[mi][e] * gp;
+            PGs[mi][yc][e] += pg;
+            Gbs[mi][yc][e] += gb;
+            grow[e] += pg * QKt[mi][yc][e];
+            db3[e] += gp * KKt[mi][yc][e];
+            col += pg * QKt[mi][yc][e] + gb * KKt[mi][yc][e];
+          }
+          col += __shfl_xor(col, 16);
+          col += __shfl_xor(col, 32);
+          if (lane < 16) redch[(m0 + mi) * C + jj] = col;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 16 * mt + g4 + e;
-          const float gd = __builtin_amdgcn_exp2f(gam[i] - gam[jj]);
-          const float pg = i >= jj ? sc * P[y][e] * gd : 0.f;
-          const float gp = i > jj ? -AD[y][e] * gd : 0.f;
-          const float gb = bb[e] * gp;
-          PGs[y][e] += pg;
-          Gbs[y][e] += gb;
-          grow[e] += pg * QKt[y][e];
-          db3[e] += gp * KKt[y][e];
-          col += pg * QKt[y][e] + gb * KKt[y][e];
+          grow[e] = row16_sum(grow[e]);
+          db3[e] = row16_sum(db3[e]);
         }
-        col += __shfl_xor(col, 16);
-        col += __shfl_xor(col, 32);
-        if (lane < 16) redch[mt * C + jj] = col;
-      }
+        if (r16 == 0)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        grow[e] = row16_sum(grow[e]);
-        db3[e] = row16_sum(db3[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * (m0 + mi) + g4 + e;
+            redh[R_GROW * RS + cb * C + i] = grow[e];
+            redh[R_DB3 * RS + cb * C + i] = db3[e];
+          }
       }
-      if (r16 == 0)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          redh[R_GROW * RS + cbC * C + 16 * mt + g4 + e] = grow[e];
-          redh[R_DB3 * RS + cbC * C + 16 * mt + g4 + e] = db3[e];
-        }
     }
     if (aD) {
-      f32x4 Kc[NTD], Qc[NTD];  // K and Q at this wave's accumulator positions
 #pragma unroll
-      for (int y = 0; y < NTD; ++y) {
-        Kc[y] = ld_col4<OT, LD>(sK, 16 * mt + g4, 16 * (nD + y));
-        Qc[y] = ld_col4<OT, LD>(sQ, 16 * mt + g4, 16 * (nD + y));
-      }
-      acc_rowsum<NTD>(XK, mt, [&](int y, int e, float x) { return ex[e] * x * Kc[y][e]; }, redh + R_EBAR * RS + cbD * C);
-      acc_rowsum<NTD>(XQ, mt, [&](int y, int e, float x) { return sc * x * Qc[y][e]; }, redh + R_RQ * RS + cbD * C);
-      acc_rowsum<NTD>(Y, mt, [&](int y, int e, float x) { return -x * Kc[y][e]; }, redh + R_RHO * RS + cbD * C);
+      for (int mi = 0; mi < MT; ++mi) {
+        const int i = 16 * (m0 + mi) + r16;  // this lane's row of the chunk
+        const float gi = gam[i];
+        const float exi = __builtin_amdgcn_exp2f(gn - gi), bxi = __builtin_amdgcn_exp2f(gi), bbi = bet[i];
+        float pe = 0.f, pq = 0.f, pr = 0.f;  // partial row sums over this lane's d
 #pragma unroll
-      for (int y = 0; y < NTD; ++y)
+        for (int y = 0; y < NT; ++y) {
+          const f32x4 kv = ld_row4<OT, LD>(sK, i, 16 * (nD + y) + g4);
+          const f32x4 qv = ld_row4<OT, LD>(sQ, i, 16 * (nD + y) + g4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dkf[y][e] += ex[e] * XK[y][e] - bb[e] * bx[e] * Y[y][e];
-          dqf[y][e] += sc * bx[e] * XQ[y][e];
+          for (int e = 0; e < 4; ++e) {
+            pe += XKt[y][mi][e] * kv[e];
+            pq += XQt[y][mi][e] * qv[e];
+            pr += Yt[y][mi][e] * kv[e];
+            dkt[y][mi][e] += exi * XKt[y][mi][e] - bbi * bxi * Yt[y][mi][e];
+            dqt[y][mi][e] += sc * bxi * XQt[y][mi][e];
+          }
         }
+        pe = group4_sum(pe);
+        pq = group4_sum(pq);
+        pr = group4_sum(pr);
+        if (lane < 16) {
+          redh[R_EBAR * RS + cb * C + i] = exi * pe;
+          redh[R_RQ * RS + cb * C + i] = sc * pq;
+          redh[R_RHO * RS + cb * C + i] = -pr;
+        }
+      }
+    }
+    float sdot = 0.f;  // the trace of SD
+    {
+      const int e = r16 - g4;
+      if (e >= 0 && e < 4) sdot = pick4(SD, e);
     }
     sdot = wave_sum(sdot);
     if (lane == 0) swv[par][w] = sdot;
@@ -611,10 +696,12 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       for (int sl = 0; sl < R_NSLOT; ++sl) {
         float a = 0.f;
         if (ok)
-          for (int b = 0; b < NCB; ++b) a += redh[sl * RS + b * C + i];
+#pragma unroll
+          for (int q = 0; q < NCB; ++q) a += redh[sl * RS + q * C + i];
         rv[sl] = a;
       }
       if (ok)
+#pragma unroll
         for (int m = 0; m < RT; ++m) gcol += redch[m * C + i];
       const float bi = ok ? __builtin_amdgcn_exp2f(gam[i]) : 0.f, be = ok ? bet[i] : 0.f;
       float dgam = 0.f;
@@ -622,6 +709,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const float ebsum = wave_sum(rv[R_EBAR]);
       if (i == n - 1) {
         float st = 0.f;
+#pragma unroll
         for (int k = 0; k < NW; ++k) st += swv[par][k];
         dgam += __builtin_amdgcn_exp2f(gn) * st + ebsum;
       }
@@ -636,51 +724,43 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   }
 
   // ---- the key head's products with K and Q on the head sums
-  OT* const sPGs = sB[0];         // sum PG    [C][C]
-  OT* const sGbs = sB[0] + C * C;  // sum Gb   [C][C]
+  OT* const sPGs = smem;          // sum PG    [C][C]
+  OT* const sGbs = smem + C * C;  // sum Gb    [C][C]
   if (aC) {
 #pragma unroll
-    for (int y = 0; y < NTC; ++y)
+    for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * mt + g4 + e, jj = 16 * (nC + y) + r16;
-        sPGs[LC::at(i, jj)] = (OT)PGs[y][e];
-        sGbs[LC::at(i, jj)] = (OT)Gbs[y][e];
-      }
+      for (int yc = 0; yc < NTC; ++yc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * (m0 + mi) + g4 + e, jj = 16 * (nC + yc) + r16;
+          sPGs[LC::at(i, jj)] = (OT)PGs[mi][yc][e];
+          sGbs[LC::at(i, jj)] = (OT)Gbs[mi][yc][e];
+        }
   }
   lds_barrier();
   if (aD) {
-    auto fK = [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sK, 16 * (nD + y), s); };
-    {  // dq += (sum PG) K
-      f32x4 Z[1][NTD];
-      zero(Z);
-      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sPGs, 16 * mt, s); }, fK);
-#pragma unroll
-      for (int y = 0; y < NTD; ++y) dqf[y] += Z[0][y];
-    }
-    {  // dk += (sum PG)^T Q + (sum Gb)^T K + (sum Gb) K
-      f32x4 Z[1][NTD];
-      zero(Z);
-      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sPGs, 16 * mt, s); },
-                             [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sQ, 16 * (nD + y), s); });
-      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_t<OT, KSC, STD, LC>(sGbs, 16 * mt, s); }, fK);
-      wave_mm<OT, C, 1, NTD>(Z, [&](int, int s) { return ld_n<OT, KSC, STD, LC>(sGbs, 16 * mt, s); }, fK);
-#pragma unroll
-      for (int y = 0; y < NTD; ++y) dkf[y] += Z[0][y];
-    }
+    auto fK = [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sK, 16 * (nD + y), s); };  // K^T rows d
+    // dq^T += K^T (sum PG)^T
+    wave_mm<OT, C, NT, MT>(dqt, fK, [&](int mi, int s) { return ld_n<OT, KSC, STD, LC>(sPGs, 16 * (m0 + mi), s); });
+    // dk^T += Q^T (sum PG) + K^T (sum Gb) + K^T (sum Gb)^T
+    wave_mm<OT, C, NT, MT>(dkt, [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sQ, 16 * (nD + y), s); },
+                           [&](int mi, int s) { return ld_t<OT, KSC, STD, LC>(sPGs, 16 * (m0 + mi), s); });
+    wave_mm<OT, C, NT, MT>(dkt, fK, [&](int mi, int s) { return ld_t<OT, KSC, STD, LC>(sGbs, 16 * (m0 + mi), s); });
+    wave_mm<OT, C, NT, MT>(dkt, fK, [&](int mi, int s) { return ld_n<OT, KSC, STD, LC>(sGbs, 16 * (m0 + mi), s); });
   }
   lds_barrier();
-  // dq, dk of the key head: rows through LDS (the first block buffer), 16-byte stores
+  // dq, dk of the key head: rows through LDS, 16-byte stores
   {
-    TI* st = (TI*)sB[0];
+    TI* st = (TI*)smem;
     if (aD) {
 #pragma unroll
-      for (int y = 0; y < NTD; ++y)
+      for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * mt + g4 + e, d = 16 * (nD + y) + r16;
-          st[i * D + d] = (TI)dqf[y][e];
-          st[(C + i) * D + d] = (TI)dkf[y][e];
+        for (int y = 0; y < NT; ++y) {
+          const int i = 16 * (m0 + mi) + r16, d = 16 * (nD + y) + g4;
+          store4b(st + i * D + d, dqt[y][mi]);
+          store4b(st + (C + i) * D + d, dkt[y][mi]);
         }
     }
     lds_barrier();

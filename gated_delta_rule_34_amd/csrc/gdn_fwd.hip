@@ -356,12 +356,21 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     zero(Dl);
     wave_mm_cm<OT, C, RT, CT>(Dl, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sT, 16 * m, s); },
                               [&](int j, int s) { return from_acc<OT, KSC>(X[j], s, Ident{}); });
-    FragC Db[CT][NSC];  // Delta's fragments: B operand of M Delta and the saved copy
+    FragC Db[CT][NSC];  // Delta's fragments: B operand of M Delta
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int s = 0; s < NSC; ++s) Db[ct][s] = from_acc<OT, KSC>(Dl[ct], s, Ident{});
-    save_rows<OT, C, CT, RT, NSC>((OT*)p.sv_Dt + ch * D * C, v0, Dl, Db);  // Delta^T[v][i]
+    {  // Delta's columns of this wave replace the wave's own (consumed) columns of V in LDS;
+       // the full rows are written out with the output rows
+      OT* sDw = sbuf[buf] + CF::O_V;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sDw[LD::at(16 * t + g4 + e, v0 + 16 * ct + r16)] = (OT)Dl[ct][t][e];
+    }
     {  // O = b o Q S + M Delta, staged as rows for the whole workgroup
       f32x4 O[RT][CT];
       zero(O);
@@ -383,17 +392,23 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
 #pragma unroll
           for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)(sc * O[t][ct][e]);
     }
-    lds_barrier();  // the chunk's output rows are staged
-    {  // full output rows, 16-byte stores spread over every wave
+    lds_barrier();  // the chunk's output rows and Delta rows are staged
+    {  // full output and Delta rows, 16-byte stores spread over every wave
       using V = Vec16<OT>;
       constexpr int VPR = D / CE;
       TI* o = (TI*)p.o + t0 * p.o_rs + h * D;
+      OT* dl = (OT*)p.sv_D + ch * C * D;
+      constexpr int BV = grad_block<OT, D>();  // Delta goes out in blocks of BV columns
+      const OT* sD = sbuf[buf] + CF::O_V;
 #pragma unroll
       for (int idx = threadIdx.x; idx < C * VPR; idx += NW * 64) {
         const int i = idx / VPR, q = idx % VPR;
-        if (i < len)
+        if (i < len) {
           *reinterpret_cast<typename V::type*>(o + (int64_t)i * p.o_rs + q * CE) =
               *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
+          *reinterpret_cast<typename V::type*>(dl + (q * CE / BV) * C * BV + i * BV + (q * CE) % BV) =
+              *reinterpret_cast<const typename V::type*>(sD + LD::at(i, q * CE));
+        }
       }
     }
     // S <- b_n S + K^T (e o Delta)

@@ -47,7 +47,8 @@ struct Prob {
   // Saved activations written by the forward for the backward, per chunk c and value
   // head h (element type = the problem's storage type OT unless noted):
   void* sv_S;    // [c][h][D][D]  state at the start of the chunk, transposed: S^T[v][d]
-  void* sv_Dt;   // [c][h][D][C]  Delta^T[v][i]
+  void* sv_D;    // [c][h][D / BV][C][BV]  Delta in blocks of BV = grad_block<OT, D>() value
+                 // columns, each block row-major (rows past the end of a chunk not written)
   void* sv_T;    // [c][h][C][C]  T = (I + L)^-1, row-major
   void* sv_M;    // [c][h][C][C]  M = Gamma o Q K^T (lower incl. diagonal), row-major
   float* sv_gb;  // [c][h][2][C]  float32: gamma (cumulative log g), beta (0 past the end)
@@ -55,6 +56,10 @@ struct Prob {
   void* ws_dS;   // [c][h][D][D]  state adjoint flowing into the end of the chunk, dS^T[v][d]
   void* ws_At;   // [c][h][D][C]  A^T[v][i], A = T^T dDelta
 };
+
+// Value columns per block of the gradient kernel's value loop (also the block width of the
+// saved Delta, so that each block is one contiguous run of memory).
+template <typename T, int D> constexpr int grad_block() { return sizeof(T) == 2 ? (D >= 32 ? 32 : D) : 16; }
 
 // Benchmark tracing (gdn_trace.cpp): runs launch(ctx), bracketed by HIP events on s
 // while tracing is enabled.
