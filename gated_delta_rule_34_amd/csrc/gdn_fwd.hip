@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   constexpr int KQ_BYTES = 2 * C * D * (int)sizeof(OT);
   constexpr int INV_BYTES = (2 * C * LCF + 3 * 320) * 4 + C * C * (int)sizeof(OT);
   __shared__ __align__(16) char smem[KQ_BYTES > INV_BYTES ? KQ_BYTES : INV_BYTES];
-  __shared__ float sg[C], sbeta[C];
+  constexpr int GH = NW;  // gate records formed per pass: one wave per value head
+  __shared__ float sg[GH][C], sbeta[GH][C];
   OT* const sK = reinterpret_cast<OT*>(smem);
   OT* const sQ = sK + C * D;
   float* const sL = reinterpret_cast<float*>(smem);
@@ -125,6 +126,27 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
     dm.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
     dm.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
   }
+  // Gate records of value heads hb .. hb + GH - 1, one per wave (lane = row): gamma (log2
+  // units) is the inclusive scan of log2 g, beta is 0 past the end.
+  auto gates = [&](int hb) {
+    const int hh = hb + w;
+    if (hh < p.r) {
+      const int h = kh * p.r + hh;
+      const size_t ch = ch_idx(p, c, h);
+      const int i = l;
+      const bool ok = i < n && i < C;
+      const float lg = ok ? __builtin_amdgcn_logf(p.g[(int64_t)(ci.t0 + i) * p.Hv + h]) : 0.f;  // log2 g
+      const float be = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
+      const float gam = wave_scan_incl(i < C ? lg : 0.f);
+      if (i < C) {
+        sg[w][i] = gam;
+        sbeta[w][i] = be;
+        p.sv_gb[ch * 2 * C + i] = gam;
+        p.sv_gb[ch * 2 * C + C + i] = be;
+      }
+    }
+  };
+  gates(0);  // while K and Q arrive
   dma_wait();
   lds_barrier();
   // K K^T and Q K^T: wave w < C / 16 owns row tile w and every column tile.
@@ -141,28 +163,20 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = kh * p.r + hh;
     const size_t ch = ch_idx(p, c, h);
-    if (threadIdx.x < 64) {
-      const int i = threadIdx.x;
-      const bool ok = i < n && i < C;
-      const float lg = ok ? __builtin_amdgcn_logf(p.g[(int64_t)(ci.t0 + i) * p.Hv + h]) : 0.f;  // log2 g
-      const float be = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
-      const float gam = wave_scan_incl(i < C ? lg : 0.f);
-      if (i < C) {
-        sg[i] = gam;
-        sbeta[i] = be;
-        p.sv_gb[ch * 2 * C + i] = gam;
-        p.sv_gb[ch * 2 * C + C + i] = be;
-      }
+    if (hh > 0 && hh % GH == 0) {  // the next group of gate records (the last head's barrier freed sg)
+      gates(hh);
+      lds_barrier();
     }
-    lds_barrier();
+    const float* sgh = sg[hh % GH];
+    const float* sbh = sbeta[hh % GH];
     if (rw) {
 #pragma unroll
       for (int j = 0; j < RT; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * w + g4 + e, jj = 16 * j + r16;
-          const float gd = __builtin_amdgcn_exp2f(sg[i] - sg[jj]);
-          sL[i * LCF + jj] = i > jj ? sbeta[i] * gd * KK[0][j][e] : 0.f;
+          const float gd = __builtin_amdgcn_exp2f(sgh[i] - sgh[jj]);
+          sL[i * LCF + jj] = i > jj ? sbh[i] * gd * KK[0][j][e] : 0.f;
           sM[i * C + jj] = (OT)(i >= jj && i < n ? gd * QK[0][j][e] : 0.f);
         }
     }
