@@ -393,6 +393,11 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   __shared__ float red[2][R_NSLOT * RS];
   __shared__ float redc[2][RT * C];  // column sums of PG o QK^T + Gb o KK^T per row tile
   __shared__ float swv[2][NW];
+  // dbeta and dg of up to GRM value heads, written at the end as the key head's r columns
+  // of each row (the rows of dg and dbeta are tokens: one head's column alone is a strided
+  // run of single floats)
+  constexpr int GRM = 4;
+  __shared__ float sgo[2][GRM][C];
 
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
@@ -715,10 +720,17 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       }
       const float dlg = wave_rscan_incl(dgam);
       if (i < n) {
-        const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
-        p.dbeta[row] = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
+        const float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
         // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
-        p.dg[row] = dlg * __builtin_amdgcn_exp2f((i > 0 ? gam[i - 1] : 0.f) - gam[i]);
+        const float dgv = dlg * __builtin_amdgcn_exp2f((i > 0 ? gam[i - 1] : 0.f) - gam[i]);
+        if (p.r <= GRM) {
+          sgo[0][hh][i] = db;
+          sgo[1][hh][i] = dgv;
+        } else {
+          const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
+          p.dbeta[row] = db;
+          p.dg[row] = dgv;
+        }
       }
     }
   }
@@ -774,6 +786,14 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       if (i < n) {
         TI* dst = r < C ? dq + (int64_t)i * p.dq_rs + cc : dk + (int64_t)i * p.dk_rs + cc;
         *reinterpret_cast<typename V::type*>(dst) = *reinterpret_cast<const typename V::type*>(st + r * D + cc);
+      }
+    }
+    if (p.r <= GRM) {  // dbeta, dg: row i, heads h0 .. h0 + r - 1
+      const int nr = n * p.r;
+      for (int idx = threadIdx.x; idx < 2 * nr; idx += kThreadsG) {
+        const int a = idx >= nr, q = idx - a * nr, i = q / p.r, hh = q - i * p.r;
+        float* dst = a ? p.dg : p.dbeta;
+        dst[(int64_t)(ci.t0 + i) * p.Hv + h0 + hh] = sgo[a][hh][i];
       }
     }
   }
