@@ -694,35 +694,43 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     if (lane == 0) swv[par][w] = sdot;
     lds_barrier();  // the head's partial sums are complete
     if (w == FIN) {  // per-row gate gradients of head h (the other waves move on)
-      const int i = lane;
-      const bool ok = i < C;
+      const bool ok = lane < C;
+      const int i = ok ? lane : C - 1;  // lanes past C read a valid row and contribute nothing
+      // every partial sum first (independent reads), then the sums in a fixed order
+      float part[R_NSLOT][NCB], pc[RT];
+#pragma unroll
+      for (int sl = 0; sl < R_NSLOT; ++sl)
+#pragma unroll
+        for (int q = 0; q < NCB; ++q) part[sl][q] = redh[sl * RS + q * C + i];
+#pragma unroll
+      for (int m = 0; m < RT; ++m) pc[m] = redch[m * C + i];
+      const float gi = gam[i], gprev = i > 0 ? gam[i - 1] : 0.f, bei = bet[i];
       float rv[R_NSLOT], gcol = 0.f;
 #pragma unroll
       for (int sl = 0; sl < R_NSLOT; ++sl) {
         float a = 0.f;
-        if (ok)
 #pragma unroll
-          for (int q = 0; q < NCB; ++q) a += redh[sl * RS + q * C + i];
-        rv[sl] = a;
+        for (int q = 0; q < NCB; ++q) a += part[sl][q];
+        rv[sl] = ok ? a : 0.f;
       }
-      if (ok)
 #pragma unroll
-        for (int m = 0; m < RT; ++m) gcol += redch[m * C + i];
-      const float bi = ok ? __builtin_amdgcn_exp2f(gam[i]) : 0.f, be = ok ? bet[i] : 0.f;
+      for (int m = 0; m < RT; ++m) gcol += pc[m];
+      if (!ok) gcol = 0.f;
+      const float bi = ok ? __builtin_amdgcn_exp2f(gi) : 0.f, be = ok ? bei : 0.f;
       float dgam = 0.f;
       if (ok) dgam = bi * rv[R_RQ] + be * bi * rv[R_RHO] - rv[R_EBAR] + rv[R_GROW] + be * rv[R_DB3] - gcol;
       const float ebsum = wave_sum(rv[R_EBAR]);
-      if (i == n - 1) {
+      if (lane == n - 1) {
         float st = 0.f;
 #pragma unroll
         for (int k = 0; k < NW; ++k) st += swv[par][k];
         dgam += __builtin_amdgcn_exp2f(gn) * st + ebsum;
       }
       const float dlg = wave_rscan_incl(dgam);
-      if (i < n) {
+      if (lane < n) {  // (lane < n implies lane < C: i is the lane)
         const float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
         // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
-        const float dgv = dlg * __builtin_amdgcn_exp2f((i > 0 ? gam[i - 1] : 0.f) - gam[i]);
+        const float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
         if (p.r <= GRM) {
           sgo[0][hh][i] = db;
           sgo[1][hh][i] = dgv;
