@@ -37,19 +37,18 @@ template <typename OT> __device__ __forceinline__ void store4(OT* dst, f32x4 x) 
     *reinterpret_cast<f32x4*>(dst) = x;
 }
 
-// T := (I + L)^-1 for strictly lower triangular L (float32 LDS, row stride LC).
-// Diagonal 16 x 16 blocks by forward substitution, one column per lane, then the
-// off-diagonal blocks level by level: T_ij = -T_ii sum_{k=j}^{i-1} L_ik T_kj, with
-// float32 MFMA. X is scratch for 3 tiles of 16 x 20 floats. Ends with a barrier.
+// T := (I + L)^-1 for strictly lower triangular L (float32 LDS, row stride LC), lower
+// blocks only: the 16 x 16 blocks above the diagonal are zero and are never written (the
+// caller stores zeros for them). Diagonal blocks by forward substitution, one column per
+// lane, then the blocks below the diagonal level by level,
+// T_ij = -T_ii (sum_{k=j}^{i-1} L_ik T_kj), with float32 MFMA: the sum stays in the
+// accumulator and is the B operand of the product with T_ii (ACC order), so each level
+// costs one barrier. Ends with a barrier.
 template <int C, int LC, int NWV>
-__device__ __forceinline__ void invert_unit_lower(const float* L, float* T, float* X) {
+__device__ __forceinline__ void invert_unit_lower(const float* L, float* T) {
   constexpr int NB = C / 16;
   static_assert(NWV >= NB, "one wave per diagonal block");
-  const int w = threadIdx.x / 64, l = threadIdx.x & 63;
-  for (int idx = threadIdx.x; idx < C * C; idx += NWV * 64) {
-    const int i = idx / C, j = idx % C;
-    if (i / 16 < j / 16) T[i * LC + j] = 0.f;  // upper off-diagonal blocks
-  }
+  const int w = threadIdx.x / 64, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
   if (w < NB && l < 16) {
     const int o = w * 16, j = l;
     float t[16];
@@ -65,31 +64,24 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T, floa
   }
   lds_barrier();
   for (int d = 1; d < NB; ++d) {
-    const int npairs = NB - d;
-    const int bi = w + d, bj = w;  // wave w < npairs owns block (w + d, w)
-    if (w < npairs) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int bi = w + d, bj = w;  // wave w < NB - d owns block (w + d, w)
+    if (w < NB - d) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};  // X = sum_k L_{bi,k} T_{k,bj}
       for (int kb = bj; kb < bi; ++kb)
 #pragma unroll
         for (int k0 = 0; k0 < 16; k0 += 4) {
-          const float a = L[(bi * 16 + (l & 15)) * LC + kb * 16 + k0 + (l >> 4)];
-          const float b = T[(kb * 16 + k0 + (l >> 4)) * LC + bj * 16 + (l & 15)];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+          const float a = L[(bi * 16 + r) * LC + kb * 16 + k0 + g];
+          const float b = T[(kb * 16 + k0 + g) * LC + bj * 16 + r];
+          x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
         }
+      // T_{bi,bj} = -T_{bi,bi} X, contraction index k = 4 g + s at step s: lane (g, r)
+      // holds X[4 g + e][r], i.e. the B operand of step s is its element e = s
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X[w * 320 + ((l >> 4) * 4 + e) * 20 + (l & 15)] = acc[e];
-    }
-    lds_barrier();
-    if (w < npairs) {
-      f32x4 r = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 4; ++s)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(T[(bi * 16 + r) * LC + bi * 16 + 4 * g + s], x[s], y, 0, 0, 0);
 #pragma unroll
-      for (int k0 = 0; k0 < 16; k0 += 4) {
-        const float a = T[(bi * 16 + (l & 15)) * LC + bi * 16 + k0 + (l >> 4)];
-        const float b = X[w * 320 + (k0 + (l >> 4)) * 20 + (l & 15)];
-        r = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, r, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) T[(bi * 16 + (l >> 4) * 4 + e) * LC + bj * 16 + (l & 15)] = -r[e];
+      for (int e = 0; e < 4; ++e) T[(bi * 16 + 4 * g + e) * LC + bj * 16 + r] = -y[e];
     }
     lds_barrier();
   }
@@ -102,10 +94,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   using LD = Swz<OT, D>;
   constexpr int NW = kPrepWaves, NT = kPrepThreads, LCF = C + 4, RT = C / 16;
   constexpr int KSD = ks_of<OT, D>();
-  // K and Q (direct loads) for the Gram products; afterwards the same bytes hold L, T,
-  // the inverse's scratch and the staging tile of M.
+  // K and Q (direct loads) for the Gram products; afterwards the same bytes hold L, T and
+  // the staging tile of M.
   constexpr int KQ_BYTES = 2 * C * D * (int)sizeof(OT);
-  constexpr int INV_BYTES = (2 * C * LCF + 3 * 320) * 4 + C * C * (int)sizeof(OT);
+  constexpr int INV_BYTES = 2 * C * LCF * 4 + C * C * (int)sizeof(OT);
   __shared__ __align__(16) char smem[KQ_BYTES > INV_BYTES ? KQ_BYTES : INV_BYTES];
   constexpr int GH = NW;  // gate records formed per pass: one wave per value head
   __shared__ float sg[GH][C], sbeta[GH][C];
@@ -113,8 +105,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   OT* const sQ = sK + C * D;
   float* const sL = reinterpret_cast<float*>(smem);
   float* const sT = sL + C * LCF;
-  float* const sX = sT + C * LCF;
-  OT* const sM = reinterpret_cast<OT*>(sX + 3 * 320);
+  OT* const sM = reinterpret_cast<OT*>(sT + C * LCF);
 
   const int c = blockIdx.x, kh = blockIdx.y;
   const ChunkInfo ci = p.chunks[c];
@@ -187,12 +178,13 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
       const typename V::type* src = reinterpret_cast<const typename V::type*>(sM);
       for (int idx = threadIdx.x; idx < C * C / V::N; idx += NT) dst[idx] = src[idx];
     }
-    invert_unit_lower<C, LCF, NW>(sL, sT, sX);
-    {
+    invert_unit_lower<C, LCF, NW>(sL, sT);
+    {  // T with zeros above the diagonal blocks
       OT* dst = (OT*)p.sv_T + ch * C * C;
       for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
         const int i = idx / (C / 4), j0 = (idx % (C / 4)) * 4;
-        store4(dst + i * C + j0, *reinterpret_cast<const f32x4*>(sT + i * LCF + j0));
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        store4(dst + i * C + j0, j0 / 16 > i / 16 ? z : *reinterpret_cast<const f32x4*>(sT + i * LCF + j0));
       }
     }
     lds_barrier();  // sL, sT, sM free for the next head
