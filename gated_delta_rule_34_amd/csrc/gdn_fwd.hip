@@ -179,12 +179,21 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
       for (int idx = threadIdx.x; idx < C * C / V::N; idx += NT) dst[idx] = src[idx];
     }
     invert_unit_lower<C, LCF, NW>(sL, sT);
-    {  // T with zeros above the diagonal blocks
+    {  // T with zeros above the diagonal blocks, 16-byte stores
       OT* dst = (OT*)p.sv_T + ch * C * C;
-      for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
-        const int i = idx / (C / 4), j0 = (idx % (C / 4)) * 4;
+      constexpr int E8 = 16 / (int)sizeof(OT);  // elements per 16-byte store
+      for (int idx = threadIdx.x; idx < C * C / E8; idx += NT) {
+        const int i = idx / (C / E8), j0 = (idx % (C / E8)) * E8;
+        const bool up = j0 / 16 > i / 16;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        store4(dst + i * C + j0, j0 / 16 > i / 16 ? z : *reinterpret_cast<const f32x4*>(sT + i * LCF + j0));
+        const f32x4 a = up ? z : *reinterpret_cast<const f32x4*>(sT + i * LCF + j0);
+        if constexpr (E8 == 8) {
+          const f32x4 b = up ? z : *reinterpret_cast<const f32x4*>(sT + i * LCF + j0 + 4);
+          *reinterpret_cast<bf16x8*>(dst + i * C + j0) =
+              bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3], (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+        } else {
+          store4(dst + i * C + j0, a);
+        }
       }
     }
     lds_barrier();  // sL, sT, sM free for the next head
