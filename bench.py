@@ -132,14 +132,15 @@ def kernel_model(name, C, D, Hk, Hv, n_chunks, es=2):
     ch, ck = n_chunks * Hv, n_chunks * Hk  # (chunk, value head) and (chunk, key head) units
     cd, cc, dd = C * D * es, C * C * es, D * D * es
     gates = 8 * C  # gamma and beta (or g and beta) per unit, float32
+    grec = 16 * C  # the gate record: gamma, beta, b = 2^gamma, e = 2^(gamma_last - gamma)
     model = {
         # K K^T and Q K^T per key head. Reads K, Q, g, beta; writes T, M and the gate record.
-        "k_prep": (ck * 4 * C * C * D, ck * 2 * cd + ch * (gates + 2 * cc + gates)),
+        "k_prep": (ck * 4 * C * C * D, ck * 2 * cd + ch * (gates + 2 * cc + grec)),
         # K S, Q S, T X, M Delta, K^T (e o Delta). Reads K, Q, V, T, M, gates; writes S, Delta, O.
-        "k_fwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + gates + dd + 2 * cd)),
+        "k_fwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + grec + dd + 2 * cd)),
         # K dS, M^T dO, T^T dDelta, Q^T dO, K^T (nb o A). Reads K, Q, dO, T, M, gates; writes dS,
         # A^T (A = T^T dDelta) and dV.
-        "k_bwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + gates + dd + 2 * cd)),
+        "k_bwd_sweep": (ch * (6 * C * D * D + 4 * C * C * D), ck * 2 * cd + ch * (cd + 2 * cc + grec + dd + 2 * cd)),
         # Per value head dO S0^T, Delta dS^T, A S0^T, dO Delta^T, A Delta^T; per key head Q K^T,
         # K K^T and the three products that fold the head sums into dq and dk. Reads S0, dS,
         # Delta, A^T, dO, V, gates and g per value head, K and Q per key head; writes dg, dbeta

@@ -51,7 +51,7 @@ gdn_status check_problem(const gdn_problem* p) {
 // Region sizes in bytes (each rounded up to 256 B).
 struct Regions {
   size_t chunks, seq_chunk;        // chunk table, first chunk per sequence
-  size_t oDD, oCD, oCC, gb;        // per (chunk, value head): [D][D], [D][C], [C][C] elements, [2][C] f32
+  size_t oDD, oCD, oCC, gb;        // per (chunk, value head): [D][D], [D][C], [C][C] elements, [kGateRows][C] f32
 };
 
 Regions regions(const gdn_problem* p) {
@@ -63,7 +63,7 @@ Regions regions(const gdn_problem* p) {
   r.oDD = align_up(nc * Hv * D * D * es);
   r.oCD = align_up(nc * Hv * C * D * es);
   r.oCC = align_up(nc * Hv * C * C * es);
-  r.gb = align_up(nc * Hv * 2 * C * sizeof(float));
+  r.gb = align_up(nc * Hv * gdn::kGateRows * C * sizeof(float));
   return r;
 }
 

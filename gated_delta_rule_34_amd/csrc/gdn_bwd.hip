@@ -98,7 +98,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
   using FragD = typename Mf<OT, KSD>::frag;
   using FragC = typename Mf<OT, KSC>::frag;
   __shared__ __align__(16) OT sbuf[2][CF::BUF];
-  __shared__ __align__(16) float sgb[2][2 * C];
+  __shared__ __align__(16) float sgb[2][kGateRows * C];
   __shared__ __align__(16) OT stg[C * CF::LSO];  // the chunk's dV rows, all D columns
 
   int grp, hh;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
 
   TileDma<C, D, NW, OT> dmD;         // K, Q, dO
   TileDma<C, C, NW, OT> dmC;         // T, M
-  TileDma<1, 2 * C, NW, float> dmG;  // gate record
+  TileDma<1, kGateRows * C, NW, float> dmG;  // gate record
   dmD.init(w);
   dmC.init(w);
   dmG.init(w);
@@ -127,7 +127,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     dmD.issue(b + CF::O_O, (const OT*)p.dO + t0 * p.dO_rs + h * D, p.dO_rs, len, w);
     dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
     dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
-    dmG.issue(sgb[buf], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+    dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kGateRows * C, 1, w);
   };
 
   // The adjoint: dS[ct][dt] holds dS[16 dt + g4 + e][v0 + 16 ct + r16].
@@ -158,20 +158,21 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     const OT* sO = sbuf[buf] + CF::O_O;
     const OT* sT = sbuf[buf] + CF::O_T;
     const OT* sM = sbuf[buf] + CF::O_M;
-    const float* gam = sgb[buf];  // log2 units
-    const float* bet = gam + C;
-    const float gn = gam[C - 1], bn = __builtin_amdgcn_exp2f(gn), sc = p.scale;
+    const float* bet = sgb[buf] + C;
+    const float* brec = sgb[buf] + 2 * C;  // b = 2^gamma
+    const float* erec = sgb[buf] + 3 * C;  // e = 2^(gamma_last - gamma)
+    const float bn = brec[C - 1], sc = p.scale;
     float ex[RT][4], sbx[RT][4], nbb[RT][4];  // e_i, scale b_i, -beta_i b_i
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * t + g4);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * t + g4);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(brec + 16 * t + g4);
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(erec + 16 * t + g4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float b = __builtin_amdgcn_exp2f(gv[e]);
-        ex[t][e] = __builtin_amdgcn_exp2f(gn - gv[e]);
-        sbx[t][e] = sc * b;
-        nbb[t][e] = -bv[e] * b;
+        ex[t][e] = e4[e];
+        sbx[t][e] = sc * b4[e];
+        nbb[t][e] = -bv[e] * b4[e];
       }
     }
     // dS_C's fragments (B operand over d) and its saved copy dS^T[v][d]
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     OT* b = sB(j % CF::NBUF);
     if (part == 0) {
       dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
-      if (blk == 0) dmG.issue(sgb[(j / NBH) % 3], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+      if (blk == 0) dmG.issue(sgb[(j / NBH) % 3], p.sv_gb + ch * kGateRows * C, 2 * C, 1, w);  // gamma, beta
     } else if (part == 1) {
       dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
     } else {

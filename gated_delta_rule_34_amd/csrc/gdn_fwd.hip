@@ -129,11 +129,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
       const float lg = ok ? __builtin_amdgcn_logf(p.g[(int64_t)(ci.t0 + i) * p.Hv + h]) : 0.f;  // log2 g
       const float be = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
       const float gam = wave_scan_incl(i < C ? lg : 0.f);
+      const float glast = lane_value(gam, C - 1);
       if (i < C) {
         sg[w][i] = gam;
         sbeta[w][i] = be;
-        p.sv_gb[ch * 2 * C + i] = gam;
-        p.sv_gb[ch * 2 * C + C + i] = be;
+        float* rec = p.sv_gb + ch * kGateRows * C;
+        rec[i] = gam;
+        rec[C + i] = be;
+        rec[2 * C + i] = __builtin_amdgcn_exp2f(gam);
+        rec[3 * C + i] = __builtin_amdgcn_exp2f(glast - gam);
       }
     }
   };
@@ -268,7 +272,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
   using FragD = typename Mf<OT, KSD>::frag;
   using FragC = typename Mf<OT, KSC>::frag;
   __shared__ __align__(16) OT sbuf[2][CF::BUF];
-  __shared__ __align__(16) float sgb[2][2 * C];
+  __shared__ __align__(16) float sgb[2][kGateRows * C];
   __shared__ __align__(16) OT stg[C * CF::LSO];  // the chunk's output rows, all D columns
 
   int grp, hh;
@@ -283,7 +287,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
 
   TileDma<C, D, NW, OT> dmD;         // K, Q, V
   TileDma<C, C, NW, OT> dmC;         // T, M
-  TileDma<1, 2 * C, NW, float> dmG;  // gate record
+  TileDma<1, kGateRows * C, NW, float> dmG;  // gate record
   dmD.init(w);
   dmC.init(w);
   dmG.init(w);
@@ -297,7 +301,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     dmD.issue(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
     dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
     dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
-    dmG.issue(sgb[buf], p.sv_gb + ch * 2 * C, 2 * C, 1, w);
+    dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kGateRows * C, 1, w);
   };
 
   // The state: S[ct][dt] holds S[16 dt + g4 + e][v0 + 16 ct + r16].
@@ -328,19 +332,16 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     const OT* sV = sbuf[buf] + CF::O_V;
     const OT* sT = sbuf[buf] + CF::O_T;
     const OT* sM = sbuf[buf] + CF::O_M;
-    const float* gam = sgb[buf];  // log2 units
-    const float* bet = gam + C;
+    const float* bet = sgb[buf] + C;
+    const float* brec = sgb[buf] + 2 * C;  // b = 2^gamma
+    const float* erec = sgb[buf] + 3 * C;  // e = 2^(gamma_last - gamma)
     // decay factors of this lane's accumulator rows i = 16 t + g4 + e
-    const float gn = gam[C - 1], bn = __builtin_amdgcn_exp2f(gn);
-    float bx[RT][4], ex[RT][4];
+    const float bn = brec[C - 1];
+    f32x4 bx[RT], ex[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * t + g4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bx[t][e] = __builtin_amdgcn_exp2f(gv[e]);
-        ex[t][e] = __builtin_amdgcn_exp2f(gn - gv[e]);
-      }
+      bx[t] = *reinterpret_cast<const f32x4*>(brec + 16 * t + g4);
+      ex[t] = *reinterpret_cast<const f32x4*>(erec + 16 * t + g4);
     }
     // the state's MFMA fragments (B operand over d), shared by K S, Q S and the saved copy
     FragD Sb[CT][NSD];

@@ -51,11 +51,16 @@ struct Prob {
                  // columns, each block row-major (rows past the end of a chunk not written)
   void* sv_T;    // [c][h][C][C]  T = (I + L)^-1, row-major
   void* sv_M;    // [c][h][C][C]  M = Gamma o Q K^T (lower incl. diagonal), row-major
-  float* sv_gb;  // [c][h][2][C]  float32: gamma (cumulative log g), beta (0 past the end)
+  float* sv_gb;  // [c][h][kGateRows][C]  float32 gate record, rows below
   // workspace
   void* ws_dS;   // [c][h][D][D]  state adjoint flowing into the end of the chunk, dS^T[v][d]
   void* ws_At;   // [c][h][D][C]  A^T[v][i], A = T^T dDelta
 };
+
+// Rows of the per-(chunk, value head) gate record: gamma = cumulative log2 g (rows past the
+// end add 0), beta (0 past the end), b = 2^gamma and e = 2^(gamma_last - gamma), the two
+// decay factors the sweeps apply to every row.
+constexpr int kGateRows = 4;
 
 // Value columns per block of the gradient kernel's value loop (also the block width of the
 // saved Delta, so that each block is one contiguous run of memory).
