@@ -225,6 +225,14 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
           for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)(bv[e] * Z[ct][t][e]);
       }
     }
+    // dS <- b_n dS + Q^T (scale b o dO) while the other waves finish staging
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dS[ct][dt] *= bn;
+    wave_mm_cm<OT, C, DT, CT>(
+        dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sQ, 16 * m, s); },
+        [&](int j, int s) { return scale_acc<OT, KSC, RT>(ld_t<OT, KSC, ACC, LD>(sO, v0 + 16 * j, s), s, sbx); });
     lds_barrier();  // the chunk's dV rows are staged
     {  // full dV rows, 16-byte stores spread over every wave
       using V = Vec16<OT>;
@@ -238,14 +246,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
               *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
       }
     }
-    // dS <- b_n dS + Q^T (scale b o dO) - K^T (beta b o Z)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dS[ct][dt] *= bn;
-    wave_mm_cm<OT, C, DT, CT>(
-        dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sQ, 16 * m, s); },
-        [&](int j, int s) { return scale_acc<OT, KSC, RT>(ld_t<OT, KSC, ACC, LD>(sO, v0 + 16 * j, s), s, sbx); });
+    // dS <- dS - K^T (beta b o Z)
     wave_mm_cm<OT, C, DT, CT>(
         dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sK, 16 * m, s); },
         [&](int j, int s) {
