@@ -19,8 +19,10 @@ sign or index, a transposed operand, a wrong head map -- fails at least one:
 * linearity in V and in S0, split-sequence resume, zero-length sequences;
 * falsification: builds of the oracle with a planted mistake must fail a pin.
 """
+import json
 import os
 import tempfile
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -310,6 +312,39 @@ def test_threads_do_not_change_results(oracle_lib):
         assert np.array_equal(a[name], b[name]), name
 
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    """A hand-worked example: inputs and expected values as exact fractions."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        fx = json.load(f)
+    arr = lambda x: np.array(x, dtype=object).astype(str)
+    num = lambda x: np.vectorize(lambda s: float(Fraction(s)))(arr(x)).astype(np.float64)
+    ins = {k: num(v) for k, v in fx["inputs"].items()}
+    exp = {k: num(v) for k, v in fx["expected"].items()}
+    return fx, ins, exp
+
+
+def _golden_errors(lib, name="scalar_state_two_heads.json"):
+    """Largest absolute error of the oracle on a golden example, per output."""
+    fx, x, e = _golden(name)
+    cu = np.array(fx["cu_seqlens"], dtype=np.int64)
+    sc = float(Fraction(fx["scale"]))
+    o, ST = oracle.gdn_fwd(cu, x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], sc, lib=lib)
+    gr = oracle.gdn_bwd(cu, x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["dO"], x["dS_T"], sc, lib=lib)
+    got = dict(o=o, S_T=ST, **gr)
+    return {k: float(np.max(np.abs(got[k] - e[k]))) for k in e}
+
+
+def test_golden_hand_worked_example(oracle_lib):
+    """tests/golden/scalar_state_two_heads.json: two tokens, Dk = Dv = 1, two value heads
+    on one key head, every output derived by hand from the page's recurrence (the
+    derivation is in the file). Exact in binary, so the oracle must match to rounding."""
+    errs = _golden_errors(oracle.LIB)
+    assert all(v < 1e-14 for v in errs.values()), errs
+
+
 def _pins_fail(lib):
     """Run a cheap subset of the pins against an oracle build; return names that failed."""
     failed = []
@@ -322,6 +357,8 @@ def _pins_fail(lib):
                           case.scale, lib=lib)
     if normwise(o, o_ref) > 1e-12:
         failed.append("householder")
+    if any(v > 1e-14 for v in _golden_errors(lib).values()):
+        failed.append("golden")
     return failed
 
 
