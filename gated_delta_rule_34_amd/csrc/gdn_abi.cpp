@@ -45,6 +45,7 @@ gdn_status check_problem(const gdn_problem* p) {
   if (p->T_total > INT32_MAX - 64) return GDN_EINVAL;
   const int64_t nc = chunk_bound(p);
   if (nc > INT32_MAX / 64) return GDN_EINVAL;
+  if (nc * p->Hk > INT32_MAX) return GDN_EINVAL;  // one workgroup per (chunk, key head)
   return GDN_OK;
 }
 

@@ -347,7 +347,10 @@ __device__ __forceinline__ float group4_sum(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-// Grid (nc_max, Hk). Gradients of the r value heads of one key head in one chunk.
+// Grid nc_max * Hk, key head fastest: workgroup c Hk + kh takes the gradients of the r value
+// heads of key head kh in chunk c. Workgroups that start together then read the same rows
+// of q, k, v and dO (all key heads of a few chunks) and neighbouring saved blocks, which
+// the memory keeps in open rows: measurably faster than the chunk-fastest order.
 //
 // Phase 1 streams the value dimension in blocks of BV columns (direct loads, the next two
 // blocks in flight while the current one is used; one workgroup barrier per block).
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   constexpr int GRM = 4;
   __shared__ float sgo[2][GRM][C];
 
-  const int c = blockIdx.x, kh = blockIdx.y;
+  const int kh = blockIdx.x % p.Hk, c = blockIdx.x / p.Hk;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int n = ci.len;
@@ -817,7 +820,7 @@ static hipError_t bwd_seq(const Prob& p, hipStream_t s) {
     traced("k_bwd_sweep", s,
            [&] { k_bwd_sweep<TI, C, D><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });
   if (p.nc_max > 0)
-    traced("k_bwd_grad", s, [&] { k_bwd_grad<TI, C, D><<<dim3(p.nc_max, p.Hk), kThreadsG, 0, s>>>(p); });
+    traced("k_bwd_grad", s, [&] { k_bwd_grad<TI, C, D><<<p.nc_max * p.Hk, kThreadsG, 0, s>>>(p); });
   return hipGetLastError();
 }
 

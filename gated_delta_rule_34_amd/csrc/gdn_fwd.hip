@@ -87,7 +87,7 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T) {
   }
 }
 
-// Grid (nc_max, Hk).
+// Grid nc_max * Hk, key head fastest (as the gradient kernel): workgroup c Hk + kh.
 template <typename TI, int C, int D>
 __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   using OT = TI;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   float* const sT = sL + C * LCF;
   OT* const sM = reinterpret_cast<OT*>(sT + C * LCF);
 
-  const int c = blockIdx.x, kh = blockIdx.y;
+  const int kh = blockIdx.x % p.Hk, c = blockIdx.x / p.Hk;
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int n = ci.len, w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
@@ -453,7 +453,7 @@ template <typename TI, int C, int D>
 static hipError_t fwd_seq(const Prob& p, hipStream_t s) {
   using CF = SwCfg<TI, C, D>;
   traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
-  if (p.nc_max > 0) traced("k_prep", s, [&] { k_prep<TI, C, D><<<dim3(p.nc_max, p.Hk), kPrepThreads, 0, s>>>(p); });
+  if (p.nc_max > 0) traced("k_prep", s, [&] { k_prep<TI, C, D><<<p.nc_max * p.Hk, kPrepThreads, 0, s>>>(p); });
   if (p.N > 0)
     traced("k_fwd_sweep", s,
            [&] { k_fwd_sweep<TI, C, D><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });

@@ -51,7 +51,8 @@ extern "C" {
 
 typedef enum {
   GDN_OK = 0,
-  GDN_EINVAL = -1,       /* bad size, count, stride or missing required pointer */
+  GDN_EINVAL = -1,       /* bad size, count, stride or missing required pointer; also more
+                            than 2^31 - 1 (chunk, key head) pairs */
   GDN_EUNSUPPORTED = -2, /* head size / chunk / dtype combination not built */
   GDN_EALIGN = -3,       /* pointer or row stride not aligned as required */
   GDN_EWORKSPACE = -4,   /* workspace missing or smaller than the size query returns */
