@@ -11,8 +11,10 @@ import sys
 import numpy as np
 import pytest
 
+import dataclasses
+
 import oracle
-from synth import config_case, make_case
+from synth import config_case, make_case, round_f32
 from gdn_gpu import GRAD_NAMES, OUT_NAMES, compare, run_gpu
 
 pytestmark = pytest.mark.gpu
@@ -64,6 +66,27 @@ def test_small_shapes(spec):
     case = make_case(500 + len(name), lens, Hk, Hv, D, dtype=dtype, chunk=chunk, gate="clamp09",
                      with_S0=True, with_dST=True, packed=(dtype == "bf16"), varlen=varlen, name=name)
     _check(case)
+
+
+DEGENERATE = [
+    # name, gate rule, beta rule, dtype, chunk, D
+    ("g1_beta0_bf16", "one", "zero", "bf16", 64, 128),    # state carried unchanged: T = I
+    ("g1_beta1_bf16", "one", "one", "bf16", 64, 128),     # no decay, full delta-rule write
+    ("g_pow6_bf16", "pow6", "keep", "bf16", 64, 128),     # strong decay: 2^gamma underflows within a chunk
+    ("g1_beta0_f32_C16", "one", "zero", "f32", 16, 32),
+]
+
+
+@pytest.mark.parametrize("spec", DEGENERATE, ids=[s[0] for s in DEGENERATE])
+def test_degenerate_gates(spec):
+    """Boundary values of the gates: g = 1 (log g = 0), beta = 0 and 1, and gates so small
+    that the cumulative decay of a chunk falls below the float32 range (g ~ 1e-8 .. 0.8)."""
+    name, gr, br, dtype, chunk, D = spec
+    case = make_case(900 + len(name), [150, 37], 2, 6, D, dtype=dtype, chunk=chunk, gate="raw",
+                     with_S0=True, with_dST=True, packed=(dtype == "bf16"), varlen=True, name=name)
+    g = {"one": np.ones_like(case.g), "pow6": round_f32(case.g ** 6)}[gr]
+    beta = {"zero": np.zeros_like(case.beta), "one": np.ones_like(case.beta), "keep": case.beta}[br]
+    _check(dataclasses.replace(case, g=g, beta=beta))
 
 
 def test_config2_strided_vrepeat3():
