@@ -93,8 +93,8 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
   using CF = BwCfg<TI, C, D>;
   constexpr int NW = CF::NW, WC = CF::WC, CT = CF::CT, DT = CF::DT, RT = CF::RT, CE = CF::CE;
   constexpr int KSD = ks_of<OT, D>(), KSC = ks_of<OT, C>(), NSD = D / KSD, NSC = C / KSC;
-  using LD = Swz<OT, D>;
-  using LC = Swz<OT, C>;
+  using LD = Swz<OT, D, true>;
+  using LC = Swz<OT, C, true>;
   using FragD = typename Mf<OT, KSD>::frag;
   using FragC = typename Mf<OT, KSC>::frag;
   __shared__ __align__(16) OT sbuf[2][CF::BUF];
@@ -111,8 +111,8 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
   const int w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
   const int v0 = w * WC;
 
-  TileDma<C, D, NW, OT> dmD;         // K, Q, dO
-  TileDma<C, C, NW, OT> dmC;         // T, M
+  TileDma<C, D, NW, OT, true> dmD;   // K, Q, dO
+  TileDma<C, C, NW, OT, true> dmC;   // T, M
   TileDma<1, kGateRows * C, NW, float> dmG;  // gate record
   dmD.init(w);
   dmC.init(w);
@@ -380,10 +380,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   constexpr int KSC = ks_of<OT, C>(), KSB = ks_of<OT, BV>(), KSD = ks_of<OT, D>();
   using M = Mf<OT, KSB>;
   using FragB = typename M::frag;
-  using LD = Swz<OT, D>;
-  using LC = Swz<OT, C>;
-  using LB = Swz<OT, BV>;
-  using LP = Swz<OT, CF::PW>;
+  using LD = Swz<OT, D, true>;
+  using LC = Swz<OT, C, true>;
+  using LB = Swz<OT, BV, true>;
+  using LP = Swz<OT, CF::PW, true>;
   using OrdD = RowOrd<OT, D>;  // storage order of the saved S^T and dS^T rows
   using OrdC = RowOrd<OT, C>;  // storage order of the saved A^T rows
   constexpr int RS = NCB * C;  // one partial-sum slot
@@ -413,11 +413,11 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   const int h0 = kh * p.r;
   constexpr int NH = NW / 2;  // the two halves of the waves load different tensors
   constexpr int PB = CF::PB, PW = CF::PW;
-  TileDma<BV, D, NW, OT> dmS;   // S0^T, dS^T row blocks (every wave)
-  TileDma<BV, C, NH, OT> dmA;   // A^T row block (first half)
-  TileDma<C, BV, NH, OT> dmL;   // Delta block (second half)
-  TileDma<C, PW, NH, OT> dmP;   // dO (first half) or V (second half) for a pair of blocks
-  TileDma<C, D, NW, OT> dmD;    // K, Q
+  TileDma<BV, D, NW, OT, true> dmS;   // S0^T, dS^T row blocks (every wave)
+  TileDma<BV, C, NH, OT, true> dmA;   // A^T row block (first half)
+  TileDma<C, BV, NH, OT, true> dmL;   // Delta block (second half)
+  TileDma<C, PW, NH, OT, true> dmP;   // dO (first half) or V (second half) for a pair of blocks
+  TileDma<C, D, NW, OT, true> dmD;    // K, Q
   TileDma<1, 2 * C, NW, float> dmG;  // gate record
   const int wh = w % NH;
   dmS.init(w);
@@ -737,8 +737,11 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
         const float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
         if (p.r <= GRM) {
-          sgo[0][hh][i] = db;
-          sgo[1][hh][i] = dgv;
+          // the row offset is formed here rather than kept live across the item's loops
+          int li = i;
+          asm volatile("" : "+v"(li));
+          sgo[0][hh][li] = db;
+          sgo[1][hh][li] = dgv;
         } else {
           const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
           p.dbeta[row] = db;

@@ -80,12 +80,32 @@ template <int LD> struct Pad {
 };
 
 // Dense row-major [R][Cn] whose 16-byte chunks are XOR-permuted within each row, so that
-// 16 consecutive rows read at one column (ld_n) or 4 x 4 rows read across two chunks
-// (ld_t) fall in distinct banks. Dense rows are what the direct global-to-LDS loads write.
-template <typename T, int Cn> struct Swz {
+// the reads of the MFMA fragment loaders fall in distinct banks of the 64 x 4-byte LDS.
+// Dense rows are what the direct global-to-LDS loads write. Two row maps:
+//  - plain (TR = false): chunk c of row r sits at c xor (r mod 16) (rows of 16 or more
+//    chunks; shorter rows use the row's position in its 256-byte bank line band). 16
+//    consecutive rows read at one chunk column (ld_n) hit distinct banks;
+//  - transpose-friendly (TR = true, bf16 rows of 8 or 16 chunks; RL = 16 / NCH rows per
+//    256-byte bank line, k = (r / RL) mod NCH):  s = (2k mod NCH) xor (NCH/2 + 1 if
+//    k >= NCH/2). It keeps ld_n conflict-free and also the transpose reads of ld_t and
+//    ld_col4, which take two adjacent chunks of 4 rows per lane group and serve two
+//    groups per cycle (rows 8j..8j+7, or 8j..8j+3 with 8j+8..8j+11): over any such 8
+//    rows the chunk pairs (s >> 1) are distinct. With the plain map those reads measured
+//    twice their conflict-free time on the LDS bank-conflict counters (four times where
+//    a row's runs are in fragment order; the map leaves the 2-way minimum there). Its
+//    row-dependent offsets cost more registers, so kernels choose it per layout.
+template <typename T, int Cn, bool TR = false> struct Swz {
   static constexpr int CE = 16 / (int)sizeof(T), NCH = Cn / CE;
   static_assert(Cn % CE == 0 && (NCH & (NCH - 1)) == 0, "row must be a power-of-two count of 16-byte chunks");
-  __device__ __forceinline__ static int s(int r) { return NCH >= 16 ? (r & 15) : ((r * NCH) >> 4) & (NCH - 1); }
+  __device__ __forceinline__ static int s(int r) {
+    if constexpr (TR && sizeof(T) == 2 && (NCH == 16 || NCH == 8)) {
+      constexpr int RL = 16 / NCH, HB = NCH == 16 ? 3 : 2;  // rows per bank line; log2(NCH / 2)
+      const int k = (r / RL) & (NCH - 1);
+      return ((2 * k) & (NCH - 1)) ^ (((k >> HB) & 1) * (NCH / 2 + 1));
+    } else {
+      return NCH >= 16 ? (r & 15) : ((r * NCH) >> 4) & (NCH - 1);
+    }
+  }
   __device__ __forceinline__ static int at(int r, int c) { return r * Cn + (((c / CE) ^ s(r)) * CE) + (c % CE); }
 };
 
@@ -281,15 +301,15 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-// Direct loads of a global tile [R][Cn] into LDS in the layout Swz<T, Cn>, issued by NW
+// Direct loads of a global tile [R][Cn] into LDS in the layout Swz<T, Cn, TR>, issued by NW
 // waves (wave index w < NW); each wave instruction fills 1 KiB of LDS. Each lane's row and
 // byte offset within the row are fixed per instruction and computed once; issue() then
 // costs one multiply-add per instruction. Rows at or past nvalid fall outside the buffer
 // range and arrive as zeros, so rows past the end of a chunk read as zero and nothing
 // outside the caller's rows is read. Row stride times R times sizeof(T) must fit in 32 bits
 // (checked on the host).
-template <int R, int Cn, int NW, typename T> struct TileDma {
-  using L = Swz<T, Cn>;
+template <int R, int Cn, int NW, typename T, bool TR = false> struct TileDma {
+  using L = Swz<T, Cn, TR>;
   static constexpr int TOT = R * L::NCH, U = (TOT + NW * 64 - 1) / (NW * 64);
   uint32_t row[U], cof[U];
   __device__ __forceinline__ void init(int w) {
