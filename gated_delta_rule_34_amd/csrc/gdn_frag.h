@@ -94,9 +94,20 @@ template <int LD> struct Pad {
 //    twice their conflict-free time on the LDS bank-conflict counters (four times where
 //    a row's runs are in fragment order; the map leaves the 2-way minimum there). Its
 //    row-dependent offsets cost more registers, so kernels choose it per layout.
-template <typename T, int Cn, bool TR = false> struct Swz {
+//
+// PT = true leaves a 128-byte gap after every 16 rows. Two reads of one lane in
+// neighbouring 16-row tiles then differ by a constant that is not a multiple of 512
+// bytes: the compiler keeps them as two ds_read_b64 (one base, immediate offsets) instead
+// of fusing them into a ds_read2st64_b64, which measured four times their cost because
+// both rows fall in the same banks; and with the gap they fall in different ones.
+template <typename T, int Cn, bool TR = false, bool PT = false> struct Swz {
   static constexpr int CE = 16 / (int)sizeof(T), NCH = Cn / CE;
   static_assert(Cn % CE == 0 && (NCH & (NCH - 1)) == 0, "row must be a power-of-two count of 16-byte chunks");
+  static_assert(!PT || NCH >= 4, "a direct load of 64 chunks must stay inside one 16-row tile");
+  static constexpr int TSTR = 16 * Cn + (PT ? 128 / (int)sizeof(T) : 0);  // elements per 16 rows
+  // Elements spanned by R rows (R a multiple of 16 when PT).
+  static constexpr int size(int R) { return PT ? (R / 16) * TSTR : R * Cn; }
+  __device__ __forceinline__ static int row_off(int r) { return (r >> 4) * TSTR + (r & 15) * Cn; }
   __device__ __forceinline__ static int s(int r) {
     if constexpr (TR && sizeof(T) == 2 && (NCH == 16 || NCH == 8)) {
       constexpr int RL = 16 / NCH, HB = NCH == 16 ? 3 : 2;  // rows per bank line; log2(NCH / 2)
@@ -106,7 +117,7 @@ template <typename T, int Cn, bool TR = false> struct Swz {
       return NCH >= 16 ? (r & 15) : ((r * NCH) >> 4) & (NCH - 1);
     }
   }
-  __device__ __forceinline__ static int at(int r, int c) { return r * Cn + (((c / CE) ^ s(r)) * CE) + (c % CE); }
+  __device__ __forceinline__ static int at(int r, int c) { return row_off(r) + (((c / CE) ^ s(r)) * CE) + (c % CE); }
 };
 
 // ------------------------------------------------------------------ fragment loads
@@ -301,15 +312,16 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-// Direct loads of a global tile [R][Cn] into LDS in the layout Swz<T, Cn, TR>, issued by NW
+// Direct loads of a global tile [R][Cn] into LDS in the layout Swz<T, Cn, TR, PT>, issued by NW
 // waves (wave index w < NW); each wave instruction fills 1 KiB of LDS. Each lane's row and
 // byte offset within the row are fixed per instruction and computed once; issue() then
 // costs one multiply-add per instruction. Rows at or past nvalid fall outside the buffer
 // range and arrive as zeros, so rows past the end of a chunk read as zero and nothing
 // outside the caller's rows is read. Row stride times R times sizeof(T) must fit in 32 bits
 // (checked on the host).
-template <int R, int Cn, int NW, typename T, bool TR = false> struct TileDma {
-  using L = Swz<T, Cn, TR>;
+template <int R, int Cn, int NW, typename T, bool TR = false, bool PT = false> struct TileDma {
+  using L = Swz<T, Cn, TR, PT>;
+  static_assert(!PT || R % 16 == 0, "padded tiles hold whole 16-row groups");
   static constexpr int TOT = R * L::NCH, U = (TOT + NW * 64 - 1) / (NW * 64);
   uint32_t row[U], cof[U];
   __device__ __forceinline__ void init(int w) {
@@ -338,7 +350,8 @@ template <int R, int Cn, int NW, typename T, bool TR = false> struct TileDma {
     for (int u = 0; u < U; ++u) {
       const int base = (u * NW + w) * 64;
       if (base < TOT && base + l < TOT)
-        dma16(rsrc, row[u] * rsb + cof[u], __builtin_amdgcn_readfirstlane(la + (uint32_t)base * 16u));
+        dma16(rsrc, row[u] * rsb + cof[u],
+              __builtin_amdgcn_readfirstlane(la + (uint32_t)(L::row_off(base / L::NCH) * (int)sizeof(T))));
     }
   }
 };

@@ -211,8 +211,15 @@ template <typename TI, int C, int D> struct SwCfg {
   static constexpr int CT = WC / 16, DT = D / 16, RT = C / 16;
   static constexpr int CE = 16 / (int)sizeof(TI);  // elements per 16-byte chunk
   static constexpr int LSO = D + CE;               // row stride of the output staging tile
-  // One LDS buffer: K, Q, V [C][D] and T, M [C][C], all Swz layouts.
-  static constexpr int O_K = 0, O_Q = C * D, O_V = 2 * C * D, O_T = 3 * C * D, O_M = O_T + C * C, BUF = O_M + C * C;
+  // LDS layouts of the [C][D] tiles K, Q, V and the [C][C] tiles T, M: plain chunk map,
+  // with the 16-row tile gap where rows hold four or more chunks.
+  static constexpr bool PTD = D * (int)sizeof(TI) >= 64, PTC = C * (int)sizeof(TI) >= 64;
+  using LDL = Swz<TI, D, false, PTD>;
+  using LCL = Swz<TI, C, false, PTC>;
+  // One LDS buffer: K, Q, V, then T, M, each region followed by a 128-byte gap (so that
+  // equal offsets in two regions are not a multiple of 512 bytes apart either).
+  static constexpr int G = 128 / (int)sizeof(TI), SD = LDL::size(C) + G, SC = LCL::size(C) + G;
+  static constexpr int O_K = 0, O_Q = SD, O_V = 2 * SD, O_T = 3 * SD, O_M = O_T + SC, BUF = O_M + SC;
 };
 
 // acc[n][m] += sum_k A(m, k) B(k, n): wave_mm with the accumulator tiles stored
@@ -267,8 +274,8 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
   using CF = SwCfg<TI, C, D>;
   constexpr int NW = CF::NW, WC = CF::WC, CT = CF::CT, DT = CF::DT, RT = CF::RT, CE = CF::CE;
   constexpr int KSD = ks_of<OT, D>(), KSC = ks_of<OT, C>(), NSD = D / KSD, NSC = C / KSC;
-  using LD = Swz<OT, D>;
-  using LC = Swz<OT, C>;
+  using LD = typename CF::LDL;
+  using LC = typename CF::LCL;
   using FragD = typename Mf<OT, KSD>::frag;
   using FragC = typename Mf<OT, KSC>::frag;
   __shared__ __align__(16) OT sbuf[2][CF::BUF];
@@ -285,8 +292,8 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
   const int w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
   const int v0 = w * WC;  // first state column of this wave
 
-  TileDma<C, D, NW, OT> dmD;         // K, Q, V
-  TileDma<C, C, NW, OT> dmC;         // T, M
+  TileDma<C, D, NW, OT, false, CF::PTD> dmD;  // K, Q, V
+  TileDma<C, C, NW, OT, false, CF::PTC> dmC;  // T, M
   TileDma<1, kGateRows * C, NW, float> dmG;  // gate record
   dmD.init(w);
   dmC.init(w);
