@@ -743,7 +743,9 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           sgo[0][hh][li] = db;
           sgo[1][hh][li] = dgv;
         } else {
-          const int64_t row = (int64_t)(ci.t0 + i) * p.Hv + h;
+          int li = i;  // the row offset is formed here, not kept live across the item
+          asm volatile("" : "+v"(li));
+          const int64_t row = (int64_t)(ci.t0 + li) * p.Hv + h;
           p.dbeta[row] = db;
           p.dg[row] = dgv;
         }
@@ -780,6 +782,9 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   lds_barrier();
   // dq, dk of the key head: rows through LDS, 16-byte stores
   {
+    // rows [2C][D] (dq, then dk) in a swizzled layout: a plain row-major tile would put the
+    // 16 rows of a wave's 8-byte writes in the same banks
+    using LS = Swz<TI, D>;
     TI* st = (TI*)smem;
     if (aD) {
 #pragma unroll
@@ -787,8 +792,8 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
 #pragma unroll
         for (int y = 0; y < NT; ++y) {
           const int i = 16 * (m0 + mi) + r16, d = 16 * (nD + y) + g4;
-          store4b(st + i * D + d, dqt[y][mi]);
-          store4b(st + (C + i) * D + d, dkt[y][mi]);
+          store4b(st + LS::at(i, d), dqt[y][mi]);
+          store4b(st + LS::at(C + i, d), dkt[y][mi]);
         }
     }
     lds_barrier();
@@ -801,7 +806,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const int i = r % C;
       if (i < n) {
         TI* dst = r < C ? dq + (int64_t)i * p.dq_rs + cc : dk + (int64_t)i * p.dk_rs + cc;
-        *reinterpret_cast<typename V::type*>(dst) = *reinterpret_cast<const typename V::type*>(st + r * D + cc);
+        *reinterpret_cast<typename V::type*>(dst) = *reinterpret_cast<const typename V::type*>(st + LS::at(r, cc));
       }
     }
     if (p.r <= GRM) {  // dbeta, dg: row i, heads h0 .. h0 + r - 1
