@@ -162,19 +162,20 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     const float* brec = sgb[buf] + 2 * C;  // b = 2^gamma
     const float* erec = sgb[buf] + 3 * C;  // e = 2^(gamma_last - gamma)
     const float bn = brec[C - 1], sc = p.scale;
-    float ex[RT][4], sbx[RT][4], nbb[RT][4];  // e_i, scale b_i, -beta_i b_i
+    // per-row factors of this lane's accumulator rows i = 16 t + g4 + e, each formed from
+    // the gate record where it is used (fewer registers live across the step)
+    auto row_factors = [&](float (&f)[RT][4], auto&& fn) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * t + g4);
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(brec + 16 * t + g4);
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(erec + 16 * t + g4);
+      for (int t = 0; t < RT; ++t) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * t + g4);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(brec + 16 * t + g4);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(erec + 16 * t + g4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ex[t][e] = e4[e];
-        sbx[t][e] = sc * b4[e];
-        nbb[t][e] = -bv[e] * b4[e];
+        for (int e = 0; e < 4; ++e) f[t][e] = fn(bv[e], b4[e], e4[e]);
       }
-    }
+    };
+    float ex[RT][4];  // e_i
+    row_factors(ex, [](float, float, float e_) { return e_; });
     // dS_C's fragments (B operand over d) and its saved copy dS^T[v][d]
     FragD dSb[CT][NSD];
 #pragma unroll
@@ -230,6 +231,8 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) dS[ct][dt] *= bn;
+    float sbx[RT][4];  // scale b_i
+    row_factors(sbx, [&](float, float b_, float) { return sc * b_; });
     wave_mm_cm<OT, C, DT, CT>(
         dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sQ, 16 * m, s); },
         [&](int j, int s) { return scale_acc<OT, KSC, RT>(ld_t<OT, KSC, ACC, LD>(sO, v0 + 16 * j, s), s, sbx); });
@@ -247,6 +250,8 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
       }
     }
     // dS <- dS - K^T (beta b o Z)
+    float nbb[RT][4];  // -beta_i b_i
+    row_factors(nbb, [](float be, float b_, float) { return -be * b_; });
     wave_mm_cm<OT, C, DT, CT>(
         dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sK, 16 * m, s); },
         [&](int j, int s) {
