@@ -75,7 +75,7 @@ size_t fwd_ws(const gdn_problem* p) {
 
 size_t bwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.oDD + r.oCD;  // + dS^T and A^T per chunk
+  return r.chunks + r.seq_chunk + r.oDD + r.oCD;  // + dS^T and A per chunk
 }
 
 // Saved activations: S^T, Delta, T, M per chunk and value head, and the gate record.
@@ -237,7 +237,7 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
   P.seq_chunk = cv.take<int>(r.seq_chunk);
   P.ws_dS = cv.take<void>(r.oDD);
-  P.ws_At = cv.take<void>(r.oCD);
+  P.ws_A = cv.take<void>(r.oCD);
   const hipError_t e = gdn::launch_backward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }

@@ -205,27 +205,18 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int s = 0; s < NSC; ++s) dDb[ct][s] = from_acc<OT, KSC>(dD[ct], s, Ident{});
-    // A = T^T dDelta: the gradient kernel's A (saved as A^T[v][i]) and dV = diag(beta) A
+    // A = T^T dDelta, staged as rows: the flush writes the gradient kernel's A (in blocks
+    // of BV value columns) and dV = diag(beta) A from them
     f32x4 Z[CT][RT];
     zero(Z);
     wave_mm_cm<OT, C, RT, CT>(Z, [&](int m, int s) { return ld_t<OT, KSC, ACC, LC>(sT, 16 * m, s); },
                               [&](int j, int s) { return dDb[j][s]; });
-    {
-      FragC Ab[CT][NSC];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int s = 0; s < NSC; ++s) Ab[ct][s] = from_acc<OT, KSC>(Z[ct], s, Ident{});
-      save_rows_b<OT, C, CT, RT, NSC>((OT*)p.ws_At + ch * D * C, v0, Z, Ab);
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * t + g4);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)(bv[e] * Z[ct][t][e]);
-      }
-    }
+        for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)Z[ct][t][e];
     // dS <- b_n dS + Q^T (scale b o dO) while the other waves finish staging
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -236,17 +227,25 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     wave_mm_cm<OT, C, DT, CT>(
         dS, [&](int m, int s) { return ld_t<OT, KSC, ACC, LD>(sQ, 16 * m, s); },
         [&](int j, int s) { return scale_acc<OT, KSC, RT>(ld_t<OT, KSC, ACC, LD>(sO, v0 + 16 * j, s), s, sbx); });
-    lds_barrier();  // the chunk's dV rows are staged
-    {  // full dV rows, 16-byte stores spread over every wave
+    lds_barrier();  // the chunk's A rows are staged
+    {  // A blocks and full dV rows, 16-byte stores spread over every wave
       using V = Vec16<OT>;
       constexpr int VPR = D / CE;
+      constexpr int BV = grad_block<OT, D>();  // A goes out in blocks of BV columns
       TI* dv = (TI*)p.dv + t0 * p.dv_rs + h * D;
+      OT* ab = (OT*)p.ws_A + ch * C * D;
 #pragma unroll
       for (int idx = threadIdx.x; idx < C * VPR; idx += NW * 64) {
         const int i = idx / VPR, q = idx % VPR;
-        if (i < len)
-          *reinterpret_cast<typename V::type*>(dv + (int64_t)i * p.dv_rs + q * CE) =
-              *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
+        if (i < len) {
+          const typename V::type a = *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
+          *reinterpret_cast<typename V::type*>(ab + (q * CE / BV) * C * BV + i * BV + (q * CE) % BV) = a;
+          const float be = bet[i];
+          typename V::type dvv;
+#pragma unroll
+          for (int k = 0; k < CE; ++k) dvv[k] = (OT)(be * (float)a[k]);
+          *reinterpret_cast<typename V::type*>(dv + (int64_t)i * p.dv_rs + q * CE) = dvv;
+        }
       }
     }
     // dS <- dS - K^T (beta b o Z)
@@ -301,9 +300,9 @@ template <typename TI, int C, int D> struct GradCfg {
   static constexpr int RT = C / 16, DT = D / 16;
   using PT = Part<RT, DT, kWavesG>;
   static constexpr int NCB = PT::WCB;  // column blocks of the partial row sums
-  // One block buffer (elements): S0^T and dS^T row blocks [BV][D], the A^T row block
-  // [BV][C] and the Delta block [C][BV] (all contiguous in memory).
-  static constexpr int O_S0 = 0, O_DS = BV * D, O_AT = 2 * BV * D, O_DL = O_AT + BV * C, BUF = O_DL + C * BV;
+  // One block buffer (elements): S0^T and dS^T row blocks [BV][D], the A block [C][BV]
+  // and the Delta block [C][BV] (all contiguous in memory).
+  static constexpr int O_S0 = 0, O_DS = BV * D, O_A = 2 * BV * D, O_DL = O_A + C * BV, BUF = O_DL + C * BV;
   static constexpr int NBUF = 3;  // block buffers: two blocks in flight
   // One pair buffer: the dO and V column blocks [C][PB BV] of a pair of blocks. dO and V
   // are row views with long strides; a pair makes each row segment a whole 128-byte line.
@@ -359,8 +358,8 @@ __device__ __forceinline__ float group4_sum(float x) {
 //
 // Phase 1 streams the value dimension in blocks of BV columns (direct loads, the next two
 // blocks in flight while the current one is used; one workgroup barrier per block).
-// A = T^T dDelta comes from the reverse sweep, which formed it anyway and already wrote
-// dV = diag(beta) A. Per block, with dO unscaled (the scale is applied afterwards):
+// A = T^T dDelta comes from the reverse sweep (in blocks of BV value columns), which formed
+// it anyway and already wrote dV = diag(beta) A. Per block, with dO unscaled (the scale is applied afterwards):
 //   XQ^T += S0 dO^T,  Y^T += S0 A^T,  XK^T += dS_C Delta^T  (kept transposed, D x C, so that
 //   their row sums over d are sums within a lane),  P += dO Delta^T,  AD += A Delta^T,
 //   A V^T on the diagonal tiles (its diagonal is rowsum(A o V)), and S0 dS_C^T on the
@@ -390,7 +389,6 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   using LB = Swz<OT, BV, true>;
   using LP = Swz<OT, CF::PW, true>;
   using OrdD = RowOrd<OT, D>;  // storage order of the saved S^T and dS^T rows
-  using OrdC = RowOrd<OT, C>;  // storage order of the saved A^T rows
   constexpr int RS = NCB * C;  // one partial-sum slot
 
   __shared__ __align__(16) OT sK[C * D];
@@ -419,7 +417,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   constexpr int NH = NW / 2;  // the two halves of the waves load different tensors
   constexpr int PB = CF::PB, PW = CF::PW;
   TileDma<BV, D, NW, OT, true> dmS;   // S0^T, dS^T row blocks (every wave)
-  TileDma<BV, C, NH, OT, true> dmA;   // A^T row block (first half)
+  TileDma<C, BV, NH, OT, true> dmA;   // A block (first half)
   TileDma<C, BV, NH, OT, true> dmL;   // Delta block (second half)
   TileDma<C, PW, NH, OT, true> dmP;   // dO (first half) or V (second half) for a pair of blocks
   TileDma<C, D, NW, OT, true> dmD;    // K, Q
@@ -449,7 +447,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
     } else {
       if (w < NH)
-        dmA.issue(b + CF::O_AT, (const OT*)p.ws_At + ch * D * C + (size_t)v0 * C, C, BV, wh);
+        dmA.issue(b + CF::O_A, (const OT*)p.ws_A + ch * C * D + (size_t)blk * C * BV, BV, n, wh);
       else
         dmL.issue(b + CF::O_DL, (const OT*)p.sv_D + ch * C * D + (size_t)blk * C * BV, BV, n, wh);
     }
@@ -555,7 +553,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       }
       const OT* sS0 = cur + CF::O_S0;
       const OT* sDS = cur + CF::O_DS;
-      const OT* sAt = cur + CF::O_AT;
+      const OT* sA = cur + CF::O_A;
       const OT* sDL = cur + CF::O_DL;
       const OT* sDO = curp + CF::O_DO;
       const OT* sV = curp + CF::O_V;
@@ -565,7 +563,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
           fo[mi] = ld_n<OT, KSB, STD, LP>(sDO, 16 * (m0 + mi), sp + s);
-          fa[mi] = ld_t<OT, KSB, STD, LC, OrdC>(sAt, 16 * (m0 + mi), s);
+          fa[mi] = ld_n<OT, KSB, STD, LB>(sA, 16 * (m0 + mi), s);
         }
         if (aD) {
           FragB fs[NT], fds[NT], fd[MT];

@@ -54,7 +54,8 @@ struct Prob {
   float* sv_gb;  // [c][h][kGateRows][C]  float32 gate record, rows below
   // workspace
   void* ws_dS;   // [c][h][D][D]  state adjoint flowing into the end of the chunk, dS^T[v][d]
-  void* ws_At;   // [c][h][D][C]  A^T[v][i], A = T^T dDelta
+  void* ws_A;    // [c][h][D/BV][C][BV]  A = T^T dDelta in blocks of BV value columns
+                 // (BV = grad_block; rows past a chunk's end not written)
 };
 
 // Rows of the per-(chunk, value head) gate record: gamma = cumulative log2 g (rows past the
