@@ -50,7 +50,10 @@ void trace_launch(const char* name, hipStream_t s, void (*launch)(const void*), 
       g_free.pop_back();
     }
   }
-  if (!r.a && (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess)) {
+  // Timing-only events: no system-scope fence at record, so the records add no L2
+  // write-back between the traced launches and time only the kernel between them.
+  if (!r.a && (hipEventCreateWithFlags(&r.a, hipEventDisableSystemFence) != hipSuccess ||
+               hipEventCreateWithFlags(&r.b, hipEventDisableSystemFence) != hipSuccess)) {
     launch(ctx);
     return;
   }
