@@ -68,24 +68,28 @@ Regions regions(const gdn_problem* p) {
   return r;
 }
 
-size_t fwd_ws(const gdn_problem* p) {
-  const Regions r = regions(p);
-  return r.chunks + r.seq_chunk;
-}
+// The forward needs no workspace: its only scratch, the chunk table, is saved for the
+// backward (which then does not rebuild it).
+size_t fwd_ws(const gdn_problem*) { return 0; }
 
 size_t bwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.oDD + r.oCD;  // + dS^T and A per chunk
+  return r.oDD + r.oCD;  // dS^T and A per chunk
 }
 
-// Saved activations: S^T, Delta, T, M per chunk and value head, and the gate record.
+// Saved by the forward: the chunk table, then S^T, Delta, T, M per chunk and value head
+// and the gate record.
 size_t saved_bytes(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.oDD + r.oCD + 2 * r.oCC + r.gb;
+  return r.chunks + r.seq_chunk + r.oDD + r.oCD + 2 * r.oCC + r.gb;
 }
 
 void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
   char* b = static_cast<char*>(saved);
+  P.chunks = reinterpret_cast<gdn::ChunkInfo*>(b);
+  b += r.chunks;
+  P.seq_chunk = reinterpret_cast<int*>(b);
+  b += r.seq_chunk;
   P.sv_S = b;
   b += r.oDD;
   P.sv_D = b;
@@ -176,9 +180,8 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
   if (!chunk_states) return GDN_EINVAL;
   if (!aligned(chunk_states, 16)) return GDN_EALIGN;
-  const size_t need = fwd_ws(p);
-  if (!workspace || workspace_bytes < need) return GDN_EWORKSPACE;
-  if (!aligned(workspace, kAlign)) return GDN_EALIGN;
+  (void)workspace;  // none needed (fwd_ws is 0)
+  (void)workspace_bytes;
 
   gdn::Prob P;
   fill_common(P, p);
@@ -187,9 +190,6 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.o = o; P.o_rs = o_rs; P.ST = S_T;
   const Regions r = regions(p);
   carve_saved(P, r, chunk_states);
-  Carver cv{static_cast<char*>(workspace)};
-  P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
-  P.seq_chunk = cv.take<int>(r.seq_chunk);
   const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
@@ -232,10 +232,8 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.dq = dq; P.dq_rs = dq_rs; P.dk = dk; P.dk_rs = dk_rs; P.dv = dv; P.dv_rs = dv_rs;
   P.dg = dg; P.dbeta = dbeta; P.dS0 = dS0;
   const Regions r = regions(p);
-  carve_saved(P, r, const_cast<void*>(chunk_states));
+  carve_saved(P, r, const_cast<void*>(chunk_states));  // the chunk table comes with it
   Carver cv{static_cast<char*>(workspace)};
-  P.chunks = cv.take<gdn::ChunkInfo>(r.chunks);
-  P.seq_chunk = cv.take<int>(r.seq_chunk);
   P.ws_dS = cv.take<void>(r.oDD);
   P.ws_A = cv.take<void>(r.oCD);
   const hipError_t e = gdn::launch_backward(P, p->dtype, static_cast<hipStream_t>(stream));

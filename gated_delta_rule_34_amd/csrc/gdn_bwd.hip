@@ -826,7 +826,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
 template <typename TI, int C, int D>
 static hipError_t bwd_seq(const Prob& p, hipStream_t s) {
   using CF = BwCfg<TI, C, D>;
-  traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
+  // the chunk table is the forward's, saved with the chunk states
   if (p.N > 0)
     traced("k_bwd_sweep", s,
            [&] { k_bwd_sweep<TI, C, D><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });

@@ -80,12 +80,15 @@ typedef struct {
 } gdn_problem;
 
 /* Bytes of device workspace gdn_fwd / gdn_bwd need for this problem (0 on invalid
- * problem). The workspace is scratch: its contents on entry are ignored. */
+ * problem). The workspace is scratch: its contents on entry are ignored. gdn_fwd
+ * needs none: its query returns 0 and its workspace arguments are ignored (NULL, 0
+ * is fine); they stay in the signature so that callers need not change if that does. */
 size_t gdn_fwd_workspace_bytes(const gdn_problem* p);
 size_t gdn_bwd_workspace_bytes(const gdn_problem* p);
 
-/* Bytes of the saved-state buffer gdn_fwd writes and gdn_bwd reads: the float32
- * state at the start of every chunk (layout internal to the library). */
+/* Bytes of the saved-state buffer gdn_fwd writes and gdn_bwd reads: the chunk table of
+ * the problem's sequences and, per chunk, the state at its start and the other chunk
+ * factors (layout internal to the library). */
 size_t gdn_chunk_state_bytes(const gdn_problem* p);
 
 /*
@@ -106,7 +109,7 @@ gdn_status gdn_fwd(const gdn_problem* p,
 
 /*
  * Backward. q, k, v, g, beta, S0 and chunk_states must be those of the forward call
- * on the same problem. dO [rows][Hv*Dv] (dtype), dS_T (float32 or NULL = zeros).
+ * on the same problem (same sequences: the chunk table is read from chunk_states). dO [rows][Hv*Dv] (dtype), dS_T (float32 or NULL = zeros).
  * Writes dq, dk [rows][Hk*Dk] and dv [rows][Hv*Dv] (dtype, overwritten, each with
  * its own row stride; they may be disjoint slices of one packed buffer), dg and
  * dbeta [T_total][Hv] float32, dS0 (float32, or NULL to skip). dg is the derivative

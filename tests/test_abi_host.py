@@ -52,8 +52,8 @@ def prob(G, **kw):
 
 def test_workspace_queries(G):
     p = prob(G)
-    assert G.gdn_fwd_workspace_bytes(p) > 0
-    assert G.gdn_bwd_workspace_bytes(p) > G.gdn_fwd_workspace_bytes(p)
+    assert G.gdn_fwd_workspace_bytes(p) == 0  # the forward's chunk table is saved in the chunk states
+    assert G.gdn_bwd_workspace_bytes(p) > 0
     nc = 2 * 2  # two sequences of two chunks
     assert G.gdn_chunk_state_bytes(p) >= nc * 48 * 128 * 128 * 4
     bigger = prob(G, T_total=512, T=256)
@@ -112,6 +112,18 @@ def status_of(G, p, **over):
     return e.value.status
 
 
+def bwd_status_of(G, p, **over):
+    a = fwd_args(G, p, **over)
+    T = p.T_total
+    qk = lambda base: FakeTensor(base, T, p.Hk * p.Dk, 10240)
+    vv = lambda base: FakeTensor(base, T, p.Hv * p.Dv)
+    with pytest.raises(G.GdnError) as e:
+        G.gdn_bwd(p, a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["chunk_states"], vv(0x90000), None,
+                  qk(0xA0000), qk(0xB0000), vv(0xC0000), FakeTensor(0xD0000, T, p.Hv), FakeTensor(0xE0000, T, p.Hv),
+                  None, a["workspace"], stream=0)
+    return e.value.status
+
+
 def test_rejects_bad_problems(G):
     assert status_of(G, prob(G, Hv=47)) == G.GDN_EINVAL
     assert status_of(G, prob(G, D=96)) == G.GDN_EUNSUPPORTED
@@ -140,8 +152,8 @@ def test_rejects_bad_views(G):
 
 def test_rejects_small_workspace(G):
     p = prob(G)
-    assert status_of(G, p) == G.GDN_EWORKSPACE
-    assert status_of(G, p, workspace=None) == G.GDN_EWORKSPACE
+    assert bwd_status_of(G, p) == G.GDN_EWORKSPACE
+    assert bwd_status_of(G, p, workspace=None) == G.GDN_EWORKSPACE
 
 
 def test_rejects_varlen_inconsistency(G):
