@@ -88,16 +88,20 @@ __device__ __forceinline__ void invert_unit_lower(const float* L, float* T) {
 }
 
 // Grid nc_max * Hk, key head fastest (as the gradient kernel): workgroup c Hk + kh.
+// At least four waves per SIMD (registers for four workgroups per CU): the kernel is
+// latency-bound (triangular solves, barriers), and four workgroups per CU measured 12%
+// faster than three.
 template <typename TI, int C, int D>
-__global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_prep(Prob p) {
   using OT = TI;
   using LD = Swz<OT, D>;
   constexpr int NW = kPrepWaves, NT = kPrepThreads, LCF = C + 4, RT = C / 16;
   constexpr int KSD = ks_of<OT, D>();
-  // K and Q (direct loads) for the Gram products; afterwards the same bytes hold L, T and
-  // the staging tile of M.
+  // K and Q (direct loads) for the Gram products; afterwards the same bytes hold L and T,
+  // and before T the staging tile of M (so that four workgroups fit in a CU's LDS).
   constexpr int KQ_BYTES = 2 * C * D * (int)sizeof(OT);
-  constexpr int INV_BYTES = 2 * C * LCF * 4 + C * C * (int)sizeof(OT);
+  constexpr int INV_BYTES = 2 * C * LCF * 4;
+  static_assert(C * C * (int)sizeof(OT) <= C * LCF * 4, "M staging fits in T");
   __shared__ __align__(16) char smem[KQ_BYTES > INV_BYTES ? KQ_BYTES : INV_BYTES];
   constexpr int GH = NW;  // gate records formed per pass: one wave per value head
   __shared__ float sg[GH][C], sbeta[GH][C];
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
   OT* const sQ = sK + C * D;
   float* const sL = reinterpret_cast<float*>(smem);
   float* const sT = sL + C * LCF;
-  OT* const sM = reinterpret_cast<OT*>(sT + C * LCF);
+  OT* const sM = reinterpret_cast<OT*>(sT);
 
   const int kh = blockIdx.x % p.Hk, c = blockIdx.x / p.Hk;
   const ChunkInfo ci = p.chunks[c];
@@ -182,6 +186,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prob p) {
       const typename V::type* src = reinterpret_cast<const typename V::type*>(sM);
       for (int idx = threadIdx.x; idx < C * C / V::N; idx += NT) dst[idx] = src[idx];
     }
+    lds_barrier();  // M is out: its staging tile becomes T
     invert_unit_lower<C, LCF, NW>(sL, sT);
     {  // T with zeros above the diagonal blocks, 16-byte stores
       OT* dst = (OT*)p.sv_T + ch * C * C;
