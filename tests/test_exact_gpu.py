@@ -6,7 +6,9 @@
   bit-identical; dq/dk, which the library folds in float32 before one rounding,
   within tolerance of the host-side sum of the replicated heads;
 * two runs are bit-identical (no atomics anywhere);
-* split resume at a chunk boundary: [0, m) then [m, T) with S0 = S_m equals the whole run.
+* split resume at a chunk boundary: [0, m) then [m, T) with S0 = S_m equals the whole run;
+* the forward runs without a workspace, and the backward's outputs do not depend on what
+  its workspace holds on entry.
 """
 import numpy as np
 import pytest
@@ -116,3 +118,36 @@ def test_split_resume_at_chunk_boundary():
     for name in ("dq", "dk", "dv", "dg", "dbeta"):
         assert np.array_equal(np.concatenate([a[name], b[name]]), full[name]), name
     assert np.array_equal(a["dS0"], full["dS0"])
+
+
+def test_workspace_contents_ignored():
+    """The forward takes no workspace (NULL is accepted: its chunk table is saved in the
+    chunk states); the backward's outputs do not depend on what its workspace holds on
+    entry (zero bytes against all-one bytes, NaN in both storage types): bit-identical."""
+    import torch
+    import gated_delta_rule_34_amd as G
+    from gdn_gpu import problem, to_device
+
+    case = _case([200, 77], Hk=2, Hv=6, D=128, varlen=True)
+    d = to_device(case)
+    p = problem(case, d, None)
+    assert G.gdn_fwd_workspace_bytes(p) == 0
+    T, Hv, D, dev = case.T_total, case.Hv, case.Dk, d["v"].device
+    o = torch.empty(T, Hv, D, dtype=d["v"].dtype, device=dev)
+    S_T = torch.empty(case.N, Hv, D, D, dtype=torch.float32, device=dev)
+    states = torch.empty(G.gdn_chunk_state_bytes(p), dtype=torch.uint8, device=dev)
+    G.gdn_fwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T, states, None)
+    runs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((G.gdn_bwd_workspace_bytes(p),), fill, dtype=torch.uint8, device=dev)
+        dg = torch.empty(T, Hv, dtype=torch.float32, device=dev)
+        dbeta = torch.empty_like(dg)
+        dS0 = torch.empty(case.N, Hv, D, D, dtype=torch.float32, device=dev)
+        G.gdn_bwd(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], states, d["dO"], d["dST"], d["dq"],
+                  d["dk"], d["dv"], dg, dbeta, dS0, ws)
+        torch.cuda.synchronize()
+        runs.append({name: t.clone() for name, t in
+                     dict(dq=d["dq"], dk=d["dk"], dv=d["dv"], dg=dg, dbeta=dbeta, dS0=dS0).items()})
+    for name, t in runs[0].items():
+        assert torch.isfinite(t.float()).all(), name
+        assert torch.equal(t, runs[1][name]), name
