@@ -14,6 +14,9 @@ counter summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what the co
 reads for a plain copy of known size), or null when the kernels changed since those
 counters were taken. ``cpu_baseline`` times the float64 oracle on the whole batch (all
 four sequences, all 48 heads), fwd + bwd, on the host cores, repeated to at least 10 s.
+``decode`` is a separate measurement outside the timed training steps: one gdn_decode
+step for 256 rows at the same heads (float32 state pool, bf16 packed rows), with its
+kernel time, bytes and fraction of the HBM peak.
 
 Counter runs: ``--pmc-calib`` first copies a buffer of known size (the calibration
 dispatch); ``--summarize-pmc FETCH_DIR WRITE_DIR`` turns the two rocprofv3 result
@@ -158,6 +161,48 @@ PATH_BYTES_PER_TOKEN = 87168
 PATH_FLOPS_PER_TOKEN = 29.36e6
 
 
+def decode_bench(G, torch, steps, N=256, Hk=16, Hv=48, D=128):
+    """One decode step (gdn_decode) for a serving batch of N rows at the training heads:
+    bf16 q/k/v rows of a packed projection, float32 state pool of N slots (identity map),
+    timed over ``steps`` calls; the kernel time comes from the library's HIP events on the
+    launch stream. Bytes: the state read and written once, plus the rows in and out."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    width = 2 * Hk * D + Hv * D
+    buf = (0.1 * torch.randn(N, width, device=dev, generator=gen)).to(torch.bfloat16)
+    q, k, v = buf[:, : Hk * D], buf[:, Hk * D: 2 * Hk * D], buf[:, 2 * Hk * D:]
+    g = 0.5 + 0.5 * torch.rand(N, Hv, device=dev, generator=gen)
+    beta = torch.rand(N, Hv, device=dev, generator=gen)
+    state = 0.3 * torch.randn(N, Hv, D, D, device=dev, generator=gen)
+    o = torch.empty(N, Hv * D, dtype=torch.bfloat16, device=dev)
+    p = G.make_problem(N, N, Hk, Hv, D, T=1, dtype="bf16")
+
+    def step():
+        G.gdn_decode(p, q, k, v, g, beta, state, None, o)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    G.gdn_trace_enable(True)
+    G.gdn_trace_collect()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    G.gdn_trace_enable(False)
+    tr = G.gdn_trace_collect()
+    ms = start.elapsed_time(end) / steps
+    k_ms = tr["k_decode"][0] / tr["k_decode"][1]
+    nbytes = 2 * N * Hv * D * D * 4 + N * width * 2 + N * Hv * 8 + N * Hv * D * 2
+    return {"workload": f"{N} rows x 1 token, Hk{Hk} Hv{Hv} D{D}, bf16 packed rows, f32 state pool of {N} slots",
+            "rows_per_s": round(N / (ms / 1e3), 1), "ms_per_step": round(ms, 4), "kernel_ms": round(k_ms, 4),
+            "bytes": nbytes, "GB/s": round(nbytes / (k_ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (k_ms / 1e3) / PEAK["hbm"], 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +292,8 @@ def main():
     torch.cuda.synchronize()
     ms_fwd = start.elapsed_time(end) / args.steps
     print(f"[bench] timed: {ms_step:.3f} ms/step, fwd {ms_fwd:.3f} ms", file=sys.stderr, flush=True)
+    decode = decode_bench(G, torch, args.steps)
+    print(f"[bench] decode: {decode['kernel_ms']:.4f} ms per step, {decode['GB/s']} GB/s", file=sys.stderr, flush=True)
 
     n_chunks = T // C
     kernels = {k: round(v[0] / v[1], 4) for k, v in sorted(trace.items(), key=lambda kv: -kv[1][0])}
@@ -311,6 +358,7 @@ def main():
         "kernel_avg_ms": kernels,
         "kernels": per_kernel,
         "path_roofline": path,
+        "decode": decode,
     }
     print(json.dumps(line), flush=True)
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4, -5
 GDN_F32, GDN_BF16 = 0, 1
 
-EXPORTED = ("gdn_fwd", "gdn_bwd", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
+EXPORTED = ("gdn_fwd", "gdn_bwd", "gdn_decode", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
             "gdn_chunk_state_bytes", "gdn_strerror", "gdn_trace_enable", "gdn_trace_collect")
 
 
@@ -49,7 +49,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -m gated_delta_rule_34_amd.build, or __graft_entry__.build())")
+            "(python gated_delta_rule_34_amd/build.py, or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     prob = ctypes.POINTER(gdn_problem)
@@ -62,6 +62,8 @@ def _load():
     lib.gdn_bwd.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, P, P, I64, P,
                             P, I64, P, I64, P, I64, P, P, P, P, SZ, P]
     lib.gdn_bwd.restype = ctypes.c_int
+    lib.gdn_decode.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, ctypes.c_int32, P, P, I64, P]
+    lib.gdn_decode.restype = ctypes.c_int
     lib.gdn_trace_enable.argtypes = [ctypes.c_int]
     lib.gdn_trace_enable.restype = ctypes.c_int
     lib.gdn_trace_collect.argtypes = [ctypes.POINTER(gdn_trace_entry), ctypes.c_int]
@@ -169,6 +171,19 @@ def gdn_bwd(p, q, k, v, g, beta, S0, chunk_states, dO, dS_T, dq, dk, dv, dg, dbe
                       _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_bwd")
+
+
+def gdn_decode(p, q, k, v, g, beta, state, slot_idx, o, stream=None):
+    """Call gdn_decode: one token per row (p.T == 1, p.T_total == p.N); ``state`` is the
+    float32 [n_slots, Hv, Dk, Dv] pool updated in place, ``slot_idx`` an int32 [N] device
+    tensor of slots or None (row n -> slot n). Raises GdnError on a non-OK status."""
+    qk, vw = p.Hk * p.Dk, p.Hv * p.Dv
+    n_slots = 0 if state is None else int(state.shape[0])
+    st = _lib.gdn_decode(ctypes.byref(p), _ptr(q), _rs(q, qk), _ptr(k), _rs(k, qk), _ptr(v), _rs(v, vw),
+                         _ptr(g), _ptr(beta), _ptr(state), n_slots, _ptr(slot_idx), _ptr(o), _rs(o, vw),
+                         _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode")
 
 
 def _empty_bytes(n, device):

@@ -240,6 +240,49 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
+gdn_status gdn_decode(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                      const void* v, int64_t v_rs, const float* g, const float* beta, float* state,
+                      int32_t n_slots, const int32_t* slot_idx, void* o, int64_t o_rs, void* stream) {
+  if (!p) return GDN_EINVAL;
+  if (p->N < 0 || p->Hk <= 0 || p->Hv <= 0 || p->Hv % p->Hk) return GDN_EINVAL;
+  if (p->Dk <= 0 || p->Dv <= 0) return GDN_EINVAL;
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16) return GDN_EUNSUPPORTED;
+  if (p->Dk != p->Dv) return GDN_EUNSUPPORTED;
+  if (p->Dk != 16 && p->Dk != 32 && p->Dk != 64 && p->Dk != 128) return GDN_EUNSUPPORTED;
+  if (!std::isfinite(p->scale)) return GDN_EINVAL;
+  // one token per row: T = 1, T_total = N, no cu_seqlens (the chunk length is not used)
+  if (p->cu_seqlens || p->T != 1 || p->T_total != p->N) return GDN_EINVAL;
+  if ((int64_t)p->N * p->Hv > INT32_MAX) return GDN_EINVAL;
+  if (n_slots < 0 || (!slot_idx && n_slots < p->N)) return GDN_EINVAL;
+  const int es = p->dtype == GDN_BF16 ? 2 : 4;
+  const int64_t qkw = (int64_t)p->Hk * p->Dk, vw = (int64_t)p->Hv * p->Dv;
+  GDN_TRY(check_view(q, q_rs, qkw, es, p->N, 1));
+  GDN_TRY(check_view(k, k_rs, qkw, es, p->N, 1));
+  GDN_TRY(check_view(v, v_rs, vw, es, p->N, 1));
+  GDN_TRY(check_view(o, o_rs, vw, es, p->N, 1));
+  GDN_TRY(check_f32(g, p->N > 0));
+  GDN_TRY(check_f32(beta, p->N > 0));
+  GDN_TRY(check_f32(state, p->N > 0, 16));
+  GDN_TRY(check_f32(reinterpret_cast<const float*>(slot_idx), false));
+  if (p->N == 0) return GDN_OK;
+
+  gdn::DecArgs a{};
+  a.N = p->N;
+  a.Hv = p->Hv;
+  a.r = p->Hv / p->Hk;
+  a.D = p->Dk;
+  a.n_slots = n_slots;
+  a.scale = p->scale;
+  a.q = q; a.k = k; a.v = v;
+  a.q_rs = q_rs; a.k_rs = k_rs; a.v_rs = v_rs; a.o_rs = o_rs;
+  a.g = g; a.beta = beta;
+  a.state = state;
+  a.idx = slot_idx;
+  a.o = o;
+  const hipError_t e = gdn::launch_decode(a, p->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
 const char* gdn_strerror(int status) {
   switch (status) {
     case GDN_OK: return "success";

@@ -85,4 +85,17 @@ inline void traced(const char* name, hipStream_t s, const F& f) {
 hipError_t launch_forward(const Prob& p, int dtype, hipStream_t s);
 hipError_t launch_backward(const Prob& p, int dtype, hipStream_t s);
 
+// One decode step (gdn_decode.hip): N rows, one token each, state slots updated in place.
+struct DecArgs {
+  int N, Hv, r, D, n_slots;
+  float scale;
+  const void *q, *k, *v;  // row views, element row strides below
+  int64_t q_rs, k_rs, v_rs, o_rs;
+  const float *g, *beta;  // [N][Hv]
+  float* state;           // [n_slots][Hv][D][D]
+  const int* idx;         // [N] slot of each row, or nullptr (row n -> slot n)
+  void* o;
+};
+hipError_t launch_decode(const DecArgs& a, int dtype, hipStream_t s);
+
 }  // namespace gdn

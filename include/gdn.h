@@ -125,6 +125,30 @@ gdn_status gdn_bwd(const gdn_problem* p,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode: one step of the recurrence for each of p->N rows (one token per sequence),
+ * the per-token form of the lattice-inference gdn_backward.rs page, module doc "Forward
+ * recap" (the pages' inference path, gated_delta_net_step_fused, runs it token by token):
+ * for row n and value head h, with q, k of key head h / (Hv / Hk) and S the state of the
+ * row's slot,
+ *   kv = S^T k,  delta = beta (v - g kv),  S <- g S + k delta^T,  o = scale S^T q
+ * (o from the updated S). The problem holds one token per row: p->T == 1,
+ * p->T_total == p->N, p->cu_seqlens == NULL; p->chunk is not used.
+ * q, k [N rows][Hk*Dk], v [N rows][Hv*Dv] (dtype, row strides in elements, same
+ * alignment rules as gdn_fwd); g, beta [N][Hv] float32 (the gate value g itself).
+ * state: float32 [n_slots][Hv][Dk][Dv] (key-major), 16-byte aligned, read and
+ * overwritten in place. slot_idx: device int32 [N], the slot of each row, or NULL for
+ * row n -> slot n (then n_slots >= N is required). A row whose slot lies outside
+ * [0, n_slots) is skipped: its o row and every state are left untouched. Two rows with
+ * the same slot race (the result is undefined). o [N rows][Hv*Dv] (dtype). No
+ * workspace, no allocation; the call is enqueued on stream.
+ */
+gdn_status gdn_decode(const gdn_problem* p,
+                      const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                      const void* v, int64_t v_rs, const float* g, const float* beta,
+                      float* state, int32_t n_slots, const int32_t* slot_idx,
+                      void* o, int64_t o_rs, void* stream);
+
+/*
  * Per-kernel timing for benchmarks. While enabled (process-wide), every kernel that
  * gdn_fwd / gdn_bwd enqueue is bracketed by two HIP events recorded on the call's
  * stream (the events are created by the library on first use and reused; no device

@@ -11,7 +11,9 @@ differences of its own forward, a second formulation of the recurrence
 (S_t = g_t (I - beta_t k k^T) S_{t-1} + beta_t k v^T) differentiated by torch
 autograd, closed forms (beta = 0, T = 1, g = beta = 1 with orthonormal keys),
 the v_repeat / replication identity, linearity, zero upstream gradient and split
-resume. No function here is "parity unpinned".
+resume. ``gdn_decode`` (one step per row, state slots) is the forward over one-token
+sequences; its own pins replay the hand-worked example token by token and check the
+slot map against per-row forwards. No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -118,6 +120,28 @@ def gdn_bwd(cu, q, k, v, g, beta, S0, dO, dST, scale=None, nthreads=None, lib=No
     if rc != 0:
         raise RuntimeError(f"oracle_gdn_bwd failed ({rc})")
     return out
+
+
+def gdn_decode(q, k, v, g, beta, state, slot_idx=None, scale=None, nthreads=None, lib=None):
+    """One decode step: row n is one token of its own sequence, whose state is
+    ``state[slot_idx[n]]`` (slot n when ``slot_idx`` is None); a row whose slot lies outside
+    [0, n_slots) is skipped. This is the forward above over N one-token sequences (the
+    per-token recurrence of the "Forward recap" module doc, one step), with no arithmetic
+    of its own. q, k [N, Hk, Dk]; v [N, Hv, Dv]; g, beta [N, Hv]; state [n_slots, Hv, Dk, Dv].
+    Returns (o [N, Hv, Dv], NaN on skipped rows; the updated copy of ``state``)."""
+    N = q.shape[0]
+    n_slots = state.shape[0]
+    slots = np.arange(N) if slot_idx is None else np.asarray(slot_idx, dtype=np.int64)
+    rows = np.array([n for n in range(N) if 0 <= slots[n] < n_slots], dtype=np.int64)
+    assert len(set(slots[rows].tolist())) == len(rows), "two rows share a slot"
+    o = np.full((N,) + v.shape[1:], np.nan)
+    new = np.array(state, dtype=np.float64, copy=True)
+    if len(rows):
+        cu = np.arange(len(rows) + 1, dtype=np.int64)
+        o_r, ST = gdn_fwd(cu, q[rows], k[rows], v[rows], g[rows], beta[rows], new[slots[rows]], scale, nthreads, lib)
+        o[rows] = o_r
+        new[slots[rows]] = ST
+    return o, new
 
 
 def run_case(case, backward=True, nthreads=None, lib=None, seqs=None, key_heads=None):

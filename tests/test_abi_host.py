@@ -18,9 +18,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def G():
     lib = os.path.join(ROOT, "gated_delta_rule_34_amd", "libgdn.so")
     if not os.path.exists(lib):
-        from gated_delta_rule_34_amd.build import build
+        import importlib.util
 
-        build()
+        spec = importlib.util.spec_from_file_location("_gdn_build", os.path.join(ROOT, "gated_delta_rule_34_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import gated_delta_rule_34_amd as G
 
     return G
@@ -148,6 +151,32 @@ def test_rejects_bad_views(G):
     assert status_of(G, p, g=FakeTensor(0x40002, T, 48)) == G.GDN_EALIGN
     assert status_of(G, p, beta=None) == G.GDN_EINVAL
     assert status_of(G, p, chunk_states=None) == G.GDN_EINVAL
+
+
+def decode_status_of(G, p, n_slots=None, **over):
+    N = p.N
+    a = dict(q=FakeTensor(0x10000, N, p.Hk * p.Dk, 10240), k=FakeTensor(0x20000, N, p.Hk * p.Dk, 10240),
+             v=FakeTensor(0x30000, N, p.Hv * p.Dv, 10240), g=FakeTensor(0x40000, N, p.Hv),
+             beta=FakeTensor(0x50000, N, p.Hv), state=FakeTensor(0x70000, N if n_slots is None else n_slots, 1),
+             slot_idx=None, o=FakeTensor(0x60000, N, p.Hv * p.Dv))
+    a.update(over)
+    with pytest.raises(G.GdnError) as e:
+        G.gdn_decode(p, a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["slot_idx"], a["o"], stream=0)
+    return e.value.status
+
+
+def test_decode_rejects_bad_arguments(G):
+    one = dict(N=4, T_total=4, T=1)
+    assert decode_status_of(G, prob(G, N=4, T_total=8, T=2)) == G.GDN_EINVAL  # one token per row
+    assert decode_status_of(G, prob(G, **one), n_slots=3) == G.GDN_EINVAL  # no slot map: slots >= rows
+    assert decode_status_of(G, prob(G, **one, D=96)) == G.GDN_EUNSUPPORTED
+    assert decode_status_of(G, prob(G, **one, Hv=47)) == G.GDN_EINVAL
+    assert decode_status_of(G, prob(G, **one), state=FakeTensor(0x70004, 4, 1)) == G.GDN_EALIGN
+    assert decode_status_of(G, prob(G, **one), state=None) == G.GDN_EINVAL
+    assert decode_status_of(G, prob(G, **one), o=FakeTensor(0x60002, 4, 6144)) == G.GDN_EALIGN
+    p = prob(G, **one)
+    p.cu_seqlens = 0x90000
+    assert decode_status_of(G, p) == G.GDN_EINVAL
 
 
 def test_rejects_small_workspace(G):

@@ -345,6 +345,44 @@ def test_golden_hand_worked_example(oracle_lib):
     assert all(v < 1e-14 for v in errs.values()), errs
 
 
+def test_decode_replays_the_hand_worked_example():
+    """The decode step, called once per token with the state carried in its slot,
+    reproduces the hand-worked example's o (token by token) and final state."""
+    fx, x, e = _golden("scalar_state_two_heads.json")
+    sc = float(Fraction(fx["scale"]))
+    state = x["S0"].copy()
+    for t in range(2):
+        row = slice(t, t + 1)
+        o, state = oracle.gdn_decode(x["q"][row], x["k"][row], x["v"][row], x["g"][row], x["beta"][row], state,
+                                     None, sc)
+        assert np.max(np.abs(o[0] - e["o"][t])) < 1e-14, t
+    assert np.max(np.abs(state - e["S_T"])) < 1e-14
+
+
+def test_decode_slot_map():
+    """Decode rows reach their states through the slot map: each row equals a one-token
+    forward from its slot; rows whose slot is outside [0, n_slots) are skipped (NaN o),
+    and the slots no row names keep their values."""
+    rng = np.random.default_rng(5)
+    N, Hk, Hv, D, n_slots = 6, 2, 4, 8, 9
+    q, k = rng.standard_normal((N, Hk, D)), rng.standard_normal((N, Hk, D)) / np.sqrt(D)
+    v = rng.standard_normal((N, Hv, D))
+    g, beta = rng.uniform(0.5, 1.0, (N, Hv)), rng.uniform(0.0, 1.0, (N, Hv))
+    state = rng.standard_normal((n_slots, Hv, D, D))
+    slots = np.array([7, 2, -1, 0, 9, 4])
+    o, new = oracle.gdn_decode(q, k, v, g, beta, state, slots)
+    one = np.array([0, 1], dtype=np.int64)
+    for n in range(N):
+        s_ = slots[n]
+        if not 0 <= s_ < n_slots:
+            assert np.isnan(o[n]).all()
+            continue
+        o1, st1 = oracle.gdn_fwd(one, q[n:n + 1], k[n:n + 1], v[n:n + 1], g[n:n + 1], beta[n:n + 1], state[s_:s_ + 1])
+        assert np.array_equal(o[n], o1[0]) and np.array_equal(new[s_], st1[0]), n
+    rest = [s_ for s_ in range(n_slots) if s_ not in (7, 2, 0, 4)]
+    assert np.array_equal(new[rest], state[rest])
+
+
 def _pins_fail(lib):
     """Run a cheap subset of the pins against an oracle build; return names that failed."""
     failed = []
