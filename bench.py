@@ -16,7 +16,8 @@ counters were taken. ``cpu_baseline`` times the float64 oracle on the whole batc
 four sequences, all 48 heads), fwd + bwd, on the host cores, repeated to at least 10 s.
 ``decode`` is a separate measurement outside the timed training steps: one gdn_decode
 step for 256 rows at the same heads (float32 state pool, bf16 packed rows), with its
-kernel time, bytes and fraction of the HBM peak.
+kernel time, bytes and fraction of the HBM peak. ``conv1d`` likewise times the causal
+conv1d + SiLU forward and input gradient over the same packed projection.
 
 Counter runs: ``--pmc-calib`` first copies a buffer of known size (the calibration
 dispatch); ``--summarize-pmc FETCH_DIR WRITE_DIR`` turns the two rocprofv3 result
@@ -203,6 +204,39 @@ def decode_bench(G, torch, steps, N=256, Hk=16, Hv=48, D=128):
             "hbm_frac": round(nbytes / (k_ms / 1e3) / PEAK["hbm"], 4)}
 
 
+def conv_bench(G, torch, steps, rows=16384, ch=10240, K=4):
+    """Causal conv1d + SiLU forward and input gradient over the training shape's packed
+    projection (16384 rows x 10240 channels, bf16, 4 sequences of 4096, K = 4), timed over
+    ``steps`` calls each with the library's HIP events. Bytes: x read and y written
+    (forward); x, dy read and dx written (backward)."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    x = torch.randn(rows, ch, device=dev, generator=gen).to(torch.bfloat16)
+    dy = torch.randn(rows, ch, device=dev, generator=gen).to(torch.bfloat16)
+    w = torch.rand(ch, K, device=dev, generator=gen) - 0.5
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    p = G.make_conv_problem(4, rows, ch, K, T=rows // 4, dtype="bf16")
+    for _ in range(3):
+        G.gdn_conv1d_silu_fwd(p, x, w, y)
+        G.gdn_conv1d_silu_bwd(p, x, w, dy, dx)
+    torch.cuda.synchronize()
+    G.gdn_trace_enable(True)
+    G.gdn_trace_collect()
+    for _ in range(steps):
+        G.gdn_conv1d_silu_fwd(p, x, w, y)
+        G.gdn_conv1d_silu_bwd(p, x, w, dy, dx)
+    torch.cuda.synchronize()
+    G.gdn_trace_enable(False)
+    tr = G.gdn_trace_collect()
+    out = {"workload": f"{rows} rows x {ch} channels (4 x {rows // 4}), K {K}, bf16"}
+    for name, nb in (("k_conv_fwd", 2 * rows * ch * 2), ("k_conv_bwd", 3 * rows * ch * 2)):
+        ms = tr[name][0] / tr[name][1]
+        out[name] = {"ms": round(ms, 4), "bytes": nb, "GB/s": round(nb / (ms / 1e3) / 1e9, 1),
+                     "hbm_frac": round(nb / (ms / 1e3) / PEAK["hbm"], 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +328,9 @@ def main():
     print(f"[bench] timed: {ms_step:.3f} ms/step, fwd {ms_fwd:.3f} ms", file=sys.stderr, flush=True)
     decode = decode_bench(G, torch, args.steps)
     print(f"[bench] decode: {decode['kernel_ms']:.4f} ms per step, {decode['GB/s']} GB/s", file=sys.stderr, flush=True)
+    conv = conv_bench(G, torch, args.steps)
+    print(f"[bench] conv1d: fwd {conv['k_conv_fwd']['GB/s']} GB/s, bwd {conv['k_conv_bwd']['GB/s']} GB/s",
+          file=sys.stderr, flush=True)
 
     n_chunks = T // C
     kernels = {k: round(v[0] / v[1], 4) for k, v in sorted(trace.items(), key=lambda kv: -kv[1][0])}
@@ -359,6 +396,7 @@ def main():
         "kernels": per_kernel,
         "path_roofline": path,
         "decode": decode,
+        "conv1d": conv,
     }
     print(json.dumps(line), flush=True)
 

@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4, -5
 GDN_F32, GDN_BF16 = 0, 1
 
-EXPORTED = ("gdn_fwd", "gdn_bwd", "gdn_decode", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
-            "gdn_chunk_state_bytes", "gdn_strerror", "gdn_trace_enable", "gdn_trace_collect")
+EXPORTED = ("gdn_fwd", "gdn_bwd", "gdn_decode", "gdn_conv1d_silu_fwd", "gdn_conv1d_silu_bwd",
+            "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_chunk_state_bytes", "gdn_strerror",
+            "gdn_trace_enable", "gdn_trace_collect")
 
 
 class gdn_trace_entry(ctypes.Structure):
@@ -41,6 +42,18 @@ class gdn_problem(ctypes.Structure):
         ("Dv", ctypes.c_int32),
         ("chunk", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class gdn_conv_problem(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("T_total", ctypes.c_int64),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("channels", ctypes.c_int32),
+        ("kernel_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
     ]
 
@@ -64,6 +77,11 @@ def _load():
     lib.gdn_bwd.restype = ctypes.c_int
     lib.gdn_decode.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, ctypes.c_int32, P, P, I64, P]
     lib.gdn_decode.restype = ctypes.c_int
+    cprob = ctypes.POINTER(gdn_conv_problem)
+    lib.gdn_conv1d_silu_fwd.argtypes = [cprob, P, I64, P, P, I64, P]
+    lib.gdn_conv1d_silu_fwd.restype = ctypes.c_int
+    lib.gdn_conv1d_silu_bwd.argtypes = [cprob, P, I64, P, P, I64, P, I64, P]
+    lib.gdn_conv1d_silu_bwd.restype = ctypes.c_int
     lib.gdn_trace_enable.argtypes = [ctypes.c_int]
     lib.gdn_trace_enable.restype = ctypes.c_int
     lib.gdn_trace_collect.argtypes = [ctypes.POINTER(gdn_trace_entry), ctypes.c_int]
@@ -171,6 +189,41 @@ def gdn_bwd(p, q, k, v, g, beta, S0, chunk_states, dO, dS_T, dq, dk, dv, dg, dbe
                       _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_bwd")
+
+
+def make_conv_problem(N, T_total, channels, kernel_size, *, T=None, cu_seqlens=None, dtype="bf16"):
+    """Build a gdn_conv_problem. ``cu_seqlens``: device int32 tensor [N + 1] or None."""
+    p = gdn_conv_problem()
+    p.N, p.T_total = int(N), int(T_total)
+    p.T = int(T if T is not None else (T_total // N if (cu_seqlens is None and N) else 0))
+    p.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
+    p.channels, p.kernel_size = int(channels), int(kernel_size)
+    p.dtype = {"f32": GDN_F32, "bf16": GDN_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    return p
+
+
+def _rows(t):
+    """Row stride (elements) of a [rows, channels] view with contiguous rows."""
+    if t is None:
+        return 0
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a [rows, channels] view with contiguous rows")
+    return t.stride(0)
+
+
+def gdn_conv1d_silu_fwd(p, x, w, y, stream=None):
+    """Call gdn_conv1d_silu_fwd: y = SiLU(causal depthwise conv1d(x, w)) per sequence."""
+    st = _lib.gdn_conv1d_silu_fwd(ctypes.byref(p), _ptr(x), _rows(x), _ptr(w), _ptr(y), _rows(y), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_conv1d_silu_fwd")
+
+
+def gdn_conv1d_silu_bwd(p, x, w, dy, dx, stream=None):
+    """Call gdn_conv1d_silu_bwd: dx from dy (the input gradient; the weights are fixed)."""
+    st = _lib.gdn_conv1d_silu_bwd(ctypes.byref(p), _ptr(x), _rows(x), _ptr(w), _ptr(dy), _rows(dy), _ptr(dx),
+                                  _rows(dx), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_conv1d_silu_bwd")
 
 
 def gdn_decode(p, q, k, v, g, beta, state, slot_idx, o, stream=None):

@@ -151,6 +151,34 @@ void fill_common(gdn::Prob& P, const gdn_problem* p) {
   P.cu = p->cu_seqlens;
 }
 
+gdn_status conv_common(const gdn_conv_problem* p, const void* x, int64_t x_rs, const float* w, gdn::ConvArgs& a) {
+  if (!p) return GDN_EINVAL;
+  if (p->N < 0 || p->T_total < 0 || p->channels <= 0 || p->channels % 8) return GDN_EINVAL;
+  if (p->kernel_size < 1 || p->kernel_size > 4) return GDN_EUNSUPPORTED;
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16) return GDN_EUNSUPPORTED;
+  if (!p->cu_seqlens) {
+    if (p->T < 0 || (int64_t)p->N * p->T != p->T_total) return GDN_EINVAL;
+  } else if (p->N == 0 && p->T_total != 0) {
+    return GDN_EINVAL;
+  }
+  if (p->channels / 8 > 65535LL * 256 || p->T_total > INT32_MAX) return GDN_EINVAL;  // grid limits
+  if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
+  const int es = p->dtype == GDN_BF16 ? 2 : 4;
+  GDN_TRY(check_view(x, x_rs, p->channels, es, p->T_total, 1));
+  GDN_TRY(check_f32(w, p->T_total > 0));
+  a = gdn::ConvArgs{};
+  a.N = p->N;
+  a.T = p->cu_seqlens ? 0 : p->T;
+  a.ch = p->channels;
+  a.K = p->kernel_size;
+  a.rows = p->T_total;
+  a.cu = p->cu_seqlens;
+  a.w = w;
+  a.x = x;
+  a.x_rs = x_rs;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -280,6 +308,33 @@ gdn_status gdn_decode(const gdn_problem* p, const void* q, int64_t q_rs, const v
   a.idx = slot_idx;
   a.o = o;
   const hipError_t e = gdn::launch_decode(a, p->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_conv1d_silu_fwd(const gdn_conv_problem* p, const void* x, int64_t x_rs, const float* w, void* y,
+                               int64_t y_rs, void* stream) {
+  gdn::ConvArgs a;
+  GDN_TRY(conv_common(p, x, x_rs, w, a));
+  const int es = p->dtype == GDN_BF16 ? 2 : 4;
+  GDN_TRY(check_view(y, y_rs, p->channels, es, p->T_total, 1));
+  a.y = y;
+  a.y_rs = y_rs;
+  const hipError_t e = gdn::launch_conv(a, p->dtype, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_conv1d_silu_bwd(const gdn_conv_problem* p, const void* x, int64_t x_rs, const float* w,
+                               const void* dy, int64_t dy_rs, void* dx, int64_t dx_rs, void* stream) {
+  gdn::ConvArgs a;
+  GDN_TRY(conv_common(p, x, x_rs, w, a));
+  const int es = p->dtype == GDN_BF16 ? 2 : 4;
+  GDN_TRY(check_view(dy, dy_rs, p->channels, es, p->T_total, 1));
+  GDN_TRY(check_view(dx, dx_rs, p->channels, es, p->T_total, 1));
+  a.dy = dy;
+  a.dy_rs = dy_rs;
+  a.dx = dx;
+  a.dx_rs = dx_rs;
+  const hipError_t e = gdn::launch_conv(a, p->dtype, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -1,0 +1,254 @@
+// gdn_conv.hip -- causal depthwise conv1d + SiLU over the packed q/k/v projection, forward
+// and input gradient, on gfx950.
+//
+// Per channel ch of a row (the packed projection row of a token) and kernel size K, with
+// the K - 1 previous rows of the same sequence as the conv buffer (zeros before the
+// sequence's first row), as the lattice-inference gdn_backward.rs page computes it
+// (gdn_forward_save's conv1d_silu_fwd, and step 5 of gdn_backward, "Backward through
+// conv1d + SiLU"):
+//   pre[t] = sum_{j < K} w[ch][j] x[t - (K - 1) + j],  y[t] = SiLU(pre[t]) = pre sigma(pre)
+//   dpre[t] = dy[t] SiLU'(pre[t]),  SiLU'(z) = sigma(z) (1 + z (1 - sigma(z)))
+//   dx[t] = sum_{lag < K} w[ch][K - 1 - lag] dpre[t + lag]   (t + lag in the same sequence)
+// The pages keep the conv weights fixed (no weight gradient), and so does this file.
+//
+// Each thread owns 8 adjacent channels (one 16-byte bf16 piece of the row, two for
+// float32) and a run of RUN consecutive rows, streaming along time with the window of
+// the last K - 1 inputs (and, backward, the last K values of dpre) in registers: every
+// input and output element crosses HBM once, up to the K - 1 halo rows at a run's ends.
+// The threads of a wave cover 512 consecutive channels, so each row access is one
+// contiguous 1 KB (bf16) piece. Plain VALU streaming work, bound by HBM.
+#include "gdn_common.h"
+
+namespace gdn {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvRun = 32;  // rows per thread
+
+// Rows [lo, hi) of the sequence that holds row t.
+__device__ __forceinline__ void conv_seq(const ConvArgs& a, int64_t t, int64_t& lo, int64_t& hi) {
+  if (!a.cu) {
+    lo = t / a.T * a.T;
+    hi = lo + a.T;
+    return;
+  }
+  int l = 0, r = a.N;  // largest n with cu[n] <= t (empty sequences skipped by the search)
+  while (r - l > 1) {
+    const int m = (l + r) >> 1;
+    if (a.cu[m] <= t) l = m; else r = m;
+  }
+  lo = a.cu[l];
+  hi = a.cu[l + 1];
+  while (hi <= t && l + 1 < a.N) {  // equal offsets (empty sequences) before t's own
+    ++l;
+    lo = a.cu[l];
+    hi = a.cu[l + 1];
+  }
+  // (hi <= t still means cu[N] < T_total, a caller error: the row is then treated as the
+  // first of a sequence, and nothing outside cu[0 .. N] is read)
+}
+
+struct F8 {
+  float v[8];
+};
+
+template <typename TI> __device__ __forceinline__ F8 ld8(const TI* p) {
+  F8 r;
+  if constexpr (sizeof(TI) == 2) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.v[i] = (float)x[i];
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.v[i] = a[i];
+      r.v[4 + i] = b[i];
+    }
+  }
+  return r;
+}
+
+template <typename TI> __device__ __forceinline__ void st8(TI* p, const F8& x) {
+  if constexpr (sizeof(TI) == 2) {
+    bf16x8 y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = (__bf16)x.v[i];
+    *reinterpret_cast<bf16x8*>(p) = y;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x.v[0], x.v[1], x.v[2], x.v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x.v[4], x.v[5], x.v[6], x.v[7]};
+  }
+}
+
+__device__ __forceinline__ float sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }
+
+// Grid (rows / kConvRun, channel groups / kConvThreads).
+template <typename TI, int K>
+__global__ __launch_bounds__(kConvThreads) void k_conv_fwd(ConvArgs a) {
+  const int cg = blockIdx.y * kConvThreads + threadIdx.x;
+  if (cg * 8 >= a.ch) return;
+  const int c0 = cg * 8;
+  const int64_t t0 = (int64_t)blockIdx.x * kConvRun;
+  const int64_t t1 = t0 + kConvRun < a.rows ? t0 + kConvRun : a.rows;
+  float w[K][8];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[j][i] = a.w[(int64_t)(c0 + i) * K + j];
+  int64_t lo, hi;
+  conv_seq(a, t0, lo, hi);
+  const TI* __restrict__ x = (const TI*)a.x + c0;
+  TI* __restrict__ y = (TI*)a.y + c0;
+  F8 win[K > 1 ? K - 1 : 1];  // x[t - (K - 1) + j], j < K - 1 (zeros before the sequence)
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) {
+    const int64_t s = t0 - (K - 1) + j;
+    if (s >= lo) {
+      win[j] = ld8(x + s * a.x_rs);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+    }
+  }
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t >= hi) {  // the next sequence starts at t: its buffer is empty
+      conv_seq(a, t, lo, hi);
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+    }
+    const F8 xt = ld8(x + t * a.x_rs);
+    F8 out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float z = w[K - 1][i] * xt.v[i];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) z += w[j][i] * win[j].v[i];
+      out.v[i] = z * sigmoid(z);
+    }
+    st8(y + t * a.y_rs, out);
+#pragma unroll
+    for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+    if constexpr (K > 1) win[K - 2] = xt;
+  }
+}
+
+// Grid as the forward. Sweeps rows t0 .. t1 + K - 2: at row u it forms dpre[u] (from the
+// input window and dy[u]) and, once dpre[t .. t + K - 1] are known, dx[t] for t = u - K + 1.
+template <typename TI, int K>
+__global__ __launch_bounds__(kConvThreads) void k_conv_bwd(ConvArgs a) {
+  const int cg = blockIdx.y * kConvThreads + threadIdx.x;
+  if (cg * 8 >= a.ch) return;
+  const int c0 = cg * 8;
+  const int64_t t0 = (int64_t)blockIdx.x * kConvRun;
+  const int64_t t1 = t0 + kConvRun < a.rows ? t0 + kConvRun : a.rows;
+  float w[K][8];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[j][i] = a.w[(int64_t)(c0 + i) * K + j];
+  int64_t lo, hi;
+  conv_seq(a, t0, lo, hi);
+  const TI* __restrict__ x = (const TI*)a.x + c0;
+  const TI* __restrict__ dy = (const TI*)a.dy + c0;
+  TI* __restrict__ dx = (TI*)a.dx + c0;
+  F8 win[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) {
+    const int64_t s = t0 - (K - 1) + j;
+    if (s >= lo) {
+      win[j] = ld8(x + s * a.x_rs);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+    }
+  }
+  // dp[l] = dpre[u - (K - 1) + l]; hp[l] = end of that row's sequence (0 for rows before
+  // the run: they are never summed into a dx of the run)
+  F8 dp[K];
+  int64_t hp[K];
+#pragma unroll
+  for (int l = 0; l < K; ++l) {
+    hp[l] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dp[l].v[i] = 0.f;
+  }
+  const int64_t uend = t1 + K - 1 < a.rows ? t1 + K - 1 : a.rows;
+  for (int64_t u = t0; u < t1 + K - 1; ++u) {
+#pragma unroll
+    for (int l = 0; l + 1 < K; ++l) {
+      dp[l] = dp[l + 1];
+      hp[l] = hp[l + 1];
+    }
+    if (u < uend) {
+      if (u >= hi) {
+        conv_seq(a, u, lo, hi);
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+      }
+      const F8 xu = ld8(x + u * a.x_rs);
+      const F8 gu = ld8(dy + u * a.dy_rs);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float z = w[K - 1][i] * xu.v[i];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) z += w[j][i] * win[j].v[i];
+        const float sg = sigmoid(z);
+        dp[K - 1].v[i] = gu.v[i] * sg * (1.f + z * (1.f - sg));
+      }
+      hp[K - 1] = hi;
+#pragma unroll
+      for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+      if constexpr (K > 1) win[K - 2] = xu;
+    } else {  // past the last row: nothing to add
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dp[K - 1].v[i] = 0.f;
+      hp[K - 1] = 0;
+    }
+    const int64_t t = u - (K - 1);
+    if (t >= t0 && t < t1) {  // dx[t]: dp[0] is row t itself
+      const int64_t end = hp[0];
+      F8 out;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int l = 0; l < K; ++l)
+          if (t + l < end) s += w[K - 1 - l][i] * dp[l].v[i];
+        out.v[i] = s;
+      }
+      st8(dx + t * a.dx_rs, out);
+    }
+  }
+}
+
+template <typename TI, int K>
+static hipError_t conv_k(const ConvArgs& a, bool backward, hipStream_t s) {
+  const dim3 grid((unsigned)((a.rows + kConvRun - 1) / kConvRun), (unsigned)((a.ch / 8 + kConvThreads - 1) / kConvThreads));
+  if (backward)
+    traced("k_conv_bwd", s, [&] { k_conv_bwd<TI, K><<<grid, kConvThreads, 0, s>>>(a); });
+  else
+    traced("k_conv_fwd", s, [&] { k_conv_fwd<TI, K><<<grid, kConvThreads, 0, s>>>(a); });
+  return hipGetLastError();
+}
+
+template <typename TI>
+static hipError_t conv_t(const ConvArgs& a, bool backward, hipStream_t s) {
+  switch (a.K) {
+    case 1: return conv_k<TI, 1>(a, backward, s);
+    case 2: return conv_k<TI, 2>(a, backward, s);
+    case 3: return conv_k<TI, 3>(a, backward, s);
+    case 4: return conv_k<TI, 4>(a, backward, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv(const ConvArgs& a, int dtype, bool backward, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  return dtype == 0 ? conv_t<float>(a, backward, s) : conv_t<__bf16>(a, backward, s);
+}
+
+}  // namespace gdn

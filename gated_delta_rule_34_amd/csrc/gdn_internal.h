@@ -98,4 +98,18 @@ struct DecArgs {
 };
 hipError_t launch_decode(const DecArgs& a, int dtype, hipStream_t s);
 
+// Causal depthwise conv1d + SiLU over packed rows (gdn_conv.hip): forward, or the input
+// gradient when backward is set.
+struct ConvArgs {
+  int N, T, ch, K;   // sequences, rows per sequence when cu is null, channels, kernel size
+  int64_t rows;      // T_total
+  const int* cu;     // [N + 1] row offsets, or nullptr
+  const float* w;    // [ch][K]
+  const void* x;
+  void *y, *dx;
+  const void* dy;
+  int64_t x_rs, y_rs, dy_rs, dx_rs;
+};
+hipError_t launch_conv(const ConvArgs& a, int dtype, bool backward, hipStream_t s);
+
 }  // namespace gdn

@@ -149,6 +149,38 @@ gdn_status gdn_decode(const gdn_problem* p,
                       void* o, int64_t o_rs, void* stream);
 
 /*
+ * Causal depthwise conv1d + SiLU over rows of `channels` values (the layer's packed q/k/v
+ * projection: channels = 2 Hk Dk + Hv Dv), the step before the recurrence, as the
+ * lattice-inference gdn_backward.rs page computes it (conv1d_silu_fwd in gdn_forward_save;
+ * step 5 of gdn_backward, "Backward through conv1d + SiLU"). For channel c and row t of a
+ * sequence, with w [channels][kernel_size] float32 and the rows before the sequence's first
+ * taken as zero (each sequence starts with an empty conv buffer):
+ *   pre[t] = sum_{j < K} w[c][j] x[t - (K - 1) + j],   y[t] = pre[t] sigmoid(pre[t])
+ * Backward (input gradient only; the pages keep the conv weights fixed):
+ *   dpre[t] = dy[t] sigmoid(pre[t]) (1 + pre[t] (1 - sigmoid(pre[t])))
+ *   dx[t] = sum_{l < K} w[c][K - 1 - l] dpre[t + l]   (rows t + l of the same sequence)
+ * Sequences as in gdn_problem (N equal-length sequences of T rows, or cu_seqlens).
+ * channels: a positive multiple of 8; kernel_size 1..4 (GDN_EUNSUPPORTED otherwise).
+ * x, y, dy, dx: [T_total rows][channels] in dtype, row strides in elements, 16-byte
+ * aligned rows (as for gdn_fwd); y must not overlap x, dx must not overlap x or dy.
+ * No workspace, no allocation; enqueued on stream.
+ */
+typedef struct {
+  int32_t N;                  /* sequences */
+  int32_t T;                  /* rows per sequence when cu_seqlens is NULL */
+  int64_t T_total;            /* rows */
+  const int32_t* cu_seqlens;  /* device int32 [N + 1], or NULL */
+  int32_t channels;           /* values per row */
+  int32_t kernel_size;        /* K */
+  int32_t dtype;              /* gdn_dtype of x, y, dy, dx */
+} gdn_conv_problem;
+
+gdn_status gdn_conv1d_silu_fwd(const gdn_conv_problem* p, const void* x, int64_t x_rs, const float* w,
+                               void* y, int64_t y_rs, void* stream);
+gdn_status gdn_conv1d_silu_bwd(const gdn_conv_problem* p, const void* x, int64_t x_rs, const float* w,
+                               const void* dy, int64_t dy_rs, void* dx, int64_t dx_rs, void* stream);
+
+/*
  * Per-kernel timing for benchmarks. While enabled (process-wide), every kernel that
  * gdn_fwd / gdn_bwd enqueue is bracketed by two HIP events recorded on the call's
  * stream (the events are created by the library on first use and reused; no device

@@ -179,6 +179,34 @@ def test_decode_rejects_bad_arguments(G):
     assert decode_status_of(G, p) == G.GDN_EINVAL
 
 
+def conv_status_of(G, p, backward=False, **over):
+    R = p.T_total
+    a = dict(x=FakeTensor(0x10000, R, p.channels, 10240), w=FakeTensor(0x20000, p.channels, p.kernel_size),
+             y=FakeTensor(0x30000, R, p.channels, 10240), dy=FakeTensor(0x40000, R, p.channels, 10240),
+             dx=FakeTensor(0x50000, R, p.channels, 10240))
+    a.update(over)
+    with pytest.raises(G.GdnError) as e:
+        if backward:
+            G.gdn_conv1d_silu_bwd(p, a["x"], a["w"], a["dy"], a["dx"], stream=0)
+        else:
+            G.gdn_conv1d_silu_fwd(p, a["x"], a["w"], a["y"], stream=0)
+    return e.value.status
+
+
+def test_conv_rejects_bad_arguments(G):
+    cp = lambda **kw: G.make_conv_problem(**{**dict(N=2, T_total=64, channels=10240, kernel_size=4, T=32), **kw})
+    assert conv_status_of(G, cp(kernel_size=5)) == G.GDN_EUNSUPPORTED
+    assert conv_status_of(G, cp(kernel_size=0)) == G.GDN_EUNSUPPORTED
+    assert conv_status_of(G, cp(channels=10236)) == G.GDN_EINVAL  # not a multiple of 8
+    assert conv_status_of(G, cp(T=31)) == G.GDN_EINVAL  # N * T != T_total
+    assert conv_status_of(G, cp(dtype=7)) == G.GDN_EUNSUPPORTED
+    assert conv_status_of(G, cp(), x=FakeTensor(0x10002, 64, 10240, 10240)) == G.GDN_EALIGN
+    assert conv_status_of(G, cp(), w=None) == G.GDN_EINVAL
+    assert conv_status_of(G, cp(), y=FakeTensor(0x30000, 64, 10240, 1000)) == G.GDN_EINVAL  # stride < width
+    assert conv_status_of(G, cp(), backward=True, dy=None) == G.GDN_EINVAL
+    assert conv_status_of(G, cp(), backward=True, dx=FakeTensor(0x50004, 64, 10240, 10240)) == G.GDN_EALIGN
+
+
 def test_rejects_small_workspace(G):
     p = prob(G)
     assert bwd_status_of(G, p) == G.GDN_EWORKSPACE

@@ -411,3 +411,52 @@ def test_planted_mistake_is_caught(oracle_lib, plant):
 
 def test_unplanted_passes_the_same_pins(oracle_lib):
     assert _pins_fail(oracle.LIB) == []
+
+
+# --- causal depthwise conv1d + SiLU (oracle/conv.py)
+
+def _conv_case(seed=3, lens=(10, 0, 35, 1), ch=24, K=4):
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = rng.standard_normal((int(cu[-1]), ch))
+    w = rng.uniform(-0.8, 0.8, (ch, K))
+    dy = rng.standard_normal(x.shape)
+    return cu, x, w, dy
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_conv_matches_torch_conv1d_and_autograd(K):
+    """Per sequence, the oracle equals torch's grouped conv1d with K - 1 zeros of left
+    padding followed by silu, and its input gradient equals torch autograd of that."""
+    import torch
+    from oracle.conv import conv1d_silu_bwd, conv1d_silu_fwd
+
+    cu, x, w, dy = _conv_case(K=K)
+    y = conv1d_silu_fwd(cu, x, w)
+    dx = conv1d_silu_bwd(cu, x, w, dy)
+    wt = torch.from_numpy(w)[:, None, :]  # [ch, 1, K]
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if a == b:
+            continue
+        xt = torch.from_numpy(x[a:b].T.copy())[None].requires_grad_(True)  # [1, ch, len]
+        yt = torch.nn.functional.silu(torch.nn.functional.conv1d(xt, wt, padding=K - 1, groups=x.shape[1])[..., : b - a])
+        (yt * torch.from_numpy(dy[a:b].T.copy())[None]).sum().backward()
+        assert np.max(np.abs(yt.detach()[0].numpy().T - y[a:b])) < 1e-13, n
+        assert np.max(np.abs(xt.grad[0].numpy().T - dx[a:b])) < 1e-13, n
+
+
+def test_conv_input_gradient_finite_differences():
+    from oracle.conv import conv1d_silu_bwd, conv1d_silu_fwd
+
+    cu, x, w, dy = _conv_case(seed=9, lens=(7, 12), ch=8, K=4)
+    dx = conv1d_silu_bwd(cu, x, w, dy)
+    rng = np.random.default_rng(1)
+    h = 1e-6
+    for _ in range(12):
+        t, c = int(rng.integers(x.shape[0])), int(rng.integers(x.shape[1]))
+        xp, xm = x.copy(), x.copy()
+        xp[t, c] += h
+        xm[t, c] -= h
+        fd = np.sum((conv1d_silu_fwd(cu, xp, w) - conv1d_silu_fwd(cu, xm, w)) * dy) / (2 * h)
+        assert abs(fd - dx[t, c]) < 1e-7 * max(1.0, abs(fd)), (t, c, fd, dx[t, c])
