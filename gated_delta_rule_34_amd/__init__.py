@@ -43,6 +43,8 @@ class gdn_problem(ctypes.Structure):
         ("chunk", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("a_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
     ]
 
 
@@ -104,8 +106,11 @@ class GdnError(RuntimeError):
         self.status = status
 
 
-def make_problem(N, T_total, Hk, Hv, D, *, T=None, cu_seqlens=None, chunk=64, scale=None, dtype="bf16"):
-    """Build a gdn_problem. ``cu_seqlens``: device int32 tensor [N + 1] or None."""
+def make_problem(N, T_total, Hk, Hv, D, *, T=None, cu_seqlens=None, chunk=64, scale=None, dtype="bf16",
+                 a_log=None, dt_bias=None):
+    """Build a gdn_problem. ``cu_seqlens``: device int32 tensor [N + 1] or None. ``a_log``,
+    ``dt_bias``: device float32 tensors [Hv] (the fused gate chain: g and beta arguments then
+    carry alpha and beta_raw) or None."""
     p = gdn_problem()
     p.N = int(N)
     p.T_total = int(T_total)
@@ -115,6 +120,8 @@ def make_problem(N, T_total, Hk, Hv, D, *, T=None, cu_seqlens=None, chunk=64, sc
     p.chunk = int(chunk)
     p.scale = float(scale if scale is not None else D ** -0.5)
     p.dtype = {"f32": GDN_F32, "bf16": GDN_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    p.a_log = None if a_log is None else a_log.data_ptr()
+    p.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
     return p
 
 

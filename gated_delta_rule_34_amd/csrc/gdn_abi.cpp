@@ -27,6 +27,8 @@ int64_t chunk_bound(const gdn_problem* p) {
   return (int64_t)p->N * (((int64_t)p->T + C - 1) / C);
 }
 
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
 gdn_status check_problem(const gdn_problem* p) {
   if (!p) return GDN_EINVAL;
   if (p->N < 0 || p->T_total < 0 || p->Hk <= 0 || p->Hv <= 0 || p->Hv % p->Hk) return GDN_EINVAL;
@@ -37,6 +39,8 @@ gdn_status check_problem(const gdn_problem* p) {
   if (p->chunk != 16 && p->chunk != 64) return GDN_EUNSUPPORTED;
   if (p->dtype == GDN_F32 && p->chunk == 64 && p->Dk > 32) return GDN_EUNSUPPORTED;  // LDS budget
   if (!std::isfinite(p->scale)) return GDN_EINVAL;
+  if ((p->a_log == nullptr) != (p->dt_bias == nullptr)) return GDN_EINVAL;
+  if (!aligned(p->a_log, 4) || !aligned(p->dt_bias, 4)) return GDN_EALIGN;
   if (!p->cu_seqlens) {
     if (p->T < 0 || (int64_t)p->N * p->T != p->T_total) return GDN_EINVAL;
   } else if (p->N == 0 && p->T_total != 0) {
@@ -101,7 +105,6 @@ void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
   P.sv_gb = reinterpret_cast<float*>(b);
 }
 
-bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Kernels address one chunk of rows with 32-bit byte offsets: chunk * rs * esize < 2^31.
 constexpr int64_t kMaxChunkSpan = (int64_t)1 << 31;
@@ -149,6 +152,8 @@ void fill_common(gdn::Prob& P, const gdn_problem* p) {
   P.T_total = p->T_total;
   P.scale = p->scale;
   P.cu = p->cu_seqlens;
+  P.a_log = p->a_log;
+  P.dt_bias = p->dt_bias;
 }
 
 gdn_status conv_common(const gdn_conv_problem* p, const void* x, int64_t x_rs, const float* w, gdn::ConvArgs& a) {
@@ -278,6 +283,8 @@ gdn_status gdn_decode(const gdn_problem* p, const void* q, int64_t q_rs, const v
   if (p->Dk != p->Dv) return GDN_EUNSUPPORTED;
   if (p->Dk != 16 && p->Dk != 32 && p->Dk != 64 && p->Dk != 128) return GDN_EUNSUPPORTED;
   if (!std::isfinite(p->scale)) return GDN_EINVAL;
+  if ((p->a_log == nullptr) != (p->dt_bias == nullptr)) return GDN_EINVAL;
+  if (!aligned(p->a_log, 4) || !aligned(p->dt_bias, 4)) return GDN_EALIGN;
   // one token per row: T = 1, T_total = N, no cu_seqlens (the chunk length is not used)
   if (p->cu_seqlens || p->T != 1 || p->T_total != p->N) return GDN_EINVAL;
   if ((int64_t)p->N * p->Hv > INT32_MAX) return GDN_EINVAL;
@@ -304,6 +311,7 @@ gdn_status gdn_decode(const gdn_problem* p, const void* q, int64_t q_rs, const v
   a.q = q; a.k = k; a.v = v;
   a.q_rs = q_rs; a.k_rs = k_rs; a.v_rs = v_rs; a.o_rs = o_rs;
   a.g = g; a.beta = beta;
+  a.a_log = p->a_log; a.dt_bias = p->dt_bias;
   a.state = state;
   a.idx = slot_idx;
   a.o = o;

@@ -736,9 +736,16 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       }
       const float dlg = wave_rscan_incl(dgam);
       if (lane < n) {  // (lane < n implies lane < C: i is the lane)
-        const float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
+        float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
         // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
-        const float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
+        float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
+        if (p.a_log) {  // gate chain: d alpha = dlog g * dlog g / d alpha, d beta_raw = dbeta beta (1 - beta)
+          int la = i;
+          asm volatile("" : "+v"(la));
+          const float alpha = p.g[(int64_t)(ci.t0 + la) * p.Hv + h];
+          dgv = dlg * chain_dlogg_dalpha(alpha, p.a_log[h], p.dt_bias[h]);
+          db *= be * (1.f - be);
+        }
         if (p.r <= GRM) {
           // the row offset is formed here rather than kept live across the item's loops
           int li = i;

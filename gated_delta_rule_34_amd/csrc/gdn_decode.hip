@@ -52,7 +52,11 @@ __global__ __launch_bounds__(DecCfg<D>::NT) void k_decode(DecArgs a) {
   f32x4 s[RPG];
 #pragma unroll
   for (int i = 0; i < RPG; ++i) s[i] = *reinterpret_cast<const f32x4*>(S + (rg + RG * i) * D + c4);
-  const float gg = a.g[(int64_t)n * a.Hv + h], be = a.beta[(int64_t)n * a.Hv + h];
+  float gg = a.g[(int64_t)n * a.Hv + h], be = a.beta[(int64_t)n * a.Hv + h];
+  if (a.a_log) {  // the gate chain from alpha and beta_raw
+    gg = exp2f(chain_log2g(gg, a.a_log[h], a.dt_bias[h]));
+    be = chain_beta(be);
+  }
   const TI* vr = (const TI*)a.v + (int64_t)n * a.v_rs + h * D + c4;
   const f32x4 vv = {to_f(vr[0]), to_f(vr[1]), to_f(vr[2]), to_f(vr[3])};
   __syncthreads();  // k and q rows in LDS

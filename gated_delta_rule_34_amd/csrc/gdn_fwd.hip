@@ -130,8 +130,17 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
       const size_t ch = ch_idx(p, c, h);
       const int i = l;
       const bool ok = i < n && i < C;
-      const float lg = ok ? __builtin_amdgcn_logf(p.g[(int64_t)(ci.t0 + i) * p.Hv + h]) : 0.f;  // log2 g
-      const float be = ok ? p.beta[(int64_t)(ci.t0 + i) * p.Hv + h] : 0.f;
+      float lg = 0.f, be = 0.f;  // log2 g and beta of the row
+      if (ok) {
+        const float gx = p.g[(int64_t)(ci.t0 + i) * p.Hv + h], bx = p.beta[(int64_t)(ci.t0 + i) * p.Hv + h];
+        if (p.a_log) {  // the gate chain from alpha and beta_raw
+          lg = chain_log2g(gx, p.a_log[h], p.dt_bias[h]);
+          be = chain_beta(bx);
+        } else {
+          lg = __builtin_amdgcn_logf(gx);
+          be = bx;
+        }
+      }
       const float gam = wave_scan_incl(i < C ? lg : 0.f);
       const float glast = lane_value(gam, C - 1);
       if (i < C) {

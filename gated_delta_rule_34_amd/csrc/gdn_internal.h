@@ -24,8 +24,10 @@ struct Prob {
   const void* q; int64_t q_rs;
   const void* k; int64_t k_rs;
   const void* v; int64_t v_rs;
-  const float* g;     // [T_total][Hv]
-  const float* beta;  // [T_total][Hv]
+  const float* g;     // [T_total][Hv]: g, or alpha when a_log is set
+  const float* beta;  // [T_total][Hv]: beta, or beta_raw when a_log is set
+  const float* a_log;    // [Hv] or nullptr: gate chain fused (g, beta from alpha, beta_raw)
+  const float* dt_bias;  // [Hv], set together with a_log
   const float* S0;    // [N][Hv][D][D] or nullptr
 
   void* o; int64_t o_rs;
@@ -63,6 +65,19 @@ struct Prob {
 // decay factors the sweeps apply to every row.
 constexpr int kGateRows = 4;
 
+// The layer's gate chain: log g = -exp(a_log) softplus(alpha + dt_bias) (returned in log2
+// units), beta = sigmoid(beta_raw); and the derivative of log g with respect to alpha,
+// -exp(a_log) sigmoid(alpha + dt_bias).
+__device__ __forceinline__ float chain_log2g(float alpha, float a_log, float dt_bias) {
+  const float z = alpha + dt_bias;
+  const float sp = z > 20.f ? z : log1pf(expf(z));  // softplus
+  return -expf(a_log) * sp * 1.4426950408889634f;
+}
+__device__ __forceinline__ float chain_beta(float beta_raw) { return 1.f / (1.f + expf(-beta_raw)); }
+__device__ __forceinline__ float chain_dlogg_dalpha(float alpha, float a_log, float dt_bias) {
+  return -expf(a_log) / (1.f + expf(-(alpha + dt_bias)));
+}
+
 // Value columns per block of the gradient kernel's value loop (also the block width of the
 // saved Delta, so that each block is one contiguous run of memory).
 template <typename T, int D> constexpr int grad_block() { return sizeof(T) == 2 ? (D >= 32 ? 32 : D) : 16; }
@@ -91,7 +106,8 @@ struct DecArgs {
   float scale;
   const void *q, *k, *v;  // row views, element row strides below
   int64_t q_rs, k_rs, v_rs, o_rs;
-  const float *g, *beta;  // [N][Hv]
+  const float *g, *beta;  // [N][Hv]: g and beta, or alpha and beta_raw when a_log is set
+  const float *a_log, *dt_bias;  // [Hv] or nullptr
   float* state;           // [n_slots][Hv][D][D]
   const int* idx;         // [N] slot of each row, or nullptr (row n -> slot n)
   void* o;

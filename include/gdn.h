@@ -77,6 +77,16 @@ typedef struct {
                        up to rounding) */
   float scale;      /* output scale, normally 1 / sqrt(Dk) */
   int32_t dtype;    /* gdn_dtype */
+  /* Gate inputs. Both NULL: the g and beta arguments are the decay gate g (0 < g <= 1) and
+   * beta themselves. Both set (DEVICE float32 [Hv] each): the layer's gate chain is fused
+   * into the kernels (the lattice-inference gdn_backward.rs page, "sigmoid(beta)" and
+   * "decay gate g per value-head"): the g argument holds alpha and the beta argument
+   * beta_raw ([T_total][Hv] float32 each), and
+   *   g = exp(-exp(a_log[h]) softplus(alpha + dt_bias[h])),  beta = sigmoid(beta_raw);
+   * gdn_bwd's dg and dbeta outputs then hold d alpha and d beta_raw (the page's steps 4e
+   * and 4h). gdn_decode follows the same rule. One set without the other: GDN_EINVAL. */
+  const float* a_log;
+  const float* dt_bias;
 } gdn_problem;
 
 /* Bytes of device workspace gdn_fwd / gdn_bwd need for this problem (0 on invalid

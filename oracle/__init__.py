@@ -13,7 +13,9 @@ autograd, closed forms (beta = 0, T = 1, g = beta = 1 with orthonormal keys),
 the v_repeat / replication identity, linearity, zero upstream gradient and split
 resume. ``gdn_decode`` (one step per row, state slots) is the forward over one-token
 sequences; its own pins replay the hand-worked example token by token and check the
-slot map against per-row forwards. No function here is "parity unpinned".
+slot map against per-row forwards. ``gate_chain`` / ``gate_chain_grads`` (the layer's
+g = exp(-exp(a_log) softplus(alpha + dt_bias)), beta = sigmoid(beta_raw) and their
+derivatives) are pinned to torch autograd of the same formulas and to finite differences. No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -120,6 +122,28 @@ def gdn_bwd(cu, q, k, v, g, beta, S0, dO, dST, scale=None, nthreads=None, lib=No
     if rc != 0:
         raise RuntimeError(f"oracle_gdn_bwd failed ({rc})")
     return out
+
+
+def gate_chain(alpha, a_log, dt_bias, beta_raw):
+    """The layer's gate chain (the gdn_backward.rs page, "decay gate g per value-head" and
+    "sigmoid(beta)"): g = exp(-exp(a_log[h]) softplus(alpha + dt_bias[h])) and
+    beta = sigmoid(beta_raw). alpha, beta_raw [T, Hv]; a_log, dt_bias [Hv]. Returns (g, beta)."""
+    alpha, beta_raw = np.asarray(alpha, np.float64), np.asarray(beta_raw, np.float64)
+    a_log, dt_bias = np.asarray(a_log, np.float64), np.asarray(dt_bias, np.float64)
+    softplus = np.logaddexp(0.0, alpha + dt_bias[None, :])
+    g = np.exp(-np.exp(a_log)[None, :] * softplus)
+    beta = 1.0 / (1.0 + np.exp(-beta_raw))
+    return g, beta
+
+
+def gate_chain_grads(alpha, a_log, dt_bias, beta_raw, dg, dbeta):
+    """d alpha and d beta_raw from the gradients dg, dbeta of g and beta (the page's steps 4e
+    and 4h): dg/d alpha = g (-exp(a_log)) sigmoid(alpha + dt_bias), dbeta/d beta_raw =
+    beta (1 - beta). Returns (dalpha, dbeta_raw)."""
+    g, beta = gate_chain(alpha, a_log, dt_bias, beta_raw)
+    a_log, dt_bias = np.asarray(a_log, np.float64), np.asarray(dt_bias, np.float64)
+    sig = 1.0 / (1.0 + np.exp(-(np.asarray(alpha, np.float64) + dt_bias[None, :])))
+    return dg * g * (-np.exp(a_log)[None, :]) * sig, dbeta * beta * (1.0 - beta)
 
 
 def gdn_decode(q, k, v, g, beta, state, slot_idx=None, scale=None, nthreads=None, lib=None):

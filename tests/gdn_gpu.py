@@ -71,13 +71,13 @@ def problem(case, d, chunk=None):
                           scale=case.scale, dtype=case.dtype)
 
 
-def run_gpu(case, backward=True, chunk=None, packed=None, d=None):
+def run_gpu(case, backward=True, chunk=None, packed=None, d=None, p=None):
     """Run forward (+ backward) through the C ABI; returns numpy float64 results."""
     import torch
     import gated_delta_rule_34_amd as G
 
     d = d or to_device(case, packed=packed)
-    p = problem(case, d, chunk)
+    p = p or problem(case, d, chunk)
     T, Hk, Hv, D = case.T_total, case.Hk, case.Hv, case.Dk
     o = torch.empty(T, Hv, D, dtype=d["v"].dtype, device=d["v"].device)
     o, S_T, states = G.forward(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o=o)

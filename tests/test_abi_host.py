@@ -142,6 +142,14 @@ def test_rejects_bad_problems(G):
     assert status_of(G, p) == G.GDN_EINVAL
 
 
+def test_gate_chain_needs_both_parameters(G):
+    p = prob(G)
+    p.a_log = 0x88000  # dt_bias left NULL
+    assert status_of(G, p) == G.GDN_EINVAL
+    p.dt_bias = 0x88102  # misaligned
+    assert status_of(G, p) == G.GDN_EALIGN
+
+
 def test_rejects_bad_views(G):
     p = prob(G)
     T = p.T_total

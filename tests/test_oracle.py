@@ -460,3 +460,34 @@ def test_conv_input_gradient_finite_differences():
         xm[t, c] -= h
         fd = np.sum((conv1d_silu_fwd(cu, xp, w) - conv1d_silu_fwd(cu, xm, w)) * dy) / (2 * h)
         assert abs(fd - dx[t, c]) < 1e-7 * max(1.0, abs(fd)), (t, c, fd, dx[t, c])
+
+
+# --- the layer's gate chain (oracle.gate_chain / gate_chain_grads)
+
+def test_gate_chain_matches_torch_autograd_and_fd():
+    """g = exp(-exp(a_log) softplus(alpha + dt_bias)), beta = sigmoid(beta_raw): values and
+    the backward to alpha and beta_raw against torch (float64, torch's softplus and sigmoid,
+    autograd), and central differences."""
+    import torch
+
+    rng = np.random.default_rng(12)
+    T, Hv = 9, 5
+    alpha, beta_raw = rng.standard_normal((T, Hv)) * 3, rng.standard_normal((T, Hv)) * 3
+    a_log, dt_bias = rng.uniform(-2, 1, Hv), rng.uniform(-1, 1, Hv)
+    dg, dbeta = rng.standard_normal((T, Hv)), rng.standard_normal((T, Hv))
+    g, beta = oracle.gate_chain(alpha, a_log, dt_bias, beta_raw)
+    da, dbr = oracle.gate_chain_grads(alpha, a_log, dt_bias, beta_raw, dg, dbeta)
+    ta = torch.tensor(alpha, requires_grad=True)
+    tb = torch.tensor(beta_raw, requires_grad=True)
+    tg = torch.exp(-torch.exp(torch.tensor(a_log))[None] * torch.nn.functional.softplus(ta + torch.tensor(dt_bias)[None]))
+    tbe = torch.sigmoid(tb)
+    ((tg * torch.tensor(dg)).sum() + (tbe * torch.tensor(dbeta)).sum()).backward()
+    assert np.max(np.abs(tg.detach().numpy() - g)) < 1e-14 and np.max(np.abs(tbe.detach().numpy() - beta)) < 1e-14
+    assert np.max(np.abs(ta.grad.numpy() - da)) < 1e-13 and np.max(np.abs(tb.grad.numpy() - dbr)) < 1e-13
+    h = 1e-6
+    for t, j in [(0, 0), (4, 2), (8, 4)]:
+        ap, am = alpha.copy(), alpha.copy()
+        ap[t, j] += h
+        am[t, j] -= h
+        fd = (oracle.gate_chain(ap, a_log, dt_bias, beta_raw)[0][t, j] - oracle.gate_chain(am, a_log, dt_bias, beta_raw)[0][t, j]) / (2 * h)
+        assert abs(fd * dg[t, j] - da[t, j]) < 1e-7 * max(1.0, abs(da[t, j]))
