@@ -326,6 +326,32 @@ def main():
     torch.cuda.synchronize()
     ms_fwd = start.elapsed_time(end) / args.steps
     print(f"[bench] timed: {ms_step:.3f} ms/step, fwd {ms_fwd:.3f} ms", file=sys.stderr, flush=True)
+
+    # The same step with the layer's q/k L2 normalisation and gate chain fused into the
+    # kernels (raw q, k rows; alpha and beta_raw in place of g and beta): what the fusion
+    # costs over the plain step (outside the timed region above).
+    ta_log = torch.full((Hv,), -0.5, dtype=torch.float32, device=dev)
+    tdt = torch.full((Hv,), 0.5, dtype=torch.float32, device=dev)
+    pf = problem(case, d)
+    pf.qk_l2norm, pf.a_log, pf.dt_bias = 1, ta_log.data_ptr(), tdt.data_ptr()
+    states_f = torch.empty(G.gdn_chunk_state_bytes(pf), dtype=torch.uint8, device=dev)
+    alpha, beta_raw = torch.zeros_like(d["g"]), torch.zeros_like(d["beta"])
+
+    def step_fused():
+        G.gdn_fwd(pf, d["q"], d["k"], d["v"], alpha, beta_raw, d["S0"], o, S_T, states_f, ws)
+        G.gdn_bwd(pf, d["q"], d["k"], d["v"], alpha, beta_raw, d["S0"], states_f, d["dO"], d["dST"],
+                  d["dq"], d["dk"], d["dv"], dg, dbeta, dS0, ws)
+
+    for _ in range(args.warmup):
+        step_fused()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step_fused()
+    end.record()
+    torch.cuda.synchronize()
+    ms_fused = start.elapsed_time(end) / args.steps
+    del states_f
     decode = decode_bench(G, torch, args.steps)
     print(f"[bench] decode: {decode['kernel_ms']:.4f} ms per step, {decode['GB/s']} GB/s", file=sys.stderr, flush=True)
     conv = conv_bench(G, torch, args.steps)
@@ -390,6 +416,7 @@ def main():
                                "chunk 64, fwd (saving chunk states) + bwd",
                    "global_batch": case.N, "seq_len": case.lens[0], "parallelism": "single GPU"},
         "fwd_tokens_per_s": round(T / (ms_fwd / 1e3), 1),
+        "fused_l2norm_gate_chain": {"ms_per_step": round(ms_fused, 4), "tokens_per_s": round(T / (ms_fused / 1e3), 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_avg_ms": kernels,

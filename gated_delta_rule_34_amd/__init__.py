@@ -45,6 +45,7 @@ class gdn_problem(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("a_log", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p),
+        ("qk_l2norm", ctypes.c_int32),
     ]
 
 
@@ -107,7 +108,7 @@ class GdnError(RuntimeError):
 
 
 def make_problem(N, T_total, Hk, Hv, D, *, T=None, cu_seqlens=None, chunk=64, scale=None, dtype="bf16",
-                 a_log=None, dt_bias=None):
+                 a_log=None, dt_bias=None, qk_l2norm=False):
     """Build a gdn_problem. ``cu_seqlens``: device int32 tensor [N + 1] or None. ``a_log``,
     ``dt_bias``: device float32 tensors [Hv] (the fused gate chain: g and beta arguments then
     carry alpha and beta_raw) or None."""
@@ -122,6 +123,7 @@ def make_problem(N, T_total, Hk, Hv, D, *, T=None, cu_seqlens=None, chunk=64, sc
     p.dtype = {"f32": GDN_F32, "bf16": GDN_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
     p.a_log = None if a_log is None else a_log.data_ptr()
     p.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
+    p.qk_l2norm = 1 if qk_l2norm else 0
     return p
 
 

@@ -57,6 +57,7 @@ gdn_status check_problem(const gdn_problem* p) {
 struct Regions {
   size_t chunks, seq_chunk;        // chunk table, first chunk per sequence
   size_t oDD, oCD, oCC, gb;        // per (chunk, value head): [D][D], [D][C], [C][C] elements, [kGateRows][C] f32
+  size_t qn, rr;                   // normalised q or k rows, their factors (0 without qk_l2norm)
 };
 
 Regions regions(const gdn_problem* p) {
@@ -69,6 +70,8 @@ Regions regions(const gdn_problem* p) {
   r.oCD = align_up(nc * Hv * C * D * es);
   r.oCC = align_up(nc * Hv * C * C * es);
   r.gb = align_up(nc * Hv * gdn::kGateRows * C * sizeof(float));
+  r.qn = p->qk_l2norm ? align_up((size_t)p->T_total * p->Hk * D * es) : 0;
+  r.rr = p->qk_l2norm ? align_up((size_t)p->T_total * p->Hk * 2 * sizeof(float)) : 0;
   return r;
 }
 
@@ -85,7 +88,7 @@ size_t bwd_ws(const gdn_problem* p) {
 // and the gate record.
 size_t saved_bytes(const gdn_problem* p) {
   const Regions r = regions(p);
-  return r.chunks + r.seq_chunk + r.oDD + r.oCD + 2 * r.oCC + r.gb;
+  return r.chunks + r.seq_chunk + r.oDD + r.oCD + 2 * r.oCC + r.gb + 2 * r.qn + r.rr;
 }
 
 void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
@@ -103,6 +106,23 @@ void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
   P.sv_M = b;
   b += r.oCC;
   P.sv_gb = reinterpret_cast<float*>(b);
+  b += r.gb;
+  if (r.qn) {
+    P.sv_qn = b;
+    b += r.qn;
+    P.sv_kn = b;
+    b += r.qn;
+    P.sv_r = reinterpret_cast<float*>(b);
+  }
+}
+
+// The q and k rows the chunk kernels read: the normalised copies when prep writes them.
+void set_qk_use(gdn::Prob& P) {
+  const int64_t w = (int64_t)P.Hk * P.D;
+  P.qu = P.sv_qn ? P.sv_qn : P.q;
+  P.qu_rs = P.sv_qn ? w : P.q_rs;
+  P.ku = P.sv_kn ? P.sv_kn : P.k;
+  P.ku_rs = P.sv_kn ? w : P.k_rs;
 }
 
 
@@ -223,6 +243,7 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.o = o; P.o_rs = o_rs; P.ST = S_T;
   const Regions r = regions(p);
   carve_saved(P, r, chunk_states);
+  set_qk_use(P);
   const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
@@ -266,6 +287,7 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.dg = dg; P.dbeta = dbeta; P.dS0 = dS0;
   const Regions r = regions(p);
   carve_saved(P, r, const_cast<void*>(chunk_states));  // the chunk table comes with it
+  set_qk_use(P);
   Carver cv{static_cast<char*>(workspace)};
   P.ws_dS = cv.take<void>(r.oDD);
   P.ws_A = cv.take<void>(r.oCD);
@@ -312,6 +334,7 @@ gdn_status gdn_decode(const gdn_problem* p, const void* q, int64_t q_rs, const v
   a.q_rs = q_rs; a.k_rs = k_rs; a.v_rs = v_rs; a.o_rs = o_rs;
   a.g = g; a.beta = beta;
   a.a_log = p->a_log; a.dt_bias = p->dt_bias;
+  a.l2 = p->qk_l2norm != 0;
   a.state = state;
   a.idx = slot_idx;
   a.o = o;

@@ -98,7 +98,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
   using FragD = typename Mf<OT, KSD>::frag;
   using FragC = typename Mf<OT, KSC>::frag;
   __shared__ __align__(16) OT sbuf[2][CF::BUF];
-  __shared__ __align__(16) float sgb[2][kGateRows * C];
+  __shared__ __align__(16) float sgb[2][kSweepGateRows * C];
   __shared__ __align__(16) OT stg[C * CF::LSO];  // the chunk's dV rows, all D columns
 
   int grp, hh;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
 
   TileDma<C, D, NW, OT, true> dmD;   // K, Q, dO
   TileDma<C, C, NW, OT, true> dmC;   // T, M
-  TileDma<1, kGateRows * C, NW, float> dmG;  // gate record
+  TileDma<1, kSweepGateRows * C, NW, float> dmG;  // gate record rows 0-3
   dmD.init(w);
   dmC.init(w);
   dmG.init(w);
@@ -122,12 +122,12 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     const int len = (int)(sb - t0 < C ? sb - t0 : C);
     const size_t ch = ch_idx(p, c, h);
     OT* b = sbuf[buf];
-    dmD.issue(b + CF::O_K, (const OT*)p.k + t0 * p.k_rs + kh * D, p.k_rs, len, w);
-    dmD.issue(b + CF::O_Q, (const OT*)p.q + t0 * p.q_rs + kh * D, p.q_rs, len, w);
+    dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
+    dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
     dmD.issue(b + CF::O_O, (const OT*)p.dO + t0 * p.dO_rs + h * D, p.dO_rs, len, w);
     dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
     dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
-    dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kGateRows * C, 1, w);
+    dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
   };
 
   // The adjoint: dS[ct][dt] holds dS[16 dt + g4 + e][v0 + 16 ct + r16].
@@ -406,6 +406,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   // run of single floats)
   constexpr int GRM = 4;
   __shared__ float sgo[2][GRM][C];
+  // q/k L2 normalisation: per dq, dk row the dot of the normalised row with its gradient,
+  // and the row's factor (the norm's backward is applied at the store)
+  __shared__ float sdot[2 * C], srf[2 * C];
+  __shared__ __align__(16) float sdl[3][C];  // d log g / d alpha per row (gate chain), with sgb
 
   const int kh = blockIdx.x % p.Hk, c = blockIdx.x / p.Hk;
   const ChunkInfo ci = p.chunks[c];
@@ -422,6 +426,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   TileDma<C, PW, NH, OT, true> dmP;   // dO (first half) or V (second half) for a pair of blocks
   TileDma<C, D, NW, OT, true> dmD;    // K, Q
   TileDma<1, 2 * C, NW, float> dmG;  // gate record
+  TileDma<1, C, NW, float> dmGc;     // its d log g / d alpha row (gate chain only)
   const int wh = w % NH;
   dmS.init(w);
   dmA.init(wh);
@@ -429,6 +434,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   dmP.init(wh);
   dmD.init(w);
   dmG.init(w);
+  dmGc.init(w);
   const int njobs = p.r * NBH, npairs = njobs / PB;
   // Job j = (head h0 + j / NBH, block j % NBH) goes into sB[j % NBUF]; the first block of a
   // head also brings the head's gate record. Job j's loads are issued in the step of job
@@ -443,6 +449,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     if (part == 0) {
       dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
       if (blk == 0) dmG.issue(sgb[(j / NBH) % 3], p.sv_gb + ch * kGateRows * C, 2 * C, 1, w);  // gamma, beta
+      if (blk == 0 && p.a_log) dmGc.issue(sdl[(j / NBH) % 3], p.sv_gb + ch * kGateRows * C + 4 * C, C, 1, w);
     } else if (part == 1) {
       dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
     } else {
@@ -465,15 +472,17 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   };
   // This wave's load instructions of job j, of a pair, and of the step of job j.
   auto job_loads = [&](int j) {
-    return j < njobs ? 2 * dmS.count(w) + (w < NH ? dmA.count(wh) : dmL.count(wh)) + (j % NBH == 0 ? dmG.count(w) : 0) : 0;
+    return j < njobs ? 2 * dmS.count(w) + (w < NH ? dmA.count(wh) : dmL.count(wh)) +
+                           (j % NBH == 0 ? dmG.count(w) + (p.a_log ? dmGc.count(w) : 0) : 0)
+                     : 0;
   };
   const int pair_loads = dmP.count(wh);
   auto step_loads = [&](int j) {  // issued in the step of job j: job j + 2 and, maybe, a pair
     const int q = PB == 1 ? j + 2 : j / PB + 1;
     return job_loads(j + 2) + ((j % PB == 0 && q < npairs) ? pair_loads : 0);
   };
-  dmD.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
-  dmD.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
+  dmD.issue(sK, (const OT*)p.ku + (int64_t)ci.t0 * p.ku_rs + kh * D, p.ku_rs, n, w);
+  dmD.issue(sQ, (const OT*)p.qu + (int64_t)ci.t0 * p.qu_rs + kh * D, p.qu_rs, n, w);
   issue_job(0);
   issue_pair(0);
   if (1 < njobs) {
@@ -739,11 +748,8 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
         // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
         float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
-        if (p.a_log) {  // gate chain: d alpha = dlog g * dlog g / d alpha, d beta_raw = dbeta beta (1 - beta)
-          int la = i;
-          asm volatile("" : "+v"(la));
-          const float alpha = p.g[(int64_t)(ci.t0 + la) * p.Hv + h];
-          dgv = dlg * chain_dlogg_dalpha(alpha, p.a_log[h], p.dt_bias[h]);
+        if (p.a_log) {  // gate chain: d alpha = dlog g * dlog g / d alpha (from the record), d beta_raw = dbeta beta (1 - beta)
+          dgv = dlg * sdl[hh % 3][i];
           db *= be * (1.f - be);
         }
         if (p.r <= GRM) {
@@ -809,6 +815,21 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     lds_barrier();
     using V = Vec16<TI>;
     constexpr int VPR = D / V::N;
+    const bool l2 = p.sv_qn != nullptr;
+    if (l2) {  // x_hat . dx_hat per row (wave w takes rows w, w + NW, ... of dq, then of dk)
+      for (int rr = w; rr < 2 * C; rr += NW) {
+        const int i = rr % C;
+        const OT* X = rr < C ? sQ : sK;  // the normalised rows
+        float x = 0.f;
+        for (int c = lane; c < D; c += 64) x += (float)X[LD::at(i, c)] * (float)st[LS::at(rr, c)];
+        x = wave_sum(x);
+        if (lane == 0) {
+          sdot[rr] = x;
+          srf[rr] = i < n ? p.sv_r[((int64_t)(ci.t0 + i) * p.Hk + kh) * 2 + (rr < C ? 0 : 1)] : 0.f;
+        }
+      }
+      lds_barrier();
+    }
     TI* dq = (TI*)p.dq + (int64_t)ci.t0 * p.dq_rs + kh * D;
     TI* dk = (TI*)p.dk + (int64_t)ci.t0 * p.dk_rs + kh * D;
     for (int idx = threadIdx.x; idx < 2 * C * VPR; idx += kThreadsG) {
@@ -816,7 +837,15 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       const int i = r % C;
       if (i < n) {
         TI* dst = r < C ? dq + (int64_t)i * p.dq_rs + cc : dk + (int64_t)i * p.dk_rs + cc;
-        *reinterpret_cast<typename V::type*>(dst) = *reinterpret_cast<const typename V::type*>(st + LS::at(r, cc));
+        typename V::type val = *reinterpret_cast<const typename V::type*>(st + LS::at(r, cc));
+        if (l2) {  // dx = r (dx_hat - x_hat (x_hat . dx_hat)), the gradient of the raw row
+          const OT* X = r < C ? sQ : sK;
+          const float dt = sdot[r], rf = srf[r];
+#pragma unroll
+          for (int e = 0; e < V::N; ++e)
+            val[e] = (TI)(rf * ((float)val[e] - (float)X[LD::at(i, cc + e)] * dt));
+        }
+        *reinterpret_cast<typename V::type*>(dst) = val;
       }
     }
     if (p.r <= GRM) {  // dbeta, dg: row i, heads h0 .. h0 + r - 1

@@ -5,7 +5,8 @@
 // (lattice-inference 0.6.0, docs.rs source of src/attention/gdn_backward.rs, module doc
 // "Forward recap"; the pages' shipping inference path, gated_delta_net_step_fused, steps
 // the same recurrence one token at a time):
-//   kv = S^T k,  delta = beta (v - g kv),  S' = g S + k delta^T,  o = scale S'^T q.
+//   kv = S^T k,  delta = beta (v - g kv),  S' = g S + k delta^T,  o = scale S'^T q
+// (with q and k first L2-normalised per head row when the problem asks for it).
 // The kernel reads S once: S'^T q = g S^T q + delta (k . q), so S^T k and S^T q come from
 // the same pass over S, and S' is written from the registers that hold S. Per row and
 // head it moves 2 D^2 float32 of state and O(D) else: it is bound by HBM, and it is plain
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT) void k_decode(DecArgs a) {
   constexpr int NT = CF::NT, CPR = CF::CPR, RG = CF::RG, RPG = CF::RPG;
   __shared__ float sk[D], sq[D];
   __shared__ __align__(16) float part[2][RG][D];  // per row group: partial S^T k, S^T q
-  __shared__ float skq;
+  __shared__ float skq, srk, srq;  // k . q (of the normalised rows when a.l2), the factors of k and q
 
   const int n = blockIdx.x / a.Hv, h = blockIdx.x - n * a.Hv;
   const int slot = a.idx ? a.idx[n] : n;
@@ -70,11 +71,21 @@ __global__ __launch_bounds__(DecCfg<D>::NT) void k_decode(DecArgs a) {
   }
   *reinterpret_cast<f32x4*>(&part[0][rg][c4]) = pk;
   *reinterpret_cast<f32x4*>(&part[1][rg][c4]) = pq;
-  if (t < 64) {  // k . q
-    float x = 0.f;
-    for (int d = t; d < D; d += 64) x += sk[d] * sq[d];
+  if (t < 64) {  // k . q, and the L2 factors of k and q when the rows are normalised here
+    float x = 0.f, xk = 0.f, xq = 0.f;
+    for (int d = t; d < D; d += 64) {
+      x += sk[d] * sq[d];
+      xk += sk[d] * sk[d];
+      xq += sq[d] * sq[d];
+    }
     x = wave_sum(x);
-    if (t == 0) skq = x;
+    const float rk = a.l2 ? 1.f / sqrtf(wave_sum(xk) + 1e-6f) : 1.f;
+    const float rq = a.l2 ? 1.f / sqrtf(wave_sum(xq) + 1e-6f) : 1.f;
+    if (t == 0) {
+      skq = x * rk * rq;
+      srk = rk;
+      srq = rq;
+    }
   }
   __syncthreads();  // partial sums complete
 
@@ -85,6 +96,8 @@ __global__ __launch_bounds__(DecCfg<D>::NT) void k_decode(DecArgs a) {
     kv += *reinterpret_cast<const f32x4*>(&part[0][j][c4]);
     qv += *reinterpret_cast<const f32x4*>(&part[1][j][c4]);
   }
+  kv *= srk;  // S^T k_hat, S^T q_hat (the factors are 1 without normalisation)
+  qv *= srq;
   const f32x4 delta = be * (vv - gg * kv);
   if (rg == 0) {  // o = scale (g S^T q + delta (k . q)) for this thread's 4 columns
     const f32x4 ov = a.scale * (gg * qv + delta * skq);
@@ -92,11 +105,12 @@ __global__ __launch_bounds__(DecCfg<D>::NT) void k_decode(DecArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) orow[e] = (TI)ov[e];
   }
-  // S' = g S + k delta^T
+  // S' = g S + k_hat delta^T
+  const float rk = srk;
 #pragma unroll
   for (int i = 0; i < RPG; ++i) {
     const int d = rg + RG * i;
-    *reinterpret_cast<f32x4*>(S + d * D + c4) = gg * s[i] + sk[d] * delta;
+    *reinterpret_cast<f32x4*>(S + d * D + c4) = gg * s[i] + (sk[d] * rk) * delta;
   }
 }
 

@@ -130,12 +130,13 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
       const size_t ch = ch_idx(p, c, h);
       const int i = l;
       const bool ok = i < n && i < C;
-      float lg = 0.f, be = 0.f;  // log2 g and beta of the row
+      float lg = 0.f, be = 0.f, dla = 0.f;  // log2 g, beta, d log g / d alpha of the row
       if (ok) {
         const float gx = p.g[(int64_t)(ci.t0 + i) * p.Hv + h], bx = p.beta[(int64_t)(ci.t0 + i) * p.Hv + h];
         if (p.a_log) {  // the gate chain from alpha and beta_raw
           lg = chain_log2g(gx, p.a_log[h], p.dt_bias[h]);
           be = chain_beta(bx);
+          dla = chain_dlogg_dalpha(gx, p.a_log[h], p.dt_bias[h]);
         } else {
           lg = __builtin_amdgcn_logf(gx);
           be = bx;
@@ -151,12 +152,44 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
         rec[C + i] = be;
         rec[2 * C + i] = __builtin_amdgcn_exp2f(gam);
         rec[3 * C + i] = __builtin_amdgcn_exp2f(glast - gam);
+        rec[4 * C + i] = dla;
       }
     }
   };
   gates(0);  // while K and Q arrive
   dma_wait();
   lds_barrier();
+  if (p.sv_qn) {  // L2-normalise the q and k head rows in LDS and keep them, and the factors,
+                  // for the later kernels: PPR lanes per row, one 16-byte piece each, rows of Q
+                  // then of K, RPW rows per wave and pass
+    using V = Vec16<OT>;
+    constexpr int PPR = D / V::N, RPW = 64 / PPR;
+    const int sub = l % PPR;
+    for (int r0 = w * RPW; r0 < 2 * C; r0 += NW * RPW) {
+      const int rr = r0 + l / PPR;
+      const bool okr = rr < 2 * C;  // (every lane takes part in the group sum)
+      OT* X = rr < C ? sQ : sK;
+      const int i = okr ? rr % C : 0;
+      typename V::type xv = *reinterpret_cast<const typename V::type*>(X + LD::at(i, sub * V::N));
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < V::N; ++e) ss += (float)xv[e] * (float)xv[e];
+#pragma unroll
+      for (int o = 1; o < PPR; o <<= 1) ss += __shfl_xor(ss, o);
+      const float rf = 1.f / sqrtf(ss + 1e-6f);
+#pragma unroll
+      for (int e = 0; e < V::N; ++e) xv[e] = (OT)((float)xv[e] * rf);
+      if (okr) {
+        *reinterpret_cast<typename V::type*>(X + LD::at(i, sub * V::N)) = xv;
+        if (i < n) {
+          const int64_t hr = (int64_t)(ci.t0 + i) * p.Hk + kh;  // head row
+          *reinterpret_cast<typename V::type*>((OT*)(rr < C ? p.sv_qn : p.sv_kn) + hr * D + sub * V::N) = xv;
+          if (sub == 0) p.sv_r[hr * 2 + (rr < C ? 0 : 1)] = rf;
+        }
+      }
+    }
+    lds_barrier();
+  }
   // K K^T and Q K^T: wave w < C / 16 owns row tile w and every column tile.
   const bool rw = w < RT;
   f32x4 KK[1][RT], QK[1][RT];
@@ -293,7 +326,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
   using FragD = typename Mf<OT, KSD>::frag;
   using FragC = typename Mf<OT, KSC>::frag;
   __shared__ __align__(16) OT sbuf[2][CF::BUF];
-  __shared__ __align__(16) float sgb[2][kGateRows * C];
+  __shared__ __align__(16) float sgb[2][kSweepGateRows * C];
   __shared__ __align__(16) OT stg[C * CF::LSO];  // the chunk's output rows, all D columns
 
   int grp, hh;
@@ -308,7 +341,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
 
   TileDma<C, D, NW, OT, false, CF::PTD> dmD;  // K, Q, V
   TileDma<C, C, NW, OT, false, CF::PTC> dmC;  // T, M
-  TileDma<1, kGateRows * C, NW, float> dmG;  // gate record
+  TileDma<1, kSweepGateRows * C, NW, float> dmG;  // gate record rows 0-3
   dmD.init(w);
   dmC.init(w);
   dmG.init(w);
@@ -317,12 +350,12 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     const int len = (int)(sb - t0 < C ? sb - t0 : C);
     const size_t ch = ch_idx(p, c, h);
     OT* b = sbuf[buf];
-    dmD.issue(b + CF::O_K, (const OT*)p.k + t0 * p.k_rs + kh * D, p.k_rs, len, w);
-    dmD.issue(b + CF::O_Q, (const OT*)p.q + t0 * p.q_rs + kh * D, p.q_rs, len, w);
+    dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
+    dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
     dmD.issue(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
     dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
     dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
-    dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kGateRows * C, 1, w);
+    dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
   };
 
   // The state: S[ct][dt] holds S[16 dt + g4 + e][v0 + 16 ct + r16].

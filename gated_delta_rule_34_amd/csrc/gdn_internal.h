@@ -54,6 +54,13 @@ struct Prob {
   void* sv_T;    // [c][h][C][C]  T = (I + L)^-1, row-major
   void* sv_M;    // [c][h][C][C]  M = Gamma o Q K^T (lower incl. diagonal), row-major
   float* sv_gb;  // [c][h][kGateRows][C]  float32 gate record, rows below
+  // q/k L2 normalisation (fused when sv_qn is set): prep writes the normalised rows and
+  // 1 / sqrt(|row|^2 + 1e-6) of each q and k head row; every later kernel reads qu / ku.
+  void* sv_qn;   // [T_total][Hk][D] storage type, or nullptr
+  void* sv_kn;   // [T_total][Hk][D]
+  float* sv_r;   // [T_total][Hk][2]: the factor of q, then of k
+  const void* qu; int64_t qu_rs;  // the q rows the chunk kernels read: q, or sv_qn
+  const void* ku; int64_t ku_rs;
   // workspace
   void* ws_dS;   // [c][h][D][D]  state adjoint flowing into the end of the chunk, dS^T[v][d]
   void* ws_A;    // [c][h][D/BV][C][BV]  A = T^T dDelta in blocks of BV value columns
@@ -63,7 +70,10 @@ struct Prob {
 // Rows of the per-(chunk, value head) gate record: gamma = cumulative log2 g (rows past the
 // end add 0), beta (0 past the end), b = 2^gamma and e = 2^(gamma_last - gamma), the two
 // decay factors the sweeps apply to every row.
-constexpr int kGateRows = 4;
+constexpr int kGateRows = 5;
+// Rows 0-3 are what the sweeps read; row 4 is d log g / d alpha of the fused gate chain,
+// -exp(a_log) sigmoid(alpha + dt_bias) (0 without it), read by the gradient kernel.
+constexpr int kSweepGateRows = 4;
 
 // The layer's gate chain: log g = -exp(a_log) softplus(alpha + dt_bias) (returned in log2
 // units), beta = sigmoid(beta_raw); and the derivative of log g with respect to alpha,
@@ -108,6 +118,7 @@ struct DecArgs {
   int64_t q_rs, k_rs, v_rs, o_rs;
   const float *g, *beta;  // [N][Hv]: g and beta, or alpha and beta_raw when a_log is set
   const float *a_log, *dt_bias;  // [Hv] or nullptr
+  int l2;                 // L2-normalise the q and k rows first
   float* state;           // [n_slots][Hv][D][D]
   const int* idx;         // [N] slot of each row, or nullptr (row n -> slot n)
   void* o;

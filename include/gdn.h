@@ -87,6 +87,13 @@ typedef struct {
    * and 4h). gdn_decode follows the same rule. One set without the other: GDN_EINVAL. */
   const float* a_log;
   const float* dt_bias;
+  /* Nonzero: q and k are the layer's raw projections and the kernels L2-normalise every head
+   * row themselves, x_hat = x / sqrt(sum x^2 + 1e-6) (the gdn_backward.rs page, "L2-normalize
+   * q, k", with the epsilon inside the square root), before any use; gdn_bwd's dq and dk are
+   * then the gradients with respect to the raw q and k (the page's step 4f). The normalised
+   * rows are kept with the chunk states (gdn_chunk_state_bytes grows by 2 T_total Hk Dk
+   * elements and 8 T_total Hk bytes). Zero: q and k are used as given. */
+  int32_t qk_l2norm;
 } gdn_problem;
 
 /* Bytes of device workspace gdn_fwd / gdn_bwd need for this problem (0 on invalid

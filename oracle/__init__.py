@@ -15,7 +15,8 @@ resume. ``gdn_decode`` (one step per row, state slots) is the forward over one-t
 sequences; its own pins replay the hand-worked example token by token and check the
 slot map against per-row forwards. ``gate_chain`` / ``gate_chain_grads`` (the layer's
 g = exp(-exp(a_log) softplus(alpha + dt_bias)), beta = sigmoid(beta_raw) and their
-derivatives) are pinned to torch autograd of the same formulas and to finite differences. No function here is "parity unpinned".
+derivatives) are pinned to torch autograd of the same formulas and to finite differences,
+and so are ``l2norm_rows`` / ``l2norm_rows_grad`` (the q/k normalisation and its backward). No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -144,6 +145,20 @@ def gate_chain_grads(alpha, a_log, dt_bias, beta_raw, dg, dbeta):
     a_log, dt_bias = np.asarray(a_log, np.float64), np.asarray(dt_bias, np.float64)
     sig = 1.0 / (1.0 + np.exp(-(np.asarray(alpha, np.float64) + dt_bias[None, :])))
     return dg * g * (-np.exp(a_log)[None, :]) * sig, dbeta * beta * (1.0 - beta)
+
+
+def l2norm_rows(x):
+    """x_hat = x / sqrt(sum x^2 + 1e-6) over the last axis (the gdn_backward.rs page, "L2-normalize
+    q, k", epsilon inside the square root). Returns (x_hat, r) with r = 1 / sqrt(sum x^2 + 1e-6)."""
+    x = np.asarray(x, np.float64)
+    r = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-6)
+    return x * r, r
+
+
+def l2norm_rows_grad(x_hat, r, dx_hat):
+    """Gradient with respect to x of x_hat = x r (the page's step 4f):
+    r (dx_hat - x_hat (x_hat . dx_hat))."""
+    return r * (dx_hat - x_hat * np.sum(x_hat * dx_hat, axis=-1, keepdims=True))
 
 
 def gdn_decode(q, k, v, g, beta, state, slot_idx=None, scale=None, nthreads=None, lib=None):

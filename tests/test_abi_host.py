@@ -142,6 +142,15 @@ def test_rejects_bad_problems(G):
     assert status_of(G, p) == G.GDN_EINVAL
 
 
+def test_l2norm_keeps_the_normalised_rows(G):
+    p = prob(G)
+    base = G.gdn_chunk_state_bytes(p)
+    p.qk_l2norm = 1
+    extra = 2 * p.T_total * p.Hk * p.Dk * 2 + p.T_total * p.Hk * 8  # q_hat, k_hat (bf16), two factors per head row
+    assert G.gdn_chunk_state_bytes(p) >= base + extra
+    assert G.gdn_chunk_state_bytes(p) < base + extra + 3 * 256  # each region rounded up to 256 bytes
+
+
 def test_gate_chain_needs_both_parameters(G):
     p = prob(G)
     p.a_log = 0x88000  # dt_bias left NULL

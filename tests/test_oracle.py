@@ -491,3 +491,21 @@ def test_gate_chain_matches_torch_autograd_and_fd():
         am[t, j] -= h
         fd = (oracle.gate_chain(ap, a_log, dt_bias, beta_raw)[0][t, j] - oracle.gate_chain(am, a_log, dt_bias, beta_raw)[0][t, j]) / (2 * h)
         assert abs(fd * dg[t, j] - da[t, j]) < 1e-7 * max(1.0, abs(da[t, j]))
+
+
+def test_l2norm_rows_matches_torch_autograd():
+    """x / sqrt(sum x^2 + 1e-6) and its backward against torch autograd (float64), including
+    a zero row (where the epsilon decides)."""
+    import torch
+
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((6, 3, 16)) * 2
+    x[2, 1] = 0.0
+    dxh = rng.standard_normal(x.shape)
+    xh, r = oracle.l2norm_rows(x)
+    dx = oracle.l2norm_rows_grad(xh, r, dxh)
+    tx = torch.tensor(x, requires_grad=True)
+    th = tx / torch.sqrt((tx * tx).sum(-1, keepdim=True) + 1e-6)
+    (th * torch.tensor(dxh)).sum().backward()
+    assert np.max(np.abs(th.detach().numpy() - xh)) < 1e-14
+    assert np.max(np.abs(tx.grad.numpy() - dx)) < 1e-12
