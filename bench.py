@@ -260,8 +260,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the recurrence shards "
+              "without communication by key-head group or sequence, one process per GPU); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -72,7 +72,7 @@ typedef struct {
                                 NULL = N sequences of T tokens. Zero-length sequences allowed:
                                 their S_T is S0 and their dS0 is dS_T. */
   int32_t Hk, Hv;   /* key heads and value heads; Hv % Hk == 0, v_repeat = Hv / Hk */
-  int32_t Dk, Dv;   /* head sizes; this build requires Dk == Dv in {16, 32, 64, 128} */
+  int32_t Dk, Dv;   /* head sizes; Dk == Dv in {16, 32, 64, 128} is required */
   int32_t chunk;    /* chunk length of the chunked algorithm: 16 or 64 (results agree
                        up to rounding) */
   float scale;      /* output scale, normally 1 / sqrt(Dk) */
