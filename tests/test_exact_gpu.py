@@ -151,3 +151,31 @@ def test_workspace_contents_ignored():
     for name, t in runs[0].items():
         assert torch.isfinite(t.float()).all(), name
         assert torch.equal(t, runs[1][name]), name
+
+
+def test_fused_prologue_determinism_bitwise():
+    """With the q/k L2 norm and the gate chain fused (raw rows scaled per row, alpha and
+    beta_raw), two runs are bit-identical on every output."""
+    import dataclasses
+
+    import torch
+    from gdn_gpu import problem, to_device
+    from synth import round_bf16, round_f32
+
+    base = _case([300, 77], Hk=2, Hv=6, D=128, varlen=True)
+    rng = np.random.default_rng(31)
+    s = lambda: rng.uniform(0.2, 5.0, (base.T_total, base.Hk, 1))
+    case = dataclasses.replace(base, q=round_bf16(base.q * s()), k=round_bf16(base.k * s()),
+                               g=round_f32(rng.standard_normal((base.T_total, base.Hv))),
+                               beta=round_f32(rng.standard_normal((base.T_total, base.Hv))))
+    outs = []
+    for _ in range(2):
+        d = to_device(case)
+        dev = d["v"].device
+        a_log = torch.full((case.Hv,), -0.4, dtype=torch.float32, device=dev)
+        dt_bias = torch.full((case.Hv,), 0.6, dtype=torch.float32, device=dev)
+        p = problem(case, d)
+        p.qk_l2norm, p.a_log, p.dt_bias = 1, a_log.data_ptr(), dt_bias.data_ptr()
+        outs.append(run_gpu(case, d=d, p=p))
+    for name in ALL:
+        assert np.array_equal(outs[0][name], outs[1][name]), name
