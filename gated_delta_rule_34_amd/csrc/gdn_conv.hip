@@ -173,8 +173,11 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_fwd(ConvArgs a) {
   }
 }
 
-// Grid as the forward. Sweeps rows t0 .. t1 + K - 2: at row u it forms dpre[u] (from the
-// input window and dy[u]) and, once dpre[t .. t + K - 1] are known, dx[t] for t = u - K + 1.
+// Grid as the forward. Sweeps rows u = t0 .. t1 + K - 2: at row u it forms dpre[u] (from the
+// input window and dy[u]) and adds w[j] dpre[u] into the pending sum of dx[u - (K - 1) + j]
+// for every such row of u's own sequence; dx[u - (K - 1)] then has all its terms and is
+// stored (rows of the run only). Scattering each dpre row at once keeps K - 1 pending row
+// sums in registers instead of the last K rows of dpre with their sequence ends.
 template <typename TI, int K>
 __global__ __launch_bounds__(kConvThreads) void k_conv_bwd(ConvArgs a) {
   const int cg = blockIdx.y * kConvThreads + threadIdx.x;
@@ -203,23 +206,15 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_bwd(ConvArgs a) {
       for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
     }
   }
-  // dp[l] = dpre[u - (K - 1) + l]; hp[l] = end of that row's sequence (0 for rows before
-  // the run: they are never summed into a dx of the run)
-  F8 dp[K];
-  int64_t hp[K];
+  // acc[j]: the sum so far of dx[u - (K - 1) + j], j < K - 1 (rows before t0 are never stored)
+  F8 acc[K > 1 ? K - 1 : 1];
 #pragma unroll
-  for (int l = 0; l < K; ++l) {
-    hp[l] = 0;
+  for (int j = 0; j < K - 1; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dp[l].v[i] = 0.f;
-  }
+    for (int i = 0; i < 8; ++i) acc[j].v[i] = 0.f;
   const int64_t uend = t1 + K - 1 < a.rows ? t1 + K - 1 : a.rows;
   for (int64_t u = t0; u < t1 + K - 1; ++u) {
-#pragma unroll
-    for (int l = 0; l + 1 < K; ++l) {
-      dp[l] = dp[l + 1];
-      hp[l] = hp[l + 1];
-    }
+    F8 dp;  // dpre[u], zero past the last row
     if (u < uend) {
       if (u >= hi) {
         conv_seq(a, u, lo, hi);
@@ -236,31 +231,34 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_bwd(ConvArgs a) {
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) z += w[j][i] * win[j].v[i];
         const float sg = sigmoid(z);
-        dp[K - 1].v[i] = gu.v[i] * sg * (1.f + z * (1.f - sg));
+        dp.v[i] = gu.v[i] * sg * (1.f + z * (1.f - sg));
       }
-      hp[K - 1] = hi;
 #pragma unroll
       for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
       if constexpr (K > 1) win[K - 2] = xu;
-    } else {  // past the last row: nothing to add
+      // rows u - (K - 1) + j of u's sequence take w[j] dpre[u]
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dp[K - 1].v[i] = 0.f;
-      hp[K - 1] = 0;
+      for (int j = 0; j < K - 1; ++j)
+        if (u - (K - 1) + j >= lo)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[j].v[i] += w[j][i] * dp.v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dp.v[i] = 0.f;
+    }
+    F8 done;  // dx[u - (K - 1)]: complete once dpre[u] is in
+    if constexpr (K > 1) {
+      done = acc[0];
+#pragma unroll
+      for (int j = 0; j + 1 < K - 1; ++j) acc[j] = acc[j + 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[K - 2].v[i] = w[K - 1][i] * dp.v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) done.v[i] = w[0][i] * dp.v[i];
     }
     const int64_t t = u - (K - 1);
-    if (t >= t0 && t < t1) {  // dx[t]: dp[0] is row t itself
-      const int64_t end = hp[0];
-      F8 out;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int l = 0; l < K; ++l)
-          if (t + l < end) s += w[K - 1 - l][i] * dp[l].v[i];
-        out.v[i] = s;
-      }
-      st8(dx + t * a.dx_rs, out);
-    }
+    if (t >= t0) st8(dx + t * a.dx_rs, done);
   }
 }
 
