@@ -91,3 +91,16 @@ def test_conv_training_projection_sampled_channels():
     sel = np.concatenate([np.arange(g * 8, g * 8 + 8) for g in range(0, 10240 // 8, 7)])
     assert normwise(y[:, sel], conv1d_silu_fwd(cu, x[:, sel], w[sel])) < TOL["bf16"]
     assert normwise(dx[:, sel], conv1d_silu_bwd(cu, x[:, sel], w[sel], dy[:, sel])) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("K", [2, 4])
+def test_conv_sequence_starts_on_run_boundaries(K):
+    """Sequence starts at rows 32, 96 and 128 (each the first row of a thread's 32-row run),
+    empty sequences at a run start, and a one-row last sequence: the rows a run reads before
+    its start (forward window) and past its end (backward halo) belong to other sequences
+    and must not enter its sums."""
+    from oracle.conv import conv1d_silu_bwd, conv1d_silu_fwd
+
+    cu, x, w, dy, y, dx = _run("bf16", [32, 64, 0, 32, 0, 1], 520, K, seed=90 + K)
+    assert normwise(y, conv1d_silu_fwd(cu, x, w)) < TOL["bf16"]
+    assert normwise(dx, conv1d_silu_bwd(cu, x, w, dy)) < TOL["bf16"]
