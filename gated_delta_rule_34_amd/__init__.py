@@ -254,8 +254,10 @@ def _empty_bytes(n, device):
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
-def forward(p, q, k, v, g, beta, S0=None, o=None, want_final=True, workspace=None, stream=None):
-    """Allocate o, S_T and the saved chunk states, run gdn_fwd; returns (o, S_T, states)."""
+def forward(p, q, k, v, g, beta, S0=None, o=None, want_final=True, workspace=None, stream=None, save=True):
+    """Allocate o, S_T and (``save``) the saved chunk states, run gdn_fwd; returns
+    (o, S_T, states). With ``save=False`` the call is forward-only: nothing is saved for a
+    backward (states is None) and the forward's factors live in a workspace."""
     import torch
 
     dev = v.device
@@ -263,8 +265,8 @@ def forward(p, q, k, v, g, beta, S0=None, o=None, want_final=True, workspace=Non
     if o is None:
         o = torch.empty(T, p.Hv, p.Dv, dtype=v.dtype, device=dev)
     S_T = torch.empty(p.N, p.Hv, p.Dk, p.Dv, dtype=torch.float32, device=dev) if want_final else None
-    states = _empty_bytes(gdn_chunk_state_bytes(p), dev)
-    if workspace is None:
+    states = _empty_bytes(gdn_chunk_state_bytes(p), dev) if save else None
+    if workspace is None and not save:
         workspace = _empty_bytes(gdn_fwd_workspace_bytes(p), dev)
     gdn_fwd(p, q, k, v, g, beta, S0, o, S_T, states, workspace, stream)
     return o, S_T, states

@@ -75,9 +75,15 @@ Regions regions(const gdn_problem* p) {
   return r;
 }
 
-// The forward needs no workspace: its only scratch, the chunk table, is saved for the
-// backward (which then does not rebuild it).
-size_t fwd_ws(const gdn_problem*) { return 0; }
+// A forward that saves its chunk states (for a backward) needs no workspace: its only
+// scratch, the chunk table, is saved with them. A forward-only call (chunk_states NULL)
+// keeps in the workspace what prep writes and the sweep reads: the chunk table, T, M, the
+// gate record (and the normalised q, k rows with their factors), but no chunk-start states
+// and no Delta, which only the backward reads.
+size_t fwd_ws(const gdn_problem* p) {
+  const Regions r = regions(p);
+  return r.chunks + r.seq_chunk + 2 * r.oCC + r.gb + 2 * r.qn + r.rr;
+}
 
 size_t bwd_ws(const gdn_problem* p) {
   const Regions r = regions(p);
@@ -91,16 +97,20 @@ size_t saved_bytes(const gdn_problem* p) {
   return r.chunks + r.seq_chunk + r.oDD + r.oCD + 2 * r.oCC + r.gb + 2 * r.qn + r.rr;
 }
 
-void carve_saved(gdn::Prob& P, const Regions& r, void* saved) {
+// The saved-state layout (with_states) or the forward-only workspace layout (without the
+// chunk-start states and Delta: sv_S and sv_D stay null, and the forward then saves neither).
+void carve_saved(gdn::Prob& P, const Regions& r, void* saved, bool with_states = true) {
   char* b = static_cast<char*>(saved);
   P.chunks = reinterpret_cast<gdn::ChunkInfo*>(b);
   b += r.chunks;
   P.seq_chunk = reinterpret_cast<int*>(b);
   b += r.seq_chunk;
-  P.sv_S = b;
-  b += r.oDD;
-  P.sv_D = b;
-  b += r.oCD;
+  if (with_states) {
+    P.sv_S = b;
+    b += r.oDD;
+    P.sv_D = b;
+    b += r.oCD;
+  }
   P.sv_T = b;
   b += r.oCC;
   P.sv_M = b;
@@ -231,10 +241,12 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   GDN_TRY(check_f32(S_T, false, 16));
   if (p->N == 0) return GDN_OK;
   if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
-  if (!chunk_states) return GDN_EINVAL;
-  if (!aligned(chunk_states, 16)) return GDN_EALIGN;
-  (void)workspace;  // none needed (fwd_ws is 0)
-  (void)workspace_bytes;
+  if (chunk_states) {
+    if (!aligned(chunk_states, 16)) return GDN_EALIGN;  // the workspace is not used
+  } else {
+    if (!workspace || workspace_bytes < fwd_ws(p)) return GDN_EWORKSPACE;
+    if (!aligned(workspace, kAlign)) return GDN_EALIGN;
+  }
 
   gdn::Prob P;
   fill_common(P, p);
@@ -242,7 +254,8 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
   P.g = g; P.beta = beta; P.S0 = S0;
   P.o = o; P.o_rs = o_rs; P.ST = S_T;
   const Regions r = regions(p);
-  carve_saved(P, r, chunk_states);
+  if (chunk_states) carve_saved(P, r, chunk_states);
+  else carve_saved(P, r, workspace, false);
   set_qk_use(P);
   const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_EHIP;

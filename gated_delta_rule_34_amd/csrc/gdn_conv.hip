@@ -24,6 +24,18 @@ namespace gdn {
 constexpr int kConvThreads = 256;
 constexpr int kConvRun = 32;  // rows per thread
 
+// Rows [lo, hi) of sequence l from the device table, clamped so that 0 <= lo <= hi <= rows:
+// a malformed table (a negative or decreasing entry) then gives wrong sequence boundaries but
+// never a row outside the caller's buffers (every row a kernel touches is >= lo or >= its
+// run's first row, and < rows).
+__device__ __forceinline__ void conv_clamp(const ConvArgs& a, int l, int64_t& lo, int64_t& hi) {
+  int64_t x = a.cu[l], y = a.cu[l + 1];
+  x = x < 0 ? 0 : (x > a.rows ? a.rows : x);
+  y = y < x ? x : (y > a.rows ? a.rows : y);
+  lo = x;
+  hi = y;
+}
+
 // Rows [lo, hi) of the sequence that holds row t.
 __device__ __forceinline__ void conv_seq(const ConvArgs& a, int64_t t, int64_t& lo, int64_t& hi) {
   if (!a.cu) {
@@ -36,12 +48,10 @@ __device__ __forceinline__ void conv_seq(const ConvArgs& a, int64_t t, int64_t& 
     const int m = (l + r) >> 1;
     if (a.cu[m] <= t) l = m; else r = m;
   }
-  lo = a.cu[l];
-  hi = a.cu[l + 1];
+  conv_clamp(a, l, lo, hi);
   while (hi <= t && l + 1 < a.N) {  // equal offsets (empty sequences) before t's own
     ++l;
-    lo = a.cu[l];
-    hi = a.cu[l + 1];
+    conv_clamp(a, l, lo, hi);
   }
   // (hi <= t still means cu[N] < T_total, a caller error: the row is then treated as the
   // first of a sequence, and nothing outside cu[0 .. N] is read)

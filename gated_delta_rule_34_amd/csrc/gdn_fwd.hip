@@ -314,8 +314,10 @@ __device__ __forceinline__ void save_rows(OT* dst, int v0, const f32x4 (&Xc)[CT]
 __device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Grid xcd_grid(N * Hk, r): one workgroup per (sequence, value head); the r value heads
-// of a key head run on one XCD (they read the same K and Q).
-template <typename TI, int C, int D>
+// of a key head run on one XCD (they read the same K and Q). SAVE: keep the chunk-start
+// state and Delta of every chunk for the backward (off for a forward-only call, which then
+// writes only o and S_T).
+template <typename TI, int C, int D, bool SAVE>
 __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p) {
   using OT = TI;
   using CF = SwCfg<TI, C, D>;
@@ -403,7 +405,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int s = 0; s < NSD; ++s) Sb[ct][s] = from_acc<OT, KSD>(S[ct], s, Ident{});
-    save_rows<OT, D, CT, DT, NSD>((OT*)p.sv_S + ch * D * D, v0, S, Sb);  // S^T[v][d] at the chunk start
+    if constexpr (SAVE) save_rows<OT, D, CT, DT, NSD>((OT*)p.sv_S + ch * D * D, v0, S, Sb);  // S^T[v][d] at the chunk start
     // X = beta o (V - b o K S), then Delta = T X
     f32x4 X[CT][RT];
     {
@@ -431,8 +433,8 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int s = 0; s < NSC; ++s) Db[ct][s] = from_acc<OT, KSC>(Dl[ct], s, Ident{});
-    {  // Delta's columns of this wave replace the wave's own (consumed) columns of V in LDS;
-       // the full rows are written out with the output rows
+    if constexpr (SAVE) {  // Delta's columns of this wave replace the wave's own (consumed)
+                           // columns of V in LDS; the full rows are written out with the output rows
       OT* sDw = sbuf[buf] + CF::O_V;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -463,7 +465,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
           for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)(sc * O[t][ct][e]);
     }
     lds_barrier();  // the chunk's output rows and Delta rows are staged
-    {  // full output and Delta rows, 16-byte stores spread over every wave
+    {  // full output (and Delta) rows, 16-byte stores spread over every wave
       using V = Vec16<OT>;
       constexpr int VPR = D / CE;
       TI* o = (TI*)p.o + t0 * p.o_rs + h * D;
@@ -476,8 +478,9 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
         if (i < len) {
           *reinterpret_cast<typename V::type*>(o + (int64_t)i * p.o_rs + q * CE) =
               *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
-          *reinterpret_cast<typename V::type*>(dl + (q * CE / BV) * C * BV + i * BV + (q * CE) % BV) =
-              *reinterpret_cast<const typename V::type*>(sD + LD::at(i, q * CE));
+          if constexpr (SAVE)
+            *reinterpret_cast<typename V::type*>(dl + (q * CE / BV) * C * BV + i * BV + (q * CE) % BV) =
+                *reinterpret_cast<const typename V::type*>(sD + LD::at(i, q * CE));
         }
       }
     }
@@ -508,9 +511,14 @@ static hipError_t fwd_seq(const Prob& p, hipStream_t s) {
   using CF = SwCfg<TI, C, D>;
   traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
   if (p.nc_max > 0) traced("k_prep", s, [&] { k_prep<TI, C, D><<<p.nc_max * p.Hk, kPrepThreads, 0, s>>>(p); });
-  if (p.N > 0)
-    traced("k_fwd_sweep", s,
-           [&] { k_fwd_sweep<TI, C, D><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });
+  if (p.N > 0) {
+    if (p.sv_S)
+      traced("k_fwd_sweep", s,
+             [&] { k_fwd_sweep<TI, C, D, true><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });
+    else
+      traced("k_fwd_sweep_nosave", s,
+             [&] { k_fwd_sweep<TI, C, D, false><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });
+  }
   return hipGetLastError();
 }
 

@@ -97,9 +97,11 @@ typedef struct {
 } gdn_problem;
 
 /* Bytes of device workspace gdn_fwd / gdn_bwd need for this problem (0 on invalid
- * problem). The workspace is scratch: its contents on entry are ignored. gdn_fwd
- * needs none: its query returns 0 and its workspace arguments are ignored (NULL, 0
- * is fine); they stay in the signature so that callers need not change if that does. */
+ * problem). The workspace is scratch: its contents on entry are ignored, and it must be
+ * 256-byte aligned. gdn_fwd needs it only for a forward-only call (chunk_states NULL):
+ * then it holds the per-chunk factors the forward's kernels pass to one another; a
+ * forward that saves chunk states keeps them there instead and ignores its workspace
+ * arguments (NULL, 0 is fine). */
 size_t gdn_fwd_workspace_bytes(const gdn_problem* p);
 size_t gdn_bwd_workspace_bytes(const gdn_problem* p);
 
@@ -109,11 +111,14 @@ size_t gdn_bwd_workspace_bytes(const gdn_problem* p);
 size_t gdn_chunk_state_bytes(const gdn_problem* p);
 
 /*
- * Forward. Reads q, k [rows][Hk*Dk], v [rows][Hv*Dv] (dtype), g, beta [T_total][Hv]
- * (float32; 0 < g <= 1 is required by the chunked form: it works with log g), S0
- * (float32 or NULL = zeros). Writes o [rows][Hv*Dv] (dtype, row stride o_rs),
- * S_T (or NULL to skip) and chunk_states (required, gdn_chunk_state_bytes; keep it
- * unchanged for gdn_bwd).
+ * Forward: the op that returns (o, S_T) (page 2, the dormouse review log, the fused op's
+ * (o, s) result; page 3's "Forward recap"). Reads q, k [rows][Hk*Dk], v [rows][Hv*Dv]
+ * (dtype), g, beta [T_total][Hv] (float32; 0 < g <= 1 is required by the chunked form: it
+ * works with log g), S0 (float32 or NULL = zeros). Writes o [rows][Hv*Dv] (dtype, row
+ * stride o_rs) and S_T (or NULL to skip).
+ * chunk_states: gdn_chunk_state_bytes bytes (16-byte aligned) to keep what gdn_bwd needs
+ * (keep it unchanged for gdn_bwd), or NULL for a forward-only call, which saves nothing
+ * and instead needs a workspace of gdn_fwd_workspace_bytes (GDN_EWORKSPACE otherwise).
  * Alignment: q, k, v, o and the row strides times the element size must be
  * multiples of 16 bytes; S0, S_T, dS_T, dS0 need 16-byte alignment, g, beta, dg,
  * dbeta 4-byte alignment (the same rules hold for gdn_bwd).

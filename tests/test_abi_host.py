@@ -55,10 +55,13 @@ def prob(G, **kw):
 
 def test_workspace_queries(G):
     p = prob(G)
-    assert G.gdn_fwd_workspace_bytes(p) == 0  # the forward's chunk table is saved in the chunk states
+    # forward-only calls keep T, M, the gate record and the chunk table in the workspace, but
+    # not the chunk-start states and Delta that the saved buffer also holds
+    nc, Hv, C = 2 * 2, 48, 64  # two sequences of two chunks
+    assert G.gdn_fwd_workspace_bytes(p) >= nc * Hv * 2 * C * C * 2
+    assert G.gdn_fwd_workspace_bytes(p) < G.gdn_chunk_state_bytes(p) - nc * Hv * 128 * 128 * 2
     assert G.gdn_bwd_workspace_bytes(p) > 0
-    nc = 2 * 2  # two sequences of two chunks
-    assert G.gdn_chunk_state_bytes(p) >= nc * 48 * 128 * 128 * 4
+    assert G.gdn_chunk_state_bytes(p) >= nc * Hv * 128 * 128 * 2
     bigger = prob(G, T_total=512, T=256)
     assert G.gdn_bwd_workspace_bytes(bigger) > G.gdn_bwd_workspace_bytes(p)
     bad = prob(G, Hv=47)
@@ -167,7 +170,12 @@ def test_rejects_bad_views(G):
     assert status_of(G, p, v=FakeTensor(0x30000, T, 6144, 10241)) == G.GDN_EALIGN  # stride * 2 B % 16
     assert status_of(G, p, g=FakeTensor(0x40002, T, 48)) == G.GDN_EALIGN
     assert status_of(G, p, beta=None) == G.GDN_EINVAL
-    assert status_of(G, p, chunk_states=None) == G.GDN_EINVAL
+    # forward-only (no chunk states): the workspace must hold gdn_fwd_workspace_bytes
+    assert status_of(G, p, chunk_states=None) == G.GDN_EWORKSPACE
+    assert status_of(G, p, chunk_states=None, workspace=None) == G.GDN_EWORKSPACE
+    big = G.gdn_fwd_workspace_bytes(p)
+    assert status_of(G, p, chunk_states=None, workspace=FakeTensor(0x80010, 1, 1, nbytes=big)) == G.GDN_EALIGN
+    assert status_of(G, p, chunk_states=FakeTensor(0x70008, 1, 1)) == G.GDN_EALIGN
 
 
 def decode_status_of(G, p, n_slots=None, **over):
