@@ -141,8 +141,8 @@ def summarize_counters(out_path, dirs, command):
     """Write a counter summary for the gdn kernels: per kernel the median of each counter over
     its dispatches (the plain training step; repeated identical dispatches agree to <1%). With
     FETCH_SIZE / WRITE_SIZE the calibrated HBM bytes (scaled by the counts of the calibration
-    copy of CALIB_BYTES); with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE the MFMA busy
-    fraction of the chip over the kernel's dispatches."""
+    copy of CALIB_BYTES); with rocprofv3's derived MfmaUtil the MFMA busy fraction of the
+    chip's SIMDs over the kernel's dispatches."""
     counters = {}
     for d in dirs:
         counters.update(_read_counters(d))
@@ -182,16 +182,17 @@ def summarize_counters(out_path, dirs, command):
             b = med["FETCH_SIZE"] * 1024 * scales["FETCH_SIZE"] + med["WRITE_SIZE"] * 1024 * scales["WRITE_SIZE"]
             ent["hbm_bytes"] = int(b)
             derived.append(f"HBM {b / 1e6:.1f} MB")
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
-            f = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * N_CU * SIMD_PER_CU)
-            ent["mfma_busy"] = round(f, 4)
-            derived.append(f"MFMA busy {100 * f:.1f}%")
+        if "MfmaUtil" in med:  # rocprofv3's derived counter: MFMA busy cycles / (GPU busy cycles x SIMDs)
+            ent["mfma_busy"] = round(med["MfmaUtil"] / 100.0, 4)
+            derived.append(f"MFMA busy {med['MfmaUtil']:.1f}%")
         if "SQ_INSTS_VALU" in med and med.get("SQ_INSTS_MFMA"):
             ent["valu_per_mfma"] = round(med["SQ_INSTS_VALU"] / med["SQ_INSTS_MFMA"], 2)
             derived.append(f"VALU/MFMA {ent['valu_per_mfma']}")
         if "SQ_LDS_BANK_CONFLICT" in med and med.get("SQ_LDS_IDX_ACTIVE"):
             ent["lds_conflict_frac"] = round(med["SQ_LDS_BANK_CONFLICT"] / med["SQ_LDS_IDX_ACTIVE"], 4)
-            derived.append(f"LDS conflict {100 * ent['lds_conflict_frac']:.1f}%")
+            derived.append(f"LDS cycles in conflicts {100 * ent['lds_conflict_frac']:.1f}%")
+        if "LdsUtil" in med:
+            derived.append(f"LDS busy {med['LdsUtil']:.1f}%")
         summary["kernels"][k] = ent
         n = max(len(v) for v in agg[k].values())
         lines.append(f"| {k} | {n} | " + " | ".join(f"{med.get(c, float('nan')):.0f}" for c in names) +

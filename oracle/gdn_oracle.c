@@ -19,11 +19,11 @@
  * h / (Hv/Hk) (same page: "key-head k_head = h / ratio"). The state is stored
  * key-major, S[i*Dv + j], i = key index, j = value index, as on that page.
  *
- * The backward follows the same page's gdn_backward, steps 4a-4d (output,
- * state update, delta, retrieval), run in reverse time with the state adjoint
- * dS carried across tokens. Two generalisations of that page, which starts from
- * S = 0 and dS = 0: the initial state S0 and the incoming adjoint dS_T may be
- * non-zero (NULL means zero), and dS0 is returned. dq and dk of a key head are
+ * The backward is the reverse-mode adjoint of that recurrence, derived here from
+ * its Householder form (see run_backward_head), run in reverse time with the state
+ * adjoint carried across tokens. The page's backward starts from S = 0 and dS = 0;
+ * here the initial state S0 and the incoming adjoint dS_T may be non-zero (NULL
+ * means zero), and dS0 is returned. dq and dk of a key head are
  * the sums of the per-value-head contributions over the value heads that read
  * it, added in ascending head order (step 4g of that page; and page 1, the
  * llama.cpp fork's "delta-net backward at the shape the 27B emits", which
@@ -113,123 +113,143 @@ static void run_forward_head(job_t* J, int n, int h, double* S, double* kv, doub
 }
 
 /*
- * Reverse-time backward of one (sequence, value head). dq/dk of this head are
- * added into dq/dk of its key head (the caller walks the heads of a group in
- * ascending order). Buffers: ckpt holds S at every SEG boundary, segS the
- * states before each token of the current segment plus the state after it.
+ * Reverse-time backward of one (sequence, value head), as the adjoint of the recurrence
+ * regrouped in its Householder form (the same map as the forward above):
+ *
+ *   S_t = g_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,    o_t = scale S_t^T q_t.
+ *
+ * Let A = dL/dS_t, the adjoint of the state after token t (o_t's own term included),
+ * u = S_{t-1}^T k_t and w = A^T k_t (both Dv vectors). Differentiating the map term by term:
+ *
+ *   dq_t   = scale S_t dO_t                          (from o_t)
+ *   dv_t   = beta_t w                                (from beta k v^T)
+ *   dbeta  = w . (v_t - g_t u)                       (from -g beta k u^T + beta k v^T)
+ *   dg     = <S_{t-1}, A> - beta_t (u . w)           (from g (I - beta k k^T) S_{t-1})
+ *   dk_t   = beta_t A (v_t - g_t u) - g_t beta_t S_{t-1} w
+ *            (k enters twice in -g beta k k^T S_{t-1}, once in beta k v^T)
+ *   dL/dS_{t-1} = g_t (I - beta_t k_t k_t^T) A = g_t (A - beta_t k_t w^T)
+ *
+ * The adjoint starts from dS_T (zero when absent) and ends as dS0. dq and dk of this head
+ * are added into those of its key head (the caller walks the heads of a group in
+ * ascending order).
  */
+
+/* States of tokens a .. b-1 of one segment, recomputed from the segment's checkpoint:
+ * st[r] is the state before token a + r, st[b - a] the state after the last token. */
+static void segment_states(job_t* J, int h, int kh, int64_t a, int64_t b, const double* ckpt, double* st,
+                           double* kv, double* delta) {
+  const int Hk = J->Hk, Hv = J->Hv, Dk = J->Dk, Dv = J->Dv;
+  const size_t SS = (size_t)Dk * Dv;
+  memcpy(st, ckpt, SS * sizeof(double));
+  for (int64_t t = a; t < b; ++t) {
+    double* next = st + (size_t)(t - a + 1) * SS;
+    memcpy(next, st + (size_t)(t - a) * SS, SS * sizeof(double));
+    step_forward(next, J->k + ((size_t)t * Hk + kh) * Dk, J->v + ((size_t)t * Hv + h) * Dv,
+                 J->g[(size_t)t * Hv + h], J->beta[(size_t)t * Hv + h], kv, delta, Dk, Dv);
+  }
+}
+
+/* One token of the adjoint: A holds dL/dS_t without o_t's term on entry and dL/dS_{t-1} on
+ * return. Sp = S_{t-1}, Sn = S_t. u, w, r are Dv scratch vectors; dqh, dkh receive this
+ * head's dq_t, dk_t. */
+static void adjoint_token(job_t* J, int64_t t, int h, int kh, const double* Sp, const double* Sn, double* A,
+                          double* u, double* w, double* r, double* dqh, double* dkh) {
+  const int Hk = J->Hk, Hv = J->Hv, Dk = J->Dk, Dv = J->Dv;
+  const double* k = J->k + ((size_t)t * Hk + kh) * Dk;
+  const double* q = J->q + ((size_t)t * Hk + kh) * Dk;
+  const double* v = J->v + ((size_t)t * Hv + h) * Dv;
+  const double* dO = J->dO + ((size_t)t * Hv + h) * Dv;
+  const double gt = J->g[(size_t)t * Hv + h], bt = J->beta[(size_t)t * Hv + h], sc = J->scale;
+
+  /* o_t = scale S_t^T q: its adjoint joins A, and dq_t = scale S_t dO_t */
+  for (int i = 0; i < Dk; ++i) {
+    double s = 0.0;
+    for (int j = 0; j < Dv; ++j) {
+      A[i * Dv + j] += sc * q[i] * dO[j];
+      s += Sn[i * Dv + j] * dO[j];
+    }
+#if defined(ORACLE_PLANT) && ORACLE_PLANT == 4
+    dqh[i] = s; /* planted mistake: the scale of dq dropped */
+#else
+    dqh[i] = sc * s;
+#endif
+  }
+
+  /* u = S_{t-1}^T k, w = A^T k, r = v - g u */
+  for (int j = 0; j < Dv; ++j) u[j] = w[j] = 0.0;
+  for (int i = 0; i < Dk; ++i)
+    for (int j = 0; j < Dv; ++j) {
+      u[j] += Sp[i * Dv + j] * k[i];
+      w[j] += A[i * Dv + j] * k[i];
+    }
+  double uw = 0.0, wr = 0.0, SA = 0.0;
+  for (int j = 0; j < Dv; ++j) {
+    r[j] = v[j] - gt * u[j];
+    uw += u[j] * w[j];
+    wr += w[j] * r[j];
+  }
+  for (size_t ij = 0; ij < (size_t)Dk * Dv; ++ij) SA += Sp[ij] * A[ij];
+
+  double* dv = J->dv + ((size_t)t * Hv + h) * Dv;
+  for (int j = 0; j < Dv; ++j) dv[j] = bt * w[j];
+  J->dbeta[(size_t)t * Hv + h] = wr;
+#if defined(ORACLE_PLANT) && ORACLE_PLANT == 3
+  J->dg[(size_t)t * Hv + h] = SA + bt * uw; /* planted mistake: sign of the k k^T term */
+#else
+  J->dg[(size_t)t * Hv + h] = SA - bt * uw;
+#endif
+  for (int i = 0; i < Dk; ++i) {
+    double ar = 0.0, sw = 0.0;
+    for (int j = 0; j < Dv; ++j) {
+      ar += A[i * Dv + j] * r[j];
+      sw += Sp[i * Dv + j] * w[j];
+    }
+#if defined(ORACLE_PLANT) && ORACLE_PLANT == 2
+    dkh[i] = bt * ar; /* planted mistake: the k of k^T S_{t-1} (the retrieval) dropped */
+    (void)sw;
+#else
+    dkh[i] = bt * ar - gt * bt * sw;
+#endif
+  }
+
+  /* dL/dS_{t-1} = g (A - beta k w^T) */
+  for (int i = 0; i < Dk; ++i)
+    for (int j = 0; j < Dv; ++j) A[i * Dv + j] = gt * (A[i * Dv + j] - bt * k[i] * w[j]);
+}
+
 static void run_backward_head(job_t* J, int n, int h, double* ckpt, double* segS, double* dS,
-                              double* kv, double* delta, double* ddelta, double* dkv,
-                              double* dqh, double* dkh) {
+                              double* kv, double* delta, double* u, double* w, double* dqh, double* dkh) {
   const int Hk = J->Hk, Hv = J->Hv, Dk = J->Dk, Dv = J->Dv;
   const int kh = key_head_of(h, Hk, Hv);
   const size_t SS = (size_t)Dk * Dv;
   const int64_t t0 = J->cu[n], t1 = J->cu[n + 1];
-  const int64_t len = t1 - t0;
-  const int64_t nseg = (len + SEG - 1) / SEG;
+  const int64_t nseg = (t1 - t0 + SEG - 1) / SEG;
 
-  /* forward re-run keeping a copy of S at the start of every segment */
-  double* S = segS; /* scratch for the re-run */
+  /* a forward run keeping the state at the start of every segment of SEG tokens */
+  double* S = segS;
   if (J->S0) memcpy(S, J->S0 + ((size_t)n * Hv + h) * SS, SS * sizeof(double));
   else memset(S, 0, SS * sizeof(double));
   for (int64_t s = 0; s < nseg; ++s) {
     memcpy(ckpt + (size_t)s * SS, S, SS * sizeof(double));
-    int64_t a = t0 + s * SEG, b = a + SEG < t1 ? a + SEG : t1;
-    for (int64_t t = a; t < b; ++t) {
-      const double* kt = J->k + ((size_t)t * Hk + kh) * Dk;
-      const double* vt = J->v + ((size_t)t * Hv + h) * Dv;
-      step_forward(S, kt, vt, J->g[(size_t)t * Hv + h], J->beta[(size_t)t * Hv + h], kv, delta, Dk, Dv);
-    }
+    const int64_t a = t0 + s * SEG, b = a + SEG < t1 ? a + SEG : t1;
+    for (int64_t t = a; t < b; ++t)
+      step_forward(S, J->k + ((size_t)t * Hk + kh) * Dk, J->v + ((size_t)t * Hv + h) * Dv,
+                   J->g[(size_t)t * Hv + h], J->beta[(size_t)t * Hv + h], kv, delta, Dk, Dv);
   }
 
   if (J->dST) memcpy(dS, J->dST + ((size_t)n * Hv + h) * SS, SS * sizeof(double));
   else memset(dS, 0, SS * sizeof(double));
-
   for (int64_t s = nseg - 1; s >= 0; --s) {
-    int64_t a = t0 + s * SEG, b = a + SEG < t1 ? a + SEG : t1;
-    /* segS[r] = state before token a+r; segS[b-a] = state after the last token */
-    memcpy(segS, ckpt + (size_t)s * SS, SS * sizeof(double));
-    for (int64_t t = a; t < b; ++t) {
-      double* Snext = segS + (size_t)(t - a + 1) * SS;
-      memcpy(Snext, segS + (size_t)(t - a) * SS, SS * sizeof(double));
-      const double* kt = J->k + ((size_t)t * Hk + kh) * Dk;
-      const double* vt = J->v + ((size_t)t * Hv + h) * Dv;
-      step_forward(Snext, kt, vt, J->g[(size_t)t * Hv + h], J->beta[(size_t)t * Hv + h], kv, delta, Dk, Dv);
-    }
+    const int64_t a = t0 + s * SEG, b = a + SEG < t1 ? a + SEG : t1;
+    segment_states(J, h, kh, a, b, ckpt + (size_t)s * SS, segS, kv, delta);
     for (int64_t t = b - 1; t >= a; --t) {
-      const double* Sprev = segS + (size_t)(t - a) * SS;
-      const double* St = segS + (size_t)(t - a + 1) * SS;
-      const double* kt = J->k + ((size_t)t * Hk + kh) * Dk;
-      const double* qt = J->q + ((size_t)t * Hk + kh) * Dk;
-      const double* vt = J->v + ((size_t)t * Hv + h) * Dv;
-      const double* dot = J->dO + ((size_t)t * Hv + h) * Dv;
-      const double gt = J->g[(size_t)t * Hv + h];
-      const double bt = J->beta[(size_t)t * Hv + h];
-      const double sc = J->scale;
-
-      /* recompute kv = S_{t-1}^T k and delta */
-      for (int j = 0; j < Dv; ++j) kv[j] = 0.0;
-      for (int i = 0; i < Dk; ++i)
-        for (int j = 0; j < Dv; ++j) kv[j] += Sprev[i * Dv + j] * kt[i];
-      for (int j = 0; j < Dv; ++j) delta[j] = bt * (vt[j] - gt * kv[j]);
-
-      /* 4a: o = scale * S_t^T q  ->  dS += scale * q (x) dO ; dq = scale * S_t dO */
+      adjoint_token(J, t, h, kh, segS + (size_t)(t - a) * SS, segS + (size_t)(t - a + 1) * SS, dS, u, w, kv,
+                    dqh, dkh);
+      double* dq = J->dq + ((size_t)t * Hk + kh) * Dk;
+      double* dk = J->dk + ((size_t)t * Hk + kh) * Dk;
       for (int i = 0; i < Dk; ++i) {
-        double acc = 0.0;
-        for (int j = 0; j < Dv; ++j) {
-          dS[i * Dv + j] += sc * qt[i] * dot[j];
-          acc += St[i * Dv + j] * dot[j];
-        }
-#if defined(ORACLE_PLANT) && ORACLE_PLANT == 4
-        dqh[i] = acc; /* planted mistake: scale dropped from dq */
-#else
-        dqh[i] = sc * acc;
-#endif
-      }
-
-      /* 4b: S_t = g S_{t-1} + k (x) delta */
-      double dgt = 0.0;
-      for (int i = 0; i < Dk; ++i) dkh[i] = 0.0;
-      for (int j = 0; j < Dv; ++j) ddelta[j] = 0.0;
-      for (int i = 0; i < Dk; ++i)
-        for (int j = 0; j < Dv; ++j) {
-          const double d = dS[i * Dv + j];
-          dgt += Sprev[i * Dv + j] * d;
-          dkh[i] += d * delta[j];
-          ddelta[j] += d * kt[i];
-        }
-      for (size_t ij = 0; ij < SS; ++ij) dS[ij] *= gt;
-
-      /* 4c: delta = beta (v - g kv) */
-      double dbt = 0.0;
-      double* dvt = J->dv + ((size_t)t * Hv + h) * Dv;
-      for (int j = 0; j < Dv; ++j) {
-        dvt[j] = bt * ddelta[j];
-        dkv[j] = -gt * bt * ddelta[j];
-#if defined(ORACLE_PLANT) && ORACLE_PLANT == 3
-        dgt += (kv[j] * bt) * ddelta[j]; /* planted mistake: sign */
-#else
-        dgt += (-kv[j] * bt) * ddelta[j];
-#endif
-        dbt += (vt[j] - gt * kv[j]) * ddelta[j];
-      }
-
-      /* 4d: kv = S_{t-1}^T k */
-      for (int i = 0; i < Dk; ++i)
-        for (int j = 0; j < Dv; ++j) {
-          dS[i * Dv + j] += kt[i] * dkv[j];
-#if !(defined(ORACLE_PLANT) && ORACLE_PLANT == 2)
-          dkh[i] += Sprev[i * Dv + j] * dkv[j]; /* (plant 2 drops this term) */
-#endif
-        }
-
-      J->dg[(size_t)t * Hv + h] = dgt;
-      J->dbeta[(size_t)t * Hv + h] = dbt;
-      double* dqt = J->dq + ((size_t)t * Hk + kh) * Dk;
-      double* dkt = J->dk + ((size_t)t * Hk + kh) * Dk;
-      for (int i = 0; i < Dk; ++i) {
-        dqt[i] += dqh[i];
-        dkt[i] += dkh[i];
+        dq[i] += dqh[i];
+        dk[i] += dkh[i];
       }
     }
   }
@@ -255,7 +275,7 @@ static void* worker(void* arg) {
     free(S); free(ckpt); free(segS); free(dS); free(vec);
     return NULL;
   }
-  double *kv = vec, *delta = vec + Dm, *ddelta = vec + 2 * Dm, *dkv = vec + 3 * Dm;
+  double *kv = vec, *delta = vec + Dm, *u = vec + 2 * Dm, *w = vec + 3 * Dm;
   double *dqh = vec + 4 * Dm, *dkh = vec + 5 * Dm;
   for (;;) {
     int it = take_item(J);
@@ -264,7 +284,7 @@ static void* worker(void* arg) {
     /* the value heads of key head kh, in ascending order */
     for (int h = 0; h < J->Hv; ++h) {
       if (key_head_of(h, J->Hk, J->Hv) != kh) continue;
-      if (J->backward) run_backward_head(J, n, h, ckpt, segS, dS, kv, delta, ddelta, dkv, dqh, dkh);
+      if (J->backward) run_backward_head(J, n, h, ckpt, segS, dS, kv, delta, u, w, dqh, dkh);
       else run_forward_head(J, n, h, S, kv, delta);
     }
   }
