@@ -15,8 +15,13 @@ resume. ``gdn_decode`` (one step per row, state slots) is the forward over one-t
 sequences; its own pins replay the hand-worked example token by token and check the
 slot map against per-row forwards. ``gate_chain`` / ``gate_chain_grads`` (the layer's
 g = exp(-exp(a_log) softplus(alpha + dt_bias)), beta = sigmoid(beta_raw) and their
-derivatives) are pinned to torch autograd of the same formulas and to finite differences,
-and so are ``l2norm_rows`` / ``l2norm_rows_grad`` (the q/k normalisation and its backward). No function here is "parity unpinned".
+derivatives) and ``l2norm_rows`` / ``l2norm_rows_grad`` (the q/k normalisation and its
+backward) are pinned to values worked by hand from the page's formulas
+(``tests/golden/gate_chain_l2norm.json``: a_log = 0 or +-ln 2 with alpha + dt_bias = 0 or
+ln 3 give g = 1/2 or 1/4; the series of (1 + eps/|x|^2)^(-1/2) for the norm), with planted
+mistakes (the epsilon outside the root, exp dropped on a_log, dt_bias dropped, ...) that must
+fail them; their gradients are also checked against finite differences. No function here is
+"parity unpinned".
 """
 from __future__ import annotations
 

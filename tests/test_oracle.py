@@ -509,3 +509,120 @@ def test_l2norm_rows_matches_torch_autograd():
     (th * torch.tensor(dxh)).sum().backward()
     assert np.max(np.abs(th.detach().numpy() - xh)) < 1e-14
     assert np.max(np.abs(tx.grad.numpy() - dx)) < 1e-12
+
+
+# --- hand-worked values of the gate chain and the L2 norm (tests/golden/gate_chain_l2norm.json)
+
+def _num(s):
+    """A number of the golden file: a decimal or fraction string, or ln2 / ln3 forms."""
+    import math
+
+    s = str(s)
+    named = {"ln2": math.log(2.0), "-ln2": -math.log(2.0), "ln3": math.log(3.0), "-ln3": -math.log(3.0),
+             "ln3-1/2": math.log(3.0) - 0.5}
+    return named[s] if s in named else float(Fraction(s))
+
+
+def _gate_golden():
+    with open(os.path.join(GOLDEN, "gate_chain_l2norm.json")) as f:
+        return json.load(f)
+
+
+def _gate_chain_errors(gate_chain, gate_chain_grads):
+    """Largest absolute errors of a gate_chain / gate_chain_grads pair on the golden rows."""
+    fx = _gate_golden()["gate_chain"]
+    col = lambda k: np.array([_num(x) for x in fx[k]])
+    a_log, dt_bias, alpha, beta_raw = col("a_log"), col("dt_bias"), col("alpha")[None, :], col("beta_raw")[None, :]
+    g, beta = gate_chain(alpha, a_log, dt_bias, beta_raw)
+    da, dbr = gate_chain_grads(alpha, a_log, dt_bias, beta_raw, np.ones_like(alpha), np.ones_like(beta_raw))
+    got = dict(g=g[0], beta=beta[0], dalpha=da[0], dbeta_raw=dbr[0])
+    return {k: float(np.max(np.abs(got[k] - col(k)))) for k in got}
+
+
+def _l2norm_errors(l2norm_rows, l2norm_rows_grad):
+    """Largest relative errors of an l2norm_rows / l2norm_rows_grad pair on the golden rows."""
+    fx = _gate_golden()["l2norm"]
+    errs = {"r": 0.0, "x_hat": 0.0, "dx": 0.0}
+    rel = lambda a, b: float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-300))) if np.any(b) else float(np.max(np.abs(a)))
+    for row in fx["rows"]:
+        xh, r = l2norm_rows(np.array(row["x"], np.float64)[None, :])
+        errs["r"] = max(errs["r"], rel(r[0, 0], _num(row["r"])))
+        errs["x_hat"] = max(errs["x_hat"], rel(xh[0], np.array([_num(v) for v in row["x_hat"]])))
+    for row in fx["grad"]:
+        xh, r = l2norm_rows(np.array(row["x"], np.float64)[None, :])
+        dx = l2norm_rows_grad(xh, r, np.array(row["dx_hat"], np.float64)[None, :])
+        errs["dx"] = max(errs["dx"], rel(dx[0], np.array([_num(v) for v in row["dx"]])))
+    return errs
+
+
+def test_gate_chain_hand_worked_values():
+    """g, beta and their derivatives at the golden rows, worked by hand from the page's
+    formulas (a_log = 0 or +-ln 2 and alpha + dt_bias = 0 or ln 3 give g = 1/2 or 1/4)."""
+    errs = _gate_chain_errors(oracle.gate_chain, oracle.gate_chain_grads)
+    assert all(v < 1e-15 for v in errs.values()), errs
+
+
+def test_l2norm_hand_worked_values():
+    """r, x_hat and the backward at the golden rows, from the series of (1 + eps / |x|^2)^(-1/2)
+    (the epsilon inside the square root decides the eighth significant digit of (3, 4) / 5)."""
+    errs = _l2norm_errors(oracle.l2norm_rows, oracle.l2norm_rows_grad)
+    assert all(v < 1e-15 for v in errs.values()), errs
+
+
+def _mutant(fn, old, new, extra=None):
+    """fn rebuilt from its source with one textual change (a planted mistake)."""
+    import inspect
+    import textwrap
+
+    src = textwrap.dedent(inspect.getsource(fn))
+    assert old in src, (fn.__name__, old)
+    ns = {"np": np}
+    ns.update(extra or {})
+    exec(compile(src.replace(old, new, 1), f"<mutant {fn.__name__}>", "exec"), ns)
+    return ns[fn.__name__]
+
+
+GATE_MUTANTS = [
+    ("gate_chain", "np.exp(-np.exp(a_log)[None, :] * softplus)", "np.exp(-a_log[None, :] * softplus)"),  # exp dropped on a_log
+    ("gate_chain", "alpha + dt_bias[None, :]", "alpha"),  # dt_bias dropped
+    ("gate_chain", "np.logaddexp(0.0, alpha + dt_bias[None, :])", "np.log1p(alpha + dt_bias[None, :])"),  # not softplus
+    ("gate_chain", "np.exp(-np.exp(a_log)", "np.exp(np.exp(a_log)"),  # sign
+    ("gate_chain", "np.exp(-beta_raw)", "np.exp(beta_raw)"),  # sigmoid of -beta_raw
+    ("gate_chain_grads", "* sig", ""),  # softplus' derivative dropped
+    ("gate_chain_grads", "(-np.exp(a_log)[None, :])", "(-a_log[None, :])"),
+    ("gate_chain_grads", "dbeta * beta * (1.0 - beta)", "dbeta * beta"),
+]
+
+
+@pytest.mark.parametrize("fn,old,new", GATE_MUTANTS, ids=[f"{m[0]}-{i}" for i, m in enumerate(GATE_MUTANTS)])
+def test_gate_chain_planted_mistake_is_caught(fn, old, new):
+    gc, gg = oracle.gate_chain, oracle.gate_chain_grads
+    if fn == "gate_chain":
+        gc = _mutant(gc, old, new)
+        gg = _mutant(gg, "g, beta = gate_chain(", "g, beta = gate_chain(", {"gate_chain": gc})
+    else:
+        gg = _mutant(gg, old, new, {"gate_chain": gc})
+    errs = _gate_chain_errors(gc, gg)
+    assert max(errs.values()) > 1e-6, errs
+
+
+L2_MUTANTS = [
+    ("l2norm_rows", "np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-6)",
+     "(np.sqrt(np.sum(x * x, axis=-1, keepdims=True)) + 1e-6)"),  # epsilon outside the root
+    ("l2norm_rows", "keepdims=True) + 1e-6)", "keepdims=True))"),  # epsilon dropped
+    ("l2norm_rows", "1.0 / np.sqrt(", "1.0 / ("),  # squared norm instead of norm
+    ("l2norm_rows_grad", "dx_hat - x_hat * np.sum(x_hat * dx_hat, axis=-1, keepdims=True)", "dx_hat"),  # projection dropped
+    ("l2norm_rows_grad", "return r * (", "return ("),  # factor r dropped
+]
+
+
+@pytest.mark.parametrize("fn,old,new", L2_MUTANTS, ids=[f"{m[0]}-{i}" for i, m in enumerate(L2_MUTANTS)])
+def test_l2norm_planted_mistake_is_caught(fn, old, new):
+    ln, lg = oracle.l2norm_rows, oracle.l2norm_rows_grad
+    if fn == "l2norm_rows":
+        ln = _mutant(ln, old, new)
+    else:
+        lg = _mutant(lg, old, new)
+    with np.errstate(all="ignore"):  # (a mutant may divide the zero row by zero)
+        errs = _l2norm_errors(ln, lg)
+    assert not max(errs.values()) <= 1e-9, errs
