@@ -16,7 +16,9 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgdn.so")
+# GDN_LIBRARY may name another build of the same C ABI (the host-only sanitizer build of the
+# argument checks, for instance); by default the in-tree libgdn.so is loaded.
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4, -5
 GDN_F32, GDN_BF16 = 0, 1

@@ -34,14 +34,18 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "gdn_oracle.c")
-LIB = os.path.join(_HERE, "libgdn_oracle.so")
+# GDN_ORACLE_LIBRARY may name another build of gdn_oracle.c (the sanitizer build, for instance).
+LIB = os.environ.get("GDN_ORACLE_LIBRARY") or os.path.join(_HERE, "libgdn_oracle.so")
 
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC", "-pthread"]
 
 
 def build(out: str = LIB, plant: Optional[int] = None) -> str:
     """Compile the oracle with gcc. ``plant`` builds a deliberately broken
-    variant (used only by the falsification test)."""
+    variant (used only by the falsification test). A build named by GDN_ORACLE_LIBRARY is
+    used as it is (not rebuilt)."""
+    if out == LIB and plant is None and os.environ.get("GDN_ORACLE_LIBRARY"):
+        return out
     cmd = ["gcc", *_CFLAGS, SRC, "-o", out]
     if plant is not None:
         cmd.insert(1, f"-DORACLE_PLANT={int(plant)}")
