@@ -23,7 +23,7 @@ LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4, -5
 GDN_F32, GDN_BF16 = 0, 1
 
-EXPORTED = ("gdn_fwd", "gdn_bwd", "gdn_decode", "gdn_conv1d_silu_fwd", "gdn_conv1d_silu_bwd",
+EXPORTED = ("gdn_fwd", "gdn_fwd_noalloc", "gdn_bwd", "gdn_decode", "gdn_conv1d_silu_fwd", "gdn_conv1d_silu_bwd",
             "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_chunk_state_bytes", "gdn_strerror",
             "gdn_trace_enable", "gdn_trace_collect")
 
@@ -77,6 +77,8 @@ def _load():
         fn.restype = SZ
     lib.gdn_fwd.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, P, I64, P, P, P, SZ, P]
     lib.gdn_fwd.restype = ctypes.c_int
+    lib.gdn_fwd_noalloc.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, P, I64, P, P]
+    lib.gdn_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_bwd.argtypes = [prob, P, I64, P, I64, P, I64, P, P, P, P, P, I64, P,
                             P, I64, P, I64, P, I64, P, P, P, P, SZ, P]
     lib.gdn_bwd.restype = ctypes.c_int
@@ -187,6 +189,18 @@ def gdn_fwd(p, q, k, v, g, beta, S0, o, S_T, chunk_states, workspace, stream=Non
                       _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_fwd")
+
+
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gdn_fwd_noalloc(p, q, k, v, g, beta, S0, o, S_T, stream=None):
+    """Call gdn_fwd_noalloc (forward-only, workspace in the library's fixed per-GPU scratch)."""
+    qk, vw = p.Hk * p.Dk, p.Hv * p.Dv
+    st = _lib.gdn_fwd_noalloc(ctypes.byref(p), _ptr(q), _rs(q, qk), _ptr(k), _rs(k, qk), _ptr(v), _rs(v, vw),
+                              _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _rs(o, vw), _ptr(S_T), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_fwd_noalloc")
 
 
 def gdn_bwd(p, q, k, v, g, beta, S0, chunk_states, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_decode.hip", "gdn_conv.hip", "gdn_abi.cpp", "gdn_trace.cpp"]
+SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_decode.hip", "gdn_conv.hip", "gdn_scratch.hip", "gdn_abi.cpp",
+           "gdn_trace.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-FP32 instructions are disabled for every device pass.

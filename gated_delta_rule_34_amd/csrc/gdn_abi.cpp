@@ -214,6 +214,41 @@ gdn_status conv_common(const gdn_conv_problem* p, const void* x, int64_t x_rs, c
   return GDN_OK;
 }
 
+// gdn_fwd's checks of everything but the saved buffer and the workspace.
+gdn_status check_fwd_views(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                           const void* v, int64_t v_rs, const float* g, const float* beta, const float* S0,
+                           const void* o, int64_t o_rs, const float* S_T) {
+  GDN_TRY(check_problem(p));
+  const int es = p->dtype == GDN_BF16 ? 2 : 4;
+  const int64_t qkw = (int64_t)p->Hk * p->Dk, vw = (int64_t)p->Hv * p->Dv;
+  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total, p->chunk));
+  GDN_TRY(check_view(o, o_rs, vw, es, p->T_total, p->chunk));
+  GDN_TRY(check_f32(g, p->T_total > 0));
+  GDN_TRY(check_f32(beta, p->T_total > 0));
+  GDN_TRY(check_f32(S0, false, 16));
+  GDN_TRY(check_f32(S_T, false, 16));
+  if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
+  return GDN_OK;
+}
+
+gdn_status fwd_launch(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                      const void* v, int64_t v_rs, const float* g, const float* beta, const float* S0, void* o,
+                      int64_t o_rs, float* S_T, void* chunk_states, void* workspace, void* stream) {
+  gdn::Prob P;
+  fill_common(P, p);
+  P.q = q; P.q_rs = q_rs; P.k = k; P.k_rs = k_rs; P.v = v; P.v_rs = v_rs;
+  P.g = g; P.beta = beta; P.S0 = S0;
+  P.o = o; P.o_rs = o_rs; P.ST = S_T;
+  const Regions r = regions(p);
+  if (chunk_states) carve_saved(P, r, chunk_states);
+  else carve_saved(P, r, workspace, false);
+  set_qk_use(P);
+  const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,37 +263,26 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, int64_t q_rs, const void
                    const void* v, int64_t v_rs, const float* g, const float* beta, const float* S0, void* o,
                    int64_t o_rs, float* S_T, void* chunk_states, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  GDN_TRY(check_problem(p));
-  const int es = p->dtype == GDN_BF16 ? 2 : 4;
-  const int64_t qkw = (int64_t)p->Hk * p->Dk, vw = (int64_t)p->Hv * p->Dv;
-  GDN_TRY(check_view(q, q_rs, qkw, es, p->T_total, p->chunk));
-  GDN_TRY(check_view(k, k_rs, qkw, es, p->T_total, p->chunk));
-  GDN_TRY(check_view(v, v_rs, vw, es, p->T_total, p->chunk));
-  GDN_TRY(check_view(o, o_rs, vw, es, p->T_total, p->chunk));
-  GDN_TRY(check_f32(g, p->T_total > 0));
-  GDN_TRY(check_f32(beta, p->T_total > 0));
-  GDN_TRY(check_f32(S0, false, 16));
-  GDN_TRY(check_f32(S_T, false, 16));
+  GDN_TRY(check_fwd_views(p, q, q_rs, k, k_rs, v, v_rs, g, beta, S0, o, o_rs, S_T));
   if (p->N == 0) return GDN_OK;
-  if (p->cu_seqlens && !aligned(p->cu_seqlens, 4)) return GDN_EALIGN;
   if (chunk_states) {
     if (!aligned(chunk_states, 16)) return GDN_EALIGN;  // the workspace is not used
   } else {
     if (!workspace || workspace_bytes < fwd_ws(p)) return GDN_EWORKSPACE;
     if (!aligned(workspace, kAlign)) return GDN_EALIGN;
   }
+  return fwd_launch(p, q, q_rs, k, k_rs, v, v_rs, g, beta, S0, o, o_rs, S_T, chunk_states, workspace, stream);
+}
 
-  gdn::Prob P;
-  fill_common(P, p);
-  P.q = q; P.q_rs = q_rs; P.k = k; P.k_rs = k_rs; P.v = v; P.v_rs = v_rs;
-  P.g = g; P.beta = beta; P.S0 = S0;
-  P.o = o; P.o_rs = o_rs; P.ST = S_T;
-  const Regions r = regions(p);
-  if (chunk_states) carve_saved(P, r, chunk_states);
-  else carve_saved(P, r, workspace, false);
-  set_qk_use(P);
-  const hipError_t e = gdn::launch_forward(P, p->dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+gdn_status gdn_fwd_noalloc(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                           const void* v, int64_t v_rs, const float* g, const float* beta, const float* S0,
+                           void* o, int64_t o_rs, float* S_T, void* stream) {
+  GDN_TRY(check_fwd_views(p, q, q_rs, k, k_rs, v, v_rs, g, beta, S0, o, o_rs, S_T));
+  if (fwd_ws(p) > GDN_NOALLOC_SCRATCH_BYTES) return GDN_EWORKSPACE;
+  if (p->N == 0) return GDN_OK;
+  void* ws = gdn::noalloc_scratch();
+  if (!ws) return GDN_EHIP;
+  return fwd_launch(p, q, q_rs, k, k_rs, v, v_rs, g, beta, S0, o, o_rs, S_T, nullptr, ws, stream);
 }
 
 gdn_status gdn_bwd(const gdn_problem* p, const void* q, int64_t q_rs, const void* k, int64_t k_rs,

@@ -106,6 +106,11 @@ inline void traced(const char* name, hipStream_t s, const F& f) {
   trace_launch(name, s, [](const void* c) { (*static_cast<const F*>(c))(); }, &f);
 }
 
+// Device address of the current device's fixed scratch array (gdn_scratch.hip), the workspace
+// of gdn_fwd_noalloc: GDN_NOALLOC_SCRATCH_BYTES, 256-byte aligned; nullptr if it cannot be
+// looked up.
+void* noalloc_scratch();
+
 // Kernel launch sequences (defined in gdn_fwd.hip / gdn_bwd.hip). Return a HIP error code.
 hipError_t launch_forward(const Prob& p, int dtype, hipStream_t s);
 hipError_t launch_backward(const Prob& p, int dtype, hipStream_t s);

@@ -130,6 +130,26 @@ gdn_status gdn_fwd(const gdn_problem* p,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward-only without allocation, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It is
+ * gdn_fwd with chunk_states NULL whose workspace is a fixed scratch array inside the library,
+ * GDN_NOALLOC_SCRATCH_BYTES long, one per GPU, which each GPU the library runs on holds until
+ * the process ends; the array of the current device (hipGetDevice) is used, so make the
+ * stream's device current. The caller passes the inputs and outputs as for gdn_fwd. A
+ * problem whose gdn_fwd_workspace_bytes exceeds the array returns GDN_EWORKSPACE (about
+ * 3,600 (chunk, value head) pairs: some 4,800 tokens at 48 value heads and chunk 64). Every
+ * call on a GPU shares that GPU's array and leaves its own contents there; nothing in it
+ * needs to start at any particular value, and calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race. The first call on a device looks
+ * the array's address up (hipGetSymbolAddress); no call allocates or frees anything.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_fwd_noalloc(const gdn_problem* p,
+                           const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                           const void* v, int64_t v_rs, const float* g, const float* beta,
+                           const float* S0, void* o, int64_t o_rs, float* S_T, void* stream);
+
+/*
  * Backward. q, k, v, g, beta, S0 and chunk_states must be those of the forward call
  * on the same problem (same sequences: the chunk table is read from chunk_states). dO [rows][Hv*Dv] (dtype), dS_T (float32 or NULL = zeros).
  * Writes dq, dk [rows][Hk*Dk] and dv [rows][Hv*Dv] (dtype, overwritten, each with

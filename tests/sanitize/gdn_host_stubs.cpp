@@ -14,6 +14,7 @@ hipError_t launch_forward(const Prob&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_backward(const Prob&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode(const DecArgs&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_conv(const ConvArgs&, int, bool, hipStream_t) { return hipSuccess; }
+void* noalloc_scratch() { return nullptr; }
 }  // namespace gdn
 
 extern "C" {

@@ -243,3 +243,22 @@ def test_rejects_varlen_inconsistency(G):
     p.N = 0
     p.cu_seqlens = 0x90000
     assert status_of(G, p) == G.GDN_EINVAL  # no sequences but rows
+
+
+def test_fwd_noalloc_rejects_on_the_host(G):
+    """gdn_fwd_noalloc checks its arguments like gdn_fwd, and a problem whose forward-only
+    workspace exceeds the library's fixed scratch is rejected before anything runs."""
+    def st(p, **over):
+        a = fwd_args(G, p, **over)
+        with pytest.raises(G.GdnError) as e:
+            G.gdn_fwd_noalloc(p, a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"], a["S_T"], stream=0)
+        return e.value.status
+
+    big = prob(G, N=4, T_total=4 * 4096, T=4096)
+    assert G.gdn_fwd_workspace_bytes(big) > G.GDN_NOALLOC_SCRATCH_BYTES
+    assert st(big) == G.GDN_EWORKSPACE
+    small = prob(G)
+    assert G.gdn_fwd_workspace_bytes(small) <= G.GDN_NOALLOC_SCRATCH_BYTES
+    assert st(small, beta=None) == G.GDN_EINVAL
+    assert st(small, q=FakeTensor(0x10002, 256, 2048, 10240)) == G.GDN_EALIGN
+    assert st(prob(G, Hv=47)) == G.GDN_EINVAL
