@@ -607,10 +607,11 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
 #pragma unroll
           for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-            for (int yc = 0; yc < NTC; ++yc) {
-              P[mi][yc] = M::run(fo[mi], fb[yc], P[mi][yc]);
-              AD[mi][yc] = M::run(fa[mi], fb[yc], AD[mi][yc]);
-            }
+            for (int yc = 0; yc < NTC; ++yc)
+              if (m0 + mi >= nC + yc) {  // tiles above the diagonal are masked to zero later
+                P[mi][yc] = M::run(fo[mi], fb[yc], P[mi][yc]);
+                AD[mi][yc] = M::run(fa[mi], fb[yc], AD[mi][yc]);
+              }
           if (dgw) {  // A V^T on the diagonal tile
             FragB fad = fa[0];
 #pragma unroll
@@ -639,14 +640,21 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         float grow[4] = {0.f, 0.f, 0.f, 0.f}, db3[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int yc = 0; yc < NTC; ++yc) {
+          // P o Gamma and dL vanish above the diagonal (tile row < tile column, wave-uniform):
+          // such tiles add nothing; only the diagonal tile needs an element mask
+          const int tm = m0 + mi, tn = nC + yc;
+          if (tm < tn) continue;
           float col = 0.f;
-          const int jj = 16 * (nC + yc) + r16;
+          const int jj = 16 * tn + r16;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 16 * (m0 + mi) + g4 + e;
+            const int i = 16 * tm + g4 + e;
             const float gd = __builtin_amdgcn_exp2f(gam[i] - gam[jj]);
-            const float pg = i >= jj ? sc * P[mi][yc][e] * gd : 0.f;
-            const float gp = i > jj ? -AD[mi][yc][e] * gd : 0.f;
+            float pg = sc * P[mi][yc][e] * gd, gp = -AD[mi][yc][e] * gd;
+            if (tm == tn) {
+              pg = g4 + e >= r16 ? pg : 0.f;
+              gp = g4 + e > r16 ? gp : 0.f;
+            }
             const float gb = bb[mi][e] * gp;
             PGs[mi][yc][e] += pg;
             Gbs[mi][yc][e] += gb;

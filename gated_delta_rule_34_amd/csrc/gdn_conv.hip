@@ -23,6 +23,8 @@ namespace gdn {
 
 constexpr int kConvThreads = 256;
 constexpr int kConvRun = 32;  // rows per thread
+constexpr int kConvPF = 1;    // rows loaded ahead of their use (kConvRun is a multiple)
+static_assert(kConvRun % kConvPF == 0, "runs hold whole prefetch groups");
 
 // Rows [lo, hi) of sequence l from the device table, clamped so that 0 <= lo <= hi <= rows:
 // a malformed table (a negative or decreasing entry) then gives wrong sequence boundaries but
@@ -155,31 +157,40 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_fwd(ConvArgs a) {
       for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
     }
   }
-  // x[t + 1] is loaded while row t is computed (one row in flight ahead of the use; two or
-  // more rows ahead measured no faster, and the same in the backward made it slower)
-  Raw8<TI> nxt = ldraw(x + t0 * a.x_rs);
-  for (int64_t t = t0; t < t1; ++t) {
-    const F8 xt = cvt<TI>(nxt);
-    if (t + 1 < t1) nxt = ldraw(x + (t + 1) * a.x_rs);
-    if (t >= hi) {  // the next sequence starts at t: its buffer is empty
-      conv_seq(a, t, lo, hi);
+  // Rows t + 1 .. t + kConvPF are in flight while row t is computed: buf[u] holds the row
+  // base + u of the current group, and its slot is refilled with the row kConvPF ahead as
+  // soon as it is converted (the loads carry no wait until their row is reached).
+  Raw8<TI> buf[kConvPF];
 #pragma unroll
-      for (int j = 0; j < K - 1; ++j)
+  for (int u = 0; u < kConvPF; ++u)
+    if (t0 + u < t1) buf[u] = ldraw(x + (t0 + u) * a.x_rs);
+  for (int64_t base = t0; base < t1; base += kConvPF) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+    for (int u = 0; u < kConvPF; ++u) {
+      const int64_t t = base + u;
+      if (t >= t1) break;
+      const F8 xt = cvt<TI>(buf[u]);
+      if (t + kConvPF < t1) buf[u] = ldraw(x + (t + kConvPF) * a.x_rs);
+      if (t >= hi) {  // the next sequence starts at t: its buffer is empty
+        conv_seq(a, t, lo, hi);
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+      }
+      F8 out;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float z = w[K - 1][i] * xt.v[i];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) z += w[j][i] * win[j].v[i];
+        out.v[i] = z * sigmoid(z);
+      }
+      st8(y + t * a.y_rs, out);
+#pragma unroll
+      for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+      if constexpr (K > 1) win[K - 2] = xt;
     }
-    F8 out;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float z = w[K - 1][i] * xt.v[i];
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) z += w[j][i] * win[j].v[i];
-      out.v[i] = z * sigmoid(z);
-    }
-    st8(y + t * a.y_rs, out);
-#pragma unroll
-    for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
-    if constexpr (K > 1) win[K - 2] = xt;
   }
 }
 
@@ -222,53 +233,71 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_bwd(ConvArgs a) {
   for (int j = 0; j < K - 1; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[j].v[i] = 0.f;
-  const int64_t uend = t1 + K - 1 < a.rows ? t1 + K - 1 : a.rows;
-  for (int64_t u = t0; u < t1 + K - 1; ++u) {
-    F8 dp;  // dpre[u], zero past the last row
-    if (u < uend) {
-      if (u >= hi) {
-        conv_seq(a, u, lo, hi);
+  const int64_t uend = t1 + K - 1 < a.rows ? t1 + K - 1 : a.rows;  // rows loaded: [t0, uend)
+  // x and dy of rows u + 1 .. u + kConvPF are in flight while row u is computed (slots as in
+  // the forward); the K - 1 rows past the run are loaded in the last group.
+  Raw8<TI> bx[kConvPF], bg[kConvPF];
+#pragma unroll
+  for (int s = 0; s < kConvPF; ++s)
+    if (t0 + s < uend) {
+      bx[s] = ldraw(x + (t0 + s) * a.x_rs);
+      bg[s] = ldraw(dy + (t0 + s) * a.dy_rs);
+    }
+  for (int64_t base = t0; base < t1 + K - 1; base += kConvPF) {
+#pragma unroll
+    for (int s = 0; s < kConvPF; ++s) {
+      const int64_t u = base + s;
+      if (u >= t1 + K - 1) break;
+      F8 dp;  // dpre[u], zero past the last row
+      if (u < uend) {
+        const F8 xu = cvt<TI>(bx[s]);
+        const F8 gu = cvt<TI>(bg[s]);
+        if (u + kConvPF < uend) {
+          bx[s] = ldraw(x + (u + kConvPF) * a.x_rs);
+          bg[s] = ldraw(dy + (u + kConvPF) * a.dy_rs);
+        }
+        if (u >= hi) {
+          conv_seq(a, u, lo, hi);
+#pragma unroll
+          for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float z = w[K - 1][i] * xu.v[i];
+#pragma unroll
+          for (int j = 0; j < K - 1; ++j) z += w[j][i] * win[j].v[i];
+          const float sg = sigmoid(z);
+          dp.v[i] = gu.v[i] * sg * (1.f + z * (1.f - sg));
+        }
+#pragma unroll
+        for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+        if constexpr (K > 1) win[K - 2] = xu;
+        // rows u - (K - 1) + j of u's sequence take w[j] dpre[u]
 #pragma unroll
         for (int j = 0; j < K - 1; ++j)
+          if (u - (K - 1) + j >= lo)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) win[j].v[i] = 0.f;
+            for (int i = 0; i < 8; ++i) acc[j].v[i] += w[j][i] * dp.v[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dp.v[i] = 0.f;
       }
-      const F8 xu = ld8(x + u * a.x_rs);
-      const F8 gu = ld8(dy + u * a.dy_rs);
+      F8 done;  // dx[u - (K - 1)]: complete once dpre[u] is in
+      if constexpr (K > 1) {
+        done = acc[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float z = w[K - 1][i] * xu.v[i];
+        for (int j = 0; j + 1 < K - 1; ++j) acc[j] = acc[j + 1];
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) z += w[j][i] * win[j].v[i];
-        const float sg = sigmoid(z);
-        dp.v[i] = gu.v[i] * sg * (1.f + z * (1.f - sg));
+        for (int i = 0; i < 8; ++i) acc[K - 2].v[i] = w[K - 1][i] * dp.v[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) done.v[i] = w[0][i] * dp.v[i];
       }
-#pragma unroll
-      for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
-      if constexpr (K > 1) win[K - 2] = xu;
-      // rows u - (K - 1) + j of u's sequence take w[j] dpre[u]
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j)
-        if (u - (K - 1) + j >= lo)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[j].v[i] += w[j][i] * dp.v[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dp.v[i] = 0.f;
+      const int64_t t = u - (K - 1);
+      if (t >= t0) st8(dx + t * a.dx_rs, done);
     }
-    F8 done;  // dx[u - (K - 1)]: complete once dpre[u] is in
-    if constexpr (K > 1) {
-      done = acc[0];
-#pragma unroll
-      for (int j = 0; j + 1 < K - 1; ++j) acc[j] = acc[j + 1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[K - 2].v[i] = w[K - 1][i] * dp.v[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) done.v[i] = w[0][i] * dp.v[i];
-    }
-    const int64_t t = u - (K - 1);
-    if (t >= t0) st8(dx + t * a.dx_rs, done);
   }
 }
 
