@@ -39,18 +39,19 @@ template <typename OT> __device__ __forceinline__ void store4(OT* dst, f32x4 x) 
 
 // T := (I + L)^-1 for strictly lower triangular L (float32 LDS, row stride LC), lower
 // blocks only: the 16 x 16 blocks above the diagonal are zero and are never written (the
-// caller stores zeros for them). Diagonal blocks by forward substitution, one column per
-// lane, then the blocks below the diagonal level by level,
+// caller stores zeros for them). Diagonal blocks by forward substitution in one wave (a
+// group of 16 lanes per block, one column per lane), then the blocks below the diagonal
+// level by level,
 // T_ij = -T_ii (sum_{k=j}^{i-1} L_ik T_kj), with float32 MFMA: the sum stays in the
 // accumulator and is the B operand of the product with T_ii (ACC order), so each level
 // costs one barrier. Ends with a barrier.
 template <int C, int LC, int NWV>
 __device__ __forceinline__ void invert_unit_lower(const float* L, float* T) {
   constexpr int NB = C / 16;
-  static_assert(NWV >= NB, "one wave per diagonal block");
+  static_assert(NWV >= NB && NB <= 4, "one wave per off-diagonal block, one lane group per diagonal block");
   const int w = threadIdx.x / 64, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
-  if (w < NB && l < 16) {
-    const int o = w * 16, j = l;
+  if (w == 0 && g < NB) {  // wave 0: lane group g substitutes in diagonal block g, lane r owns column r
+    const int o = g * 16, j = r;
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -115,15 +116,29 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
   const ChunkInfo ci = p.chunks[c];
   if (ci.seq < 0) return;
   const int n = ci.len, w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
+  // Gate records of value heads hb .. hb + GH - 1, one per wave (lane = row): gamma (log2
+  // units) is the inclusive scan of log2 g, beta is 0 past the end. The raw g and beta of a
+  // row are loaded first (gate_load) and turned into the record later (gates), so that the
+  // loads' latency hides behind other work.
+  auto gate_load = [&](int hb, float& gx, float& bx) {
+    const int hh = hb + w, i = l;
+    gx = 1.f;
+    bx = 0.f;
+    if (hh < p.r && i < n && i < C) {
+      const int h = kh * p.r + hh;
+      gx = p.g[(int64_t)(ci.t0 + i) * p.Hv + h];
+      bx = p.beta[(int64_t)(ci.t0 + i) * p.Hv + h];
+    }
+  };
+  float gx0, bx0;
+  gate_load(0, gx0, bx0);  // issued before K and Q: they arrive while K and Q do
   {
     TileDma<C, D, NW, OT> dm;
     dm.init(w);
     dm.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
     dm.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
   }
-  // Gate records of value heads hb .. hb + GH - 1, one per wave (lane = row): gamma (log2
-  // units) is the inclusive scan of log2 g, beta is 0 past the end.
-  auto gates = [&](int hb) {
+  auto gates = [&](int hb, float gx, float bx) {
     const int hh = hb + w;
     if (hh < p.r) {
       const int h = kh * p.r + hh;
@@ -132,7 +147,6 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
       const bool ok = i < n && i < C;
       float lg = 0.f, be = 0.f, dla = 0.f;  // log2 g, beta, d log g / d alpha of the row
       if (ok) {
-        const float gx = p.g[(int64_t)(ci.t0 + i) * p.Hv + h], bx = p.beta[(int64_t)(ci.t0 + i) * p.Hv + h];
         if (p.a_log) {  // the gate chain from alpha and beta_raw
           lg = chain_log2g(gx, p.a_log[h], p.dt_bias[h]);
           be = chain_beta(bx);
@@ -156,7 +170,6 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
       }
     }
   };
-  gates(0);  // while K and Q arrive
   dma_wait();
   lds_barrier();
   if (p.sv_qn) {  // L2-normalise the q and k head rows in LDS and keep them, and the factors,
@@ -200,26 +213,42 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
     wave_mm<OT, D, 1, RT>(KK, [&](int, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * w, s); }, fb);
     wave_mm<OT, D, 1, RT>(QK, [&](int, int s) { return ld_n<OT, KSD, STD, LD>(sQ, 16 * w, s); }, fb);
   }
-  lds_barrier();  // K and Q consumed
+  gates(0, gx0, bx0);  // the first GH records (their raw values were loaded at the start)
+  lds_barrier();  // K and Q consumed; the records are in LDS
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = kh * p.r + hh;
     const size_t ch = ch_idx(p, c, h);
     if (hh > 0 && hh % GH == 0) {  // the next group of gate records (the last head's barrier freed sg)
-      gates(hh);
+      float gx, bx;
+      gate_load(hh, gx, bx);
+      gates(hh, gx, bx);
       lds_barrier();
     }
     const float* sgh = sg[hh % GH];
     const float* sbh = sbeta[hh % GH];
-    if (rw) {
+    if (rw) {  // wave w: row tile w of L and M. Above the diagonal M is zero and L is never
+               // read; below it no element mask is needed.
 #pragma unroll
-      for (int j = 0; j < RT; ++j)
+      for (int j = 0; j < RT; ++j) {
+        if (j > w) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sM[(16 * w + g4 + e) * C + 16 * j + r16] = (OT)0.f;
+          continue;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * w + g4 + e, jj = 16 * j + r16;
           const float gd = __builtin_amdgcn_exp2f(sgh[i] - sgh[jj]);
-          sL[i * LCF + jj] = i > jj ? sbh[i] * gd * KK[0][j][e] : 0.f;
-          sM[i * C + jj] = (OT)(i >= jj && i < n ? gd * QK[0][j][e] : 0.f);
+          float lv = sbh[i] * gd * KK[0][j][e], mv = gd * QK[0][j][e];
+          if (j == w) {
+            lv = g4 + e > r16 ? lv : 0.f;
+            mv = g4 + e >= r16 ? mv : 0.f;
+          }
+          if (n < C) mv = i < n ? mv : 0.f;
+          sL[i * LCF + jj] = lv;
+          sM[i * C + jj] = (OT)mv;
         }
+      }
     }
     lds_barrier();
     {
