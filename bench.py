@@ -206,6 +206,26 @@ def summarize_counters(out_path, dirs, command):
     print("\n".join(lines))
 
 
+def summarize_stats(out_path, stats_csv, command, title):
+    """Write a kernel-statistics summary from a rocprofv3 ``--stats`` kernel_stats.csv: per gdn
+    kernel the calls and the average, minimum and maximum duration."""
+    rows = []
+    for r in csv.DictReader(open(stats_csv)):
+        k = _kernel_key(r["Name"])
+        if k:
+            rows.append((k, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lines = [f"# Kernel statistics: {title}", "", "Command (one MI355X; REPO is the repository root):", "", "```",
+             command, "```", "", f"Source: rocprofv3 `--stats` kernel statistics (`{os.path.basename(stats_csv)}`). "
+             "Warmup and timed calls are both counted; the minima are the steady-state figures.", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for k, n, avg, mn, mx, pct in rows:
+        lines.append(f"| {k} | {n} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f} % |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def committed_counter(path, kernel, key):
     blob = _blob(path)
     if not blob or blob.get("source_hash") != source_hash():
@@ -420,14 +440,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-step", action="store_true",
                     help="run only warmup + timed plain training steps (for rocprofv3)")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="with --profile-step: time forward-only calls instead of training steps")
     ap.add_argument("--pmc-calib", action="store_true",
                     help="first copy a buffer of known size (the counter calibration dispatch)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="PATH",
                     help="OUT_MD DIR...: write a counter summary from rocprofv3 counter result directories")
-    ap.add_argument("--command", default="", help="command line recorded in a counter summary")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("OUT_MD", "STATS_CSV", "TITLE"),
+                    help="write a kernel-statistics summary from a rocprofv3 kernel_stats.csv")
+    ap.add_argument("--command", default="", help="command line recorded in a counter or statistics summary")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.command)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats[:2], args.command, args.summarize_stats[2])
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -455,15 +482,16 @@ def main():
     wl = workload(G, torch, case)
     print(f"[bench] workload ready: T_total={T} Hk={Hk} Hv={Hv} D={D} C={C}", file=sys.stderr, flush=True)
 
+    step_fn = wl["fwd_only"] if (args.profile_step and args.fwd_only) else wl["step"]
     G.gdn_trace_enable(True)
     G.gdn_trace_collect()  # (warmup launches are collected and dropped below)
     for i in range(args.warmup):
         timer.flush(i)
-        wl["step"]()
+        step_fn()
     torch.cuda.synchronize()
     G.gdn_trace_collect()
     print("[bench] warmup done", file=sys.stderr, flush=True)
-    eager_t = timer.run(wl["step"], args.steps, 0)
+    eager_t = timer.run(step_fn, args.steps, 0)
     G.gdn_trace_enable(False)
     trace = G.gdn_trace_collect()
     print(f"[bench] eager: {eager_t['median_ms']:.4f} ms/step (median of {args.steps})", file=sys.stderr, flush=True)
