@@ -55,7 +55,7 @@ gdn_status check_problem(const gdn_problem* p) {
 
 // Region sizes in bytes (each rounded up to 256 B).
 struct Regions {
-  size_t chunks, seq_chunk;        // chunk table, first chunk per sequence
+  size_t chunks, seq_chunk;        // chunk table; first chunk per sequence and the sweep order
   size_t oDD, oCD, oCC, gb;        // per (chunk, value head): [D][D], [D][C], [C][C] elements, [kGateRows][C] f32
   size_t qn, rr;                   // normalised q or k rows, their factors (0 without qk_l2norm)
 };
@@ -65,7 +65,7 @@ Regions regions(const gdn_problem* p) {
   const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
   Regions r;
   r.chunks = align_up(nc * sizeof(gdn::ChunkInfo));
-  r.seq_chunk = align_up(((size_t)p->N + 1) * sizeof(int));
+  r.seq_chunk = align_up((2 * (size_t)p->N + 1) * sizeof(int));  // first chunks, then the sweep order
   r.oDD = align_up(nc * Hv * D * D * es);
   r.oCD = align_up(nc * Hv * C * D * es);
   r.oCC = align_up(nc * Hv * C * C * es);
@@ -104,6 +104,7 @@ void carve_saved(gdn::Prob& P, const Regions& r, void* saved, bool with_states =
   P.chunks = reinterpret_cast<gdn::ChunkInfo*>(b);
   b += r.chunks;
   P.seq_chunk = reinterpret_cast<int*>(b);
+  P.seq_order = P.seq_chunk + P.N + 1;
   b += r.seq_chunk;
   if (with_states) {
     P.sv_S = b;

@@ -103,7 +103,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
 
   int grp, hh;
   if (!xcd_group(blockIdx.x, p.N * p.Hk, p.r, grp, hh)) return;
-  const int n = grp / p.Hk, kh = grp % p.Hk, h = kh * p.r + hh;
+  const int n = p.seq_order[grp / p.Hk], kh = grp % p.Hk, h = kh * p.r + hh;  // longest sequences first
   const size_t nh = (size_t)n * p.Hv + h;
   const int c0 = p.seq_chunk[n], c1 = p.seq_chunk[n + 1];
   int64_t sa, sb;  // rows of the sequence; chunk c starts at sa + (c - c0) C (as in the chunk table)

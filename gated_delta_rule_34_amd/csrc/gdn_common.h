@@ -77,9 +77,17 @@ __device__ __forceinline__ bool xcd_group(int b, int G, int r, int& grp, int& me
 }
 __host__ __device__ constexpr int xcd_grid(int G, int r) { return (G + 7) / 8 * 8 * r; }
 
-// One workgroup: chunk table and per-sequence first-chunk offsets.
+// Sequences ranked for the sweeps' order up to this count; beyond it the order is the identity.
+constexpr int kOrderMax = 1024;
+
+// One workgroup: chunk table, per-sequence first-chunk offsets and the sweep order. The
+// sweeps give one workgroup to each (sequence, value head) and walk its chunks serially;
+// when there are more of them than CUs, the longest sequences must start first (the dispatcher
+// takes workgroups in index order), so seq_order lists the sequences by decreasing chunk count
+// (ties by index: a permutation).
 template <int C>
 __global__ __launch_bounds__(NTHREADS) void k_table(Prob p) {
+  __shared__ int cnt[kOrderMax];
   if (threadIdx.x == 0) {
     int64_t off = 0;
     for (int n = 0; n < p.N; ++n) {
@@ -102,6 +110,18 @@ __global__ __launch_bounds__(NTHREADS) void k_table(Prob p) {
     }
   }
   for (int c = p.seq_chunk[p.N] + threadIdx.x; c < p.nc_max; c += NTHREADS) p.chunks[c] = ChunkInfo{-1, 0, 0, 0};
+  if (p.N > kOrderMax) {
+    for (int n = threadIdx.x; n < p.N; n += NTHREADS) p.seq_order[n] = n;
+    return;
+  }
+  for (int n = threadIdx.x; n < p.N; n += NTHREADS) cnt[n] = p.seq_chunk[n + 1] - p.seq_chunk[n];
+  __syncthreads();
+  for (int n = threadIdx.x; n < p.N; n += NTHREADS) {
+    const int cn = cnt[n];
+    int rank = 0;
+    for (int m = 0; m < p.N; ++m) rank += (cnt[m] > cn) || (cnt[m] == cn && m < n);
+    p.seq_order[rank] = n;
+  }
 }
 
 }  // namespace gdn

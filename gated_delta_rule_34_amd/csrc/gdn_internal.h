@@ -45,6 +45,7 @@ struct Prob {
   // chunk table
   ChunkInfo* chunks;  // [nc_max]
   int* seq_chunk;     // [N + 1] first chunk of each sequence
+  int* seq_order;     // [N] sequences by decreasing chunk count: the sweeps' workgroup order
 
   // Saved activations written by the forward for the backward, per chunk c and value
   // head h (element type = the problem's storage type OT unless noted):
