@@ -515,6 +515,77 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   zero(PGs);
   zero(Gbs);
 
+  // Per-row gate gradients of head fh (dg, dbeta from the head's partial row sums, with the
+  // reverse scan of d log g), done by one wave. Head fh's partials stay in their slots (parity
+  // fh & 1) until head fh + 2 zeroes them, so with two or more value blocks per head the wave
+  // does this inside the first block step of head fh + 1, after its own products, while the
+  // other waves work on that step (the next block step's barrier then orders its reads before
+  // that zeroing), and the last head's in the end phase. With one block per head it follows
+  // the head's elementwise phase behind a barrier.
+  auto finish = [&](int fh) {
+    const int hh = fh, h = h0 + hh, par = hh & 1;
+    const float* gam = sgb[hh % 3];
+    const float* bet = gam + C;
+    const float gn = gam[C - 1];
+    const float* redh = red[par];
+    const float* redch = redc[par];
+    const bool ok = lane < C;
+    const int i = ok ? lane : C - 1;  // lanes past C read a valid row and contribute nothing
+    // every partial sum first (independent reads), then the sums in a fixed order
+    float part[R_NSLOT][NCB], pc[RT];
+#pragma unroll
+    for (int sl = 0; sl < R_NSLOT; ++sl)
+#pragma unroll
+      for (int q = 0; q < NCB; ++q) part[sl][q] = redh[sl * RS + q * C + i];
+#pragma unroll
+    for (int m = 0; m < RT; ++m) pc[m] = redch[m * C + i];
+    const float gi = gam[i], gprev = i > 0 ? gam[i - 1] : 0.f, bei = bet[i];
+    float rv[R_NSLOT], gcol = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < R_NSLOT; ++sl) {
+      float a = 0.f;
+#pragma unroll
+      for (int q = 0; q < NCB; ++q) a += part[sl][q];
+      rv[sl] = ok ? a : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < RT; ++m) gcol += pc[m];
+    if (!ok) gcol = 0.f;
+    const float bi = ok ? __builtin_amdgcn_exp2f(gi) : 0.f, be = ok ? bei : 0.f;
+    float dgam = 0.f;
+    if (ok) dgam = bi * rv[R_RQ] + be * bi * rv[R_RHO] - rv[R_EBAR] + rv[R_GROW] + be * rv[R_DB3] - gcol;
+    const float ebsum = wave_sum(rv[R_EBAR]);
+    if (lane == n - 1) {
+      float st = 0.f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) st += swv[par][k];
+      dgam += __builtin_amdgcn_exp2f(gn) * st + ebsum;
+    }
+    const float dlg = wave_rscan_incl(dgam);
+    if (lane < n) {  // (lane < n implies lane < C: i is the lane)
+      float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
+      // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
+      float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
+      if (p.a_log) {  // gate chain: d alpha = dlog g * dlog g / d alpha (from the record), d beta_raw = dbeta beta (1 - beta)
+        dgv = dlg * sdl[hh % 3][i];
+        db *= be * (1.f - be);
+      }
+      if (p.r <= GRM) {
+        // the row offset is formed here rather than kept live across the item's loops
+        int li = i;
+        asm volatile("" : "+v"(li));
+        sgo[0][hh][li] = db;
+        sgo[1][hh][li] = dgv;
+      } else {
+        int li = i;  // the row offset is formed here, not kept live across the item
+        asm volatile("" : "+v"(li));
+        const int64_t row = (int64_t)(ci.t0 + li) * p.Hv + h;
+        p.dbeta[row] = db;
+        p.dg[row] = dgv;
+      }
+    }
+  };
+
   for (int hh = 0; hh < p.r; ++hh) {
     const int h = h0 + hh, par = hh & 1;
     const float* gam = sgb[hh % 3];  // log2 units
@@ -621,6 +692,8 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           }
         }
       }
+      if constexpr (NBH >= 2)  // the previous head's rows, off the barrier path (see finish)
+        if (b == 0 && hh > 0 && w == FIN) finish(hh - 1);
     }
 
     // ---- phase 2 of the head: elementwise on the wave's tiles
@@ -717,63 +790,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     }
     sdot = wave_sum(sdot);
     if (lane == 0) swv[par][w] = sdot;
-    lds_barrier();  // the head's partial sums are complete
-    if (w == FIN) {  // per-row gate gradients of head h (the other waves move on)
-      const bool ok = lane < C;
-      const int i = ok ? lane : C - 1;  // lanes past C read a valid row and contribute nothing
-      // every partial sum first (independent reads), then the sums in a fixed order
-      float part[R_NSLOT][NCB], pc[RT];
-#pragma unroll
-      for (int sl = 0; sl < R_NSLOT; ++sl)
-#pragma unroll
-        for (int q = 0; q < NCB; ++q) part[sl][q] = redh[sl * RS + q * C + i];
-#pragma unroll
-      for (int m = 0; m < RT; ++m) pc[m] = redch[m * C + i];
-      const float gi = gam[i], gprev = i > 0 ? gam[i - 1] : 0.f, bei = bet[i];
-      float rv[R_NSLOT], gcol = 0.f;
-#pragma unroll
-      for (int sl = 0; sl < R_NSLOT; ++sl) {
-        float a = 0.f;
-#pragma unroll
-        for (int q = 0; q < NCB; ++q) a += part[sl][q];
-        rv[sl] = ok ? a : 0.f;
-      }
-#pragma unroll
-      for (int m = 0; m < RT; ++m) gcol += pc[m];
-      if (!ok) gcol = 0.f;
-      const float bi = ok ? __builtin_amdgcn_exp2f(gi) : 0.f, be = ok ? bei : 0.f;
-      float dgam = 0.f;
-      if (ok) dgam = bi * rv[R_RQ] + be * bi * rv[R_RHO] - rv[R_EBAR] + rv[R_GROW] + be * rv[R_DB3] - gcol;
-      const float ebsum = wave_sum(rv[R_EBAR]);
-      if (lane == n - 1) {
-        float st = 0.f;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) st += swv[par][k];
-        dgam += __builtin_amdgcn_exp2f(gn) * st + ebsum;
-      }
-      const float dlg = wave_rscan_incl(dgam);
-      if (lane < n) {  // (lane < n implies lane < C: i is the lane)
-        float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
-        // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
-        float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
-        if (p.a_log) {  // gate chain: d alpha = dlog g * dlog g / d alpha (from the record), d beta_raw = dbeta beta (1 - beta)
-          dgv = dlg * sdl[hh % 3][i];
-          db *= be * (1.f - be);
-        }
-        if (p.r <= GRM) {
-          // the row offset is formed here rather than kept live across the item's loops
-          int li = i;
-          asm volatile("" : "+v"(li));
-          sgo[0][hh][li] = db;
-          sgo[1][hh][li] = dgv;
-        } else {
-          int li = i;  // the row offset is formed here, not kept live across the item
-          asm volatile("" : "+v"(li));
-          const int64_t row = (int64_t)(ci.t0 + li) * p.Hv + h;
-          p.dbeta[row] = db;
-          p.dg[row] = dgv;
-        }
-      }
+    if constexpr (NBH < 2) {  // one block per head: no later block barrier would separate the
+                              // finishing wave's reads from the zeroing of these slots two heads on
+      lds_barrier();
+      if (w == FIN) finish(hh);
     }
   }
 
@@ -792,7 +812,9 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           sGbs[LC::at(i, jj)] = (OT)Gbs[mi][yc][e];
         }
   }
-  lds_barrier();
+  lds_barrier();  // (also: every head's partial sums are complete)
+  if constexpr (NBH >= 2)
+    if (w == FIN) finish(p.r - 1);
   if (aD) {
     auto fK = [&](int y, int s) { return ld_t<OT, KSC, STD, LD>(sK, 16 * (nD + y), s); };  // K^T rows d
     // dq^T += K^T (sum PG)^T
