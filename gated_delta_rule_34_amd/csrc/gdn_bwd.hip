@@ -281,8 +281,8 @@ template <int RT, int DT, int NW> struct Part {
   static constexpr int WCB = NW / WRB;
   static constexpr int NT = DT >= WCB ? DT / WCB : 1;
   static constexpr int NTC = RT >= WCB ? RT / WCB : 1;
-  __device__ __forceinline__ static int rb(int w) { return w % WRB; }
-  __device__ __forceinline__ static int cb(int w) { return w / WRB; }
+  __host__ __device__ static constexpr int rb(int w) { return w % WRB; }
+  __host__ __device__ static constexpr int cb(int w) { return w / WRB; }
   __device__ __forceinline__ static bool activeD(int w) { return cb(w) * NT < DT; }
   __device__ __forceinline__ static bool activeC(int w) { return cb(w) * NTC < RT; }
 };
@@ -501,7 +501,16 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     for (int yc = 0; yc < NTC; ++yc)
       if (m0 + mi == nC + yc) dmi = mi;
   const bool dgw = aC && dmi >= 0;
-  constexpr int FIN = NW - 1;  // the wave that finishes each head's per-row gate gradients
+  // The wave that finishes each head's per-row gate gradients: the highest-numbered wave
+  // whose C x C tiles all lie above the diagonal (it skips their products and elementwise
+  // work), else the last wave.
+  constexpr int FIN = [] {
+    for (int v = NW - 1; v >= 0; --v) {
+      const int r0 = PT::rb(v) * MT, c0 = PT::cb(v) * NTC;
+      if (r0 + MT - 1 < c0) return v;
+    }
+    return NW - 1;
+  }();
 
   // dq^T, dk^T of the key head on the wave's D x C tiles [y][mi], summed over its value
   // heads in order: lane (g, r) element e holds row i = 16 (m0 + mi) + r, column
