@@ -112,7 +112,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
   const int v0 = w * WC;
 
   TileDma<C, D, NW, OT, true> dmD;   // K, Q, dO
-  TileDma<C, C, NW, OT, true> dmC;   // T, M
+  TileDmaLow<C, NW, OT, true> dmC;  // T, M (lower-block form)
   TileDma<1, kSweepGateRows * C, NW, float> dmG;  // gate record rows 0-3
   dmD.init(w);
   dmC.init(w);
@@ -125,10 +125,15 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
     dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
     dmD.issue(b + CF::O_O, (const OT*)p.dO + t0 * p.dO_rs + h * D, p.dO_rs, len, w);
-    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
-    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
+    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
+    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
     dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
   };
+#pragma unroll
+  for (int bf = 0; bf < 2; ++bf) {  // the blocks above the diagonal of T and M stay zero
+    dmC.zero_upper(sbuf[bf] + CF::O_T, w);
+    dmC.zero_upper(sbuf[bf] + CF::O_M, w);
+  }
 
   // The adjoint: dS[ct][dt] holds dS[16 dt + g4 + e][v0 + 16 ct + r16].
   f32x4 dS[CT][DT];
@@ -374,7 +379,7 @@ __device__ __forceinline__ float group4_sum(float x) {
 // with Q K^T and K K^T formed once per key head. The products with K and Q are linear in
 // PG and Gb and dq, dk sum over the value heads, so they run once per key head on the
 // head sums: dq^T += K^T (sum PG)^T,  dk^T += Q^T (sum PG) + K^T ((sum Gb) + (sum Gb)^T).
-template <typename TI, int C, int D>
+template <typename TI, int C, int D, bool CHAIN>
 __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   using OT = TI;
   using CF = GradCfg<TI, C, D>;
@@ -420,63 +425,80 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   const int h0 = kh * p.r;
   constexpr int NH = NW / 2;  // the two halves of the waves load different tensors
   constexpr int PB = CF::PB, PW = CF::PW;
+  const int wh = w % NH;
+  const bool lo = w < NH;  // first half: A and dO; second half: Delta and V
   TileDma<BV, D, NW, OT, true> dmS;   // S0^T, dS^T row blocks (every wave)
-  TileDma<C, BV, NH, OT, true> dmA;   // A block (first half)
-  TileDma<C, BV, NH, OT, true> dmL;   // Delta block (second half)
+  TileDma<C, BV, NH, OT, true> dmAL;  // A block (first half) or Delta block (second half)
   TileDma<C, PW, NH, OT, true> dmP;   // dO (first half) or V (second half) for a pair of blocks
   TileDma<C, D, NW, OT, true> dmD;    // K, Q
   TileDma<1, 2 * C, NW, float> dmG;  // gate record
   TileDma<1, C, NW, float> dmGc;     // its d log g / d alpha row (gate chain only)
-  const int wh = w % NH;
   dmS.init(w);
-  dmA.init(wh);
-  dmL.init(wh);
+  dmAL.init(wh);
   dmP.init(wh);
   dmD.init(w);
   dmG.init(w);
   dmGc.init(w);
+  // The item's sources. The saved blocks of the key head's r value heads are consecutive
+  // (chunk, head, block order), so job j = (head h0 + j / NBH, block j % NBH) finds its S^T
+  // and dS^T blocks j BV D elements, and its A and Delta blocks j C BV elements, past the
+  // first head's first block; pair q finds its dO and V columns q PW columns past the first
+  // head's. One resource per tensor serves every job (byte offsets go in the instructions'
+  // scalar offset); only the A and Delta blocks, whose rows past the chunk's end must read
+  // as zero, take a resource of their own per job.
+  const size_t ch0 = ch_idx(p, c, h0);
+  constexpr uint32_t SBB = BV * D * sizeof(OT), ABB = C * BV * sizeof(OT);
+  const uint32_t head_saved = (uint32_t)(p.r * D * D * sizeof(OT));
+  const i32x4 rS = buf_rsrc((const OT*)p.sv_S + ch0 * D * D, head_saved);
+  const i32x4 rDS = buf_rsrc((const OT*)p.ws_dS + ch0 * D * D, head_saved);
+  const uint64_t aAL =
+      reinterpret_cast<uint64_t>((lo ? (const OT*)p.ws_A : (const OT*)p.sv_D) + ch0 * C * D);
+  const int64_t prs = lo ? p.dO_rs : p.v_rs;
+  const uint32_t prsb = (uint32_t)(prs * (int64_t)sizeof(OT));
+  const i32x4 rP = buf_rsrc((lo ? (const OT*)p.dO : (const OT*)p.v) + (int64_t)ci.t0 * prs + h0 * D, (uint32_t)n * prsb);
+  const i32x4 rG = buf_rsrc(p.sv_gb + ch0 * kGateRows * C, (uint32_t)(p.r * kGateRows * C * 4));
   const int njobs = p.r * NBH, npairs = njobs / PB;
-  // Job j = (head h0 + j / NBH, block j % NBH) goes into sB[j % NBUF]; the first block of a
-  // head also brings the head's gate record. Job j's loads are issued in the step of job
-  // j - 2, in parts spread over the step (a long run of loads would stall the issuing wave).
-  // Pair q (the dO and V columns of jobs q PB .. q PB + PB - 1) goes into sP[q % NPBUF] and
-  // is issued after that step's job loads in the step of job (q - 1) PB (PB = 2) or q - 2
-  // (PB = 1). Before the first step: job 0, pair 0, job 1 (and pair 1 when PB = 1).
+  // Job j goes into sB(j % NBUF); the first block of a head also brings the head's gate
+  // record. Job j's loads are issued in the step of job j - 2, in parts spread over the step
+  // (a long run of loads would stall the issuing wave). Pair q (the dO and V columns of jobs
+  // q PB .. q PB + PB - 1) goes into sP(q % NPBUF) and is issued after that step's job loads
+  // in the step of job (q - 1) PB (PB = 2) or q - 2 (PB = 1). Before the first step: job 0,
+  // pair 0, job 1 (and pair 1 when PB = 1).
   auto issue_part = [&](int j, int part) {
-    const int h = h0 + j / NBH, blk = j % NBH, v0 = blk * BV;
-    const size_t ch = ch_idx(p, c, h);
+    const int hh = j / NBH, blk = j % NBH;
     OT* b = sB(j % CF::NBUF);
     if (part == 0) {
-      dmS.issue(b + CF::O_S0, (const OT*)p.sv_S + ch * D * D + (size_t)v0 * D, D, BV, w);
-      if (blk == 0) dmG.issue(sgb[(j / NBH) % 3], p.sv_gb + ch * kGateRows * C, 2 * C, 1, w);  // gamma, beta
-      if (blk == 0 && p.a_log) dmGc.issue(sdl[(j / NBH) % 3], p.sv_gb + ch * kGateRows * C + 4 * C, C, 1, w);
+      dmS.issue_rs(b + CF::O_S0, rS, D * sizeof(OT), (uint32_t)j * SBB, w);
+      if (blk == 0) {
+        const uint32_t go = (uint32_t)(hh * kGateRows * C * 4);
+        dmG.issue_rs(sgb[hh % 3], rG, 0, go, w);  // gamma, beta
+        if constexpr (CHAIN) dmGc.issue_rs(sdl[hh % 3], rG, 0, go + 4 * C * 4, w);
+      }
     } else if (part == 1) {
-      dmS.issue(b + CF::O_DS, (const OT*)p.ws_dS + ch * D * D + (size_t)v0 * D, D, BV, w);
+      dmS.issue_rs(b + CF::O_DS, rDS, D * sizeof(OT), (uint32_t)j * SBB, w);
     } else {
-      if (w < NH)
-        dmA.issue(b + CF::O_A, (const OT*)p.ws_A + ch * C * D + (size_t)blk * C * BV, BV, n, wh);
-      else
-        dmL.issue(b + CF::O_DL, (const OT*)p.sv_D + ch * C * D + (size_t)blk * C * BV, BV, n, wh);
+      const uint64_t a = aAL + (uint64_t)j * ABB;
+      const i32x4 r = {__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a),
+                       __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32)),
+                       (int32_t)((uint32_t)n * BV * sizeof(OT)), 0x00020000};
+      dmAL.issue_rs(b + (lo ? CF::O_A : CF::O_DL), r, BV * sizeof(OT), 0, wh);
     }
   };
   auto issue_job = [&](int j) {
     for (int part = 0; part < 3; ++part) issue_part(j, part);
   };
   auto issue_pair = [&](int q) {
-    const int h = h0 + (q * PB) / NBH, v0 = ((q * PB) % NBH) * BV;
     OT* b = sP(q % CF::NPBUF);
-    if (w < NH)
-      dmP.issue(b + CF::O_DO, (const OT*)p.dO + (int64_t)ci.t0 * p.dO_rs + h * D + v0, p.dO_rs, n, wh);
-    else
-      dmP.issue(b + CF::O_V, (const OT*)p.v + (int64_t)ci.t0 * p.v_rs + h * D + v0, p.v_rs, n, wh);
+    dmP.issue_rs(b + (lo ? CF::O_DO : CF::O_V), rP, prsb, (uint32_t)(q * PW * sizeof(OT)), wh);
   };
   // This wave's load instructions of job j, of a pair, and of the step of job j.
   auto job_loads = [&](int j) {
-    return j < njobs ? 2 * dmS.count(w) + (w < NH ? dmA.count(wh) : dmL.count(wh)) +
-                           (j % NBH == 0 ? dmG.count(w) + (p.a_log ? dmGc.count(w) : 0) : 0)
+    return j < njobs ? 2 * dmS.count(w) + dmAL.count(wh) +
+                           (j % NBH == 0 ? dmG.count(w) + (CHAIN ? dmGc.count(w) : 0) : 0)
                      : 0;
   };
   const int pair_loads = dmP.count(wh);
+  constexpr bool UNI = decltype(dmS)::CNT >= 0 && decltype(dmAL)::CNT >= 0 && decltype(dmP)::CNT >= 0;
   auto step_loads = [&](int j) {  // issued in the step of job j: job j + 2 and, maybe, a pair
     const int q = PB == 1 ? j + 2 : j / PB + 1;
     return job_loads(j + 2) + ((j % PB == 0 && q < npairs) ? pair_loads : 0);
@@ -575,7 +597,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
       float db = rv[R_DB1] + bi * rv[R_RHO] + rv[R_DB3];
       // dg = dlog g / g, with 1 / g_i = 2^(gamma_{i-1} - gamma_i) from the record
       float dgv = dlg * __builtin_amdgcn_exp2f(gprev - gi);
-      if (p.a_log) {  // gate chain: d alpha = dlog g * dlog g / d alpha (from the record), d beta_raw = dbeta beta (1 - beta)
+      if constexpr (CHAIN) {  // gate chain: d alpha = dlog g * dlog g / d alpha (from the record), d beta_raw = dbeta beta (1 - beta)
         dgv = dlg * sdl[hh % 3][i];
         db *= be * (1.f - be);
       }
@@ -612,21 +634,34 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     zero(Yt);
     zero(P);
     zero(AD);
-    for (int b = 0; b < NBH; ++b) {
+    auto block_step = [&](auto bc) {
+      constexpr int b = decltype(bc)::value;
       const int j = hh * NBH + b;
       const OT* cur = sB(j % CF::NBUF);
       const OT* curp = sP((j / PB) % CF::NPBUF);
-      const int sp = (j % PB) * (BV / KSB);  // this block's first contraction step within the pair
+      constexpr int sp = (b % PB) * (BV / KSB);  // this block's first contraction step within the pair
       // Job j and its pair are done once at most the loads issued after them are outstanding:
-      // job 1 before the first step, else the previous step's loads.
-      dma_wait_keep(j == 0 ? job_loads(1) + (PB == 1 && 1 < npairs ? pair_loads : 0) : step_loads(j - 1));
+      // job 1 before the first step, else the previous step's loads (job j + 1, and the pair
+      // issued with it). Where every wave issues the same loads per tile, that count is a
+      // constant of the block (the gate record's load, issued by wave 0 alone, is not
+      // counted: wave 0 then waits for one load more than it needs to).
+      if constexpr (UNI) {
+        constexpr int K = 2 * decltype(dmS)::CNT + decltype(dmAL)::CNT +
+                          ((((b == 0 ? NBH : b) - 1) % PB == 0) ? decltype(dmP)::CNT : 0);
+        if (b + 1 < NBH || hh + 1 < p.r)
+          dma_wait_keep(K);
+        else
+          dma_wait_keep(0);
+      } else {
+        dma_wait_keep(j == 0 ? job_loads(1) + (PB == 1 && 1 < npairs ? pair_loads : 0) : step_loads(j - 1));
+      }
       lds_barrier();  // job j (and K, Q, gates with it) is in LDS; every wave is done with job j - 1
       const bool nxt2 = j + 2 < njobs;  // every wave issues every part (the wait counts rely on it)
       if (nxt2) {
         issue_part(j + 2, 0);
         issue_part(j + 2, 1);
       }
-      if (j == 0 && aC) {  // Q K^T and K K^T of the key head on this wave's C x C tiles
+      if (b == 0 && hh == 0 && aC) {  // Q K^T and K K^T of the key head on this wave's C x C tiles
         f32x4 G2[2 * MT][NTC];
         zero(G2);
         wave_mm<OT, D, 2 * MT, NTC>(
@@ -678,7 +713,8 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         if (s == 0) {
           if (nxt2) issue_part(j + 2, 2);
           const int q = PB == 1 ? j + 2 : j / PB + 1;
-          if (j % PB == 0 && q < npairs) issue_pair(q);
+          if constexpr (b % PB == 0)
+            if (q < npairs) issue_pair(q);
         }
         if (aC) {
           FragB fb[NTC];  // Delta rows of the wave's C tiles (B operands over v)
@@ -701,9 +737,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           }
         }
       }
-      if constexpr (NBH >= 2)  // the previous head's rows, off the barrier path (see finish)
-        if (b == 0 && hh > 0 && w == FIN) finish(hh - 1);
-    }
+      if constexpr (NBH >= 2 && b == 0)  // the previous head's rows, off the barrier path (see finish)
+        if (hh > 0 && w == FIN) finish(hh - 1);
+    };
+    static_for<NBH>(block_step);
 
     // ---- phase 2 of the head: elementwise on the wave's tiles
     const float sc = p.scale, gn = gam[C - 1];
@@ -906,7 +943,12 @@ static hipError_t bwd_seq(const Prob& p, hipStream_t s) {
     traced("k_bwd_sweep", s,
            [&] { k_bwd_sweep<TI, C, D><<<xcd_grid(p.N * p.Hk, p.r), CF::NW * 64, 0, s>>>(p); });
   if (p.nc_max > 0)
-    traced("k_bwd_grad", s, [&] { k_bwd_grad<TI, C, D><<<p.nc_max * p.Hk, kThreadsG, 0, s>>>(p); });
+    traced("k_bwd_grad", s, [&] {
+      if (p.a_log)
+        k_bwd_grad<TI, C, D, true><<<p.nc_max * p.Hk, kThreadsG, 0, s>>>(p);
+      else
+        k_bwd_grad<TI, C, D, false><<<p.nc_max * p.Hk, kThreadsG, 0, s>>>(p);
+    });
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@
 //         (a, f < 4) points at row f, columns 4a..4a+3 of a 4 x 16 block, and lane d
 //         receives column d of the block (rows 0..3). float32 reads one element per lane.
 #pragma once
+#include <utility>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -310,6 +311,13 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
                "s"(lds)
                : "memory", "m0");
 }
+// As dma16, with the wave-uniform byte offset soff added to every lane's offset (the
+// instruction's scalar offset).
+__device__ __forceinline__ void dma16s(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(soff), "s"(lds)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Direct loads of a global tile [R][Cn] into LDS in the layout Swz<T, Cn, TR, PT>, issued by NW
@@ -323,6 +331,8 @@ template <int R, int Cn, int NW, typename T, bool TR = false, bool PT = false> s
   using L = Swz<T, Cn, TR, PT>;
   static_assert(!PT || R % 16 == 0, "padded tiles hold whole 16-row groups");
   static constexpr int TOT = R * L::NCH, U = (TOT + NW * 64 - 1) / (NW * 64);
+  // Instructions per wave when every wave issues the same number, else -1.
+  static constexpr int CNT = TOT % (NW * 64) == 0 ? U : -1;
   uint32_t row[U], cof[U];
   __device__ __forceinline__ void init(int w) {
     const int l = lane_id();
@@ -341,6 +351,19 @@ template <int R, int Cn, int NW, typename T, bool TR = false, bool PT = false> s
     for (int u = 0; u < U; ++u) n += (u * NW + w) * 64 < TOT ? 1 : 0;
     return n;
   }
+  // As issue(), from a resource built by the caller (row stride rsb bytes), every lane's
+  // offset moved by the wave-uniform soff bytes.
+  __device__ __forceinline__ void issue_rs(T* lds, i32x4 rsrc, uint32_t rsb, uint32_t soff, int w) const {
+    const uint32_t la = lds_addr(lds);
+    const int l = lane_id();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int base = (u * NW + w) * 64;
+      if (base < TOT && (TOT % 64 == 0 || base + l < TOT))
+        dma16s(rsrc, row[u] * rsb + cof[u], soff,
+               __builtin_amdgcn_readfirstlane(la + (uint32_t)(L::row_off(base / L::NCH) * (int)sizeof(T))));
+    }
+  }
   __device__ __forceinline__ void issue(T* lds, const T* src, int64_t rs, int nvalid, int w) const {
     const uint32_t rsb = (uint32_t)(rs * (int64_t)sizeof(T));
     const i32x4 rsrc = buf_rsrc(src, (uint32_t)nvalid * rsb);
@@ -352,6 +375,55 @@ template <int R, int Cn, int NW, typename T, bool TR = false, bool PT = false> s
       if (base < TOT && base + l < TOT)
         dma16(rsrc, row[u] * rsb + cof[u],
               __builtin_amdgcn_readfirstlane(la + (uint32_t)(L::row_off(base / L::NCH) * (int)sizeof(T))));
+    }
+  }
+};
+
+// Lower-block form of a C x C matrix that is zero above its 16 x 16 diagonal blocks (T and
+// M of a chunk): row r keeps its first low_row_len(r) elements, at element low_row_off(r),
+// rows one after the other. At C = 64 that is 10 of the 16 blocks.
+__host__ __device__ constexpr int low_row_len(int r) { return 16 * (r / 16 + 1); }
+__host__ __device__ constexpr int low_row_off(int r) { return 128 * (r / 16) * (r / 16 + 1) + low_row_len(r) * (r % 16); }
+
+// Direct loads of a C x C tile in lower-block form into LDS in the dense layout
+// Swz<T, C, TR, PT> (same slots as TileDma<C, C, NW, T, TR, PT>). Lanes whose 16-byte piece
+// lies above the diagonal blocks load nothing: those pieces keep the zeros zero_upper()
+// wrote into the buffer once.
+template <int C, int NW, typename T, bool TR = false, bool PT = false> struct TileDmaLow {
+  using L = Swz<T, C, TR, PT>;
+  static constexpr int TOT = C * L::NCH, U = (TOT + NW * 64 - 1) / (NW * 64);
+  static constexpr uint32_t NONE = 0xFFFFFFFFu;
+  uint32_t off[U];  // byte offset of the lane's piece in the lower-block form, or NONE
+  __device__ __forceinline__ void init(int w) {
+    const int l = lane_id();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pch = (u * NW + w) * 64 + l;
+      const int r = pch / L::NCH, c = (pch % L::NCH) ^ L::s(r);
+      off[u] = (pch < TOT && c * L::CE < low_row_len(r)) ? (uint32_t)((low_row_off(r) + c * L::CE) * (int)sizeof(T)) : NONE;
+    }
+  }
+  __device__ __forceinline__ void issue(T* lds, const T* src, int w) const {
+    const i32x4 rsrc = buf_rsrc(src, (uint32_t)(low_row_off(C) * (int)sizeof(T)));
+    const uint32_t la = lds_addr(lds);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int base = (u * NW + w) * 64;
+      if (base < TOT && off[u] != NONE)
+        dma16(rsrc, off[u], __builtin_amdgcn_readfirstlane(la + (uint32_t)(L::row_off(base / L::NCH) * (int)sizeof(T))));
+    }
+  }
+  // Zeros into the pieces above the diagonal blocks (the ones issue() never writes).
+  __device__ __forceinline__ void zero_upper(T* lds, int w) const {
+    const int l = lane_id();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int base = (u * NW + w) * 64;
+      if (base + l < TOT && off[u] == NONE) {
+        typedef int32_t z4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<z4*>(reinterpret_cast<char*>(lds) + L::row_off(base / L::NCH) * (int)sizeof(T) + 16 * l) =
+            z4{0, 0, 0, 0};
+      }
     }
   }
 };
@@ -377,6 +449,15 @@ __device__ __forceinline__ void dma_wait_keep(int n) {
 // Workgroup barrier that orders LDS accesses only: it does not wait for the wave's
 // outstanding global memory operations, so loads into LDS stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N - 1, in order (i is a constant in f).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Wave index, uniform across the wave (kept in a scalar register).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

@@ -37,6 +37,18 @@ template <typename OT> __device__ __forceinline__ void store4(OT* dst, f32x4 x) 
     *reinterpret_cast<f32x4*>(dst) = x;
 }
 
+// Row i and first column j0 of piece q (EPC elements) of a C x C matrix in lower-block
+// form: the pieces of a row are consecutive and rows follow one another, so piece q starts
+// at element q EPC.
+template <int C, int EPC> __device__ __forceinline__ void low_piece(int q, int& i, int& j0) {
+  int t = 0;  // row tile
+#pragma unroll
+  for (int k = 1; k < C / 16; ++k) t += q * EPC >= low_row_off(16 * k) ? 1 : 0;
+  const int rl = low_row_len(16 * t) / EPC, qq = q - low_row_off(16 * t) / EPC;
+  i = 16 * t + qq / rl;
+  j0 = (qq % rl) * EPC;
+}
+
 // T := (I + L)^-1 for strictly lower triangular L (float32 LDS, row stride LC), lower
 // blocks only: the 16 x 16 blocks above the diagonal are zero and are never written (the
 // caller stores zeros for them). Diagonal blocks by forward substitution in one wave (a
@@ -226,15 +238,12 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
     }
     const float* sgh = sg[hh % GH];
     const float* sbh = sbeta[hh % GH];
-    if (rw) {  // wave w: row tile w of L and M. Above the diagonal M is zero and L is never
-               // read; below it no element mask is needed.
+    if (rw) {  // wave w: row tile w of L and M. Above the diagonal neither is stored (M and T
+               // go out in lower-block form, and L is never read there); below it no element
+               // mask is needed.
 #pragma unroll
       for (int j = 0; j < RT; ++j) {
-        if (j > w) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sM[(16 * w + g4 + e) * C + 16 * j + r16] = (OT)0.f;
-          continue;
-        }
+        if (j > w) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * w + g4 + e, jj = 16 * j + r16;
@@ -251,28 +260,30 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
       }
     }
     lds_barrier();
-    {
+    {  // M in lower-block form, 16-byte stores
       using V = Vec16<OT>;
-      typename V::type* dst = reinterpret_cast<typename V::type*>((OT*)p.sv_M + ch * C * C);
-      const typename V::type* src = reinterpret_cast<const typename V::type*>(sM);
-      for (int idx = threadIdx.x; idx < C * C / V::N; idx += NT) dst[idx] = src[idx];
+      OT* dst = (OT*)p.sv_M + ch * C * C;
+      for (int q = threadIdx.x; q < low_row_off(C) / V::N; q += NT) {
+        int i, j0;
+        low_piece<C, V::N>(q, i, j0);
+        *reinterpret_cast<typename V::type*>(dst + q * V::N) = *reinterpret_cast<const typename V::type*>(sM + i * C + j0);
+      }
     }
     lds_barrier();  // M is out: its staging tile becomes T
     invert_unit_lower<C, LCF, NW>(sL, sT);
-    {  // T with zeros above the diagonal blocks, 16-byte stores
+    {  // T in lower-block form, 16-byte stores
       OT* dst = (OT*)p.sv_T + ch * C * C;
       constexpr int E8 = 16 / (int)sizeof(OT);  // elements per 16-byte store
-      for (int idx = threadIdx.x; idx < C * C / E8; idx += NT) {
-        const int i = idx / (C / E8), j0 = (idx % (C / E8)) * E8;
-        const bool up = j0 / 16 > i / 16;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 a = up ? z : *reinterpret_cast<const f32x4*>(sT + i * LCF + j0);
+      for (int q = threadIdx.x; q < low_row_off(C) / E8; q += NT) {
+        int i, j0;
+        low_piece<C, E8>(q, i, j0);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sT + i * LCF + j0);
         if constexpr (E8 == 8) {
-          const f32x4 b = up ? z : *reinterpret_cast<const f32x4*>(sT + i * LCF + j0 + 4);
-          *reinterpret_cast<bf16x8*>(dst + i * C + j0) =
+          const f32x4 b = *reinterpret_cast<const f32x4*>(sT + i * LCF + j0 + 4);
+          *reinterpret_cast<bf16x8*>(dst + q * E8) =
               bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3], (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
         } else {
-          store4(dst + i * C + j0, a);
+          store4(dst + q * E8, a);
         }
       }
     }
@@ -371,7 +382,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
   const int v0 = w * WC;  // first state column of this wave
 
   TileDma<C, D, NW, OT, false, CF::PTD> dmD;  // K, Q, V
-  TileDma<C, C, NW, OT, false, CF::PTC> dmC;  // T, M
+  TileDmaLow<C, NW, OT, false, CF::PTC> dmC;  // T, M (lower-block form)
   TileDma<1, kSweepGateRows * C, NW, float> dmG;  // gate record rows 0-3
   dmD.init(w);
   dmC.init(w);
@@ -384,10 +395,15 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
     dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
     dmD.issue(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
-    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, C, C, w);
-    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, C, C, w);
+    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
+    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
     dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
   };
+#pragma unroll
+  for (int bf = 0; bf < 2; ++bf) {  // the blocks above the diagonal of T and M stay zero
+    dmC.zero_upper(sbuf[bf] + CF::O_T, w);
+    dmC.zero_upper(sbuf[bf] + CF::O_M, w);
+  }
 
   // The state: S[ct][dt] holds S[16 dt + g4 + e][v0 + 16 ct + r16].
   f32x4 S[CT][DT];

@@ -52,8 +52,8 @@ struct Prob {
   void* sv_S;    // [c][h][D][D]  state at the start of the chunk, transposed: S^T[v][d]
   void* sv_D;    // [c][h][D / BV][C][BV]  Delta in blocks of BV = grad_block<OT, D>() value
                  // columns, each block row-major (rows past the end of a chunk not written)
-  void* sv_T;    // [c][h][C][C]  T = (I + L)^-1, row-major
-  void* sv_M;    // [c][h][C][C]  M = Gamma o Q K^T (lower incl. diagonal), row-major
+  void* sv_T;    // [c][h][C][C]  T = (I + L)^-1, lower-block form (low_row_off) at the slot's start
+  void* sv_M;    // [c][h][C][C]  M = Gamma o Q K^T (lower incl. diagonal), lower-block form
   float* sv_gb;  // [c][h][kGateRows][C]  float32 gate record, rows below
   // q/k L2 normalisation (fused when sv_qn is set): prep writes the normalised rows and
   // 1 / sqrt(|row|^2 + 1e-6) of each q and k head row; every later kernel reads qu / ku.
