@@ -387,17 +387,24 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
   dmD.init(w);
   dmC.init(w);
   dmG.init(w);
-  auto issue = [&](int c, int buf) {
+  // The next chunk's loads, in parts: part 0 right after the step's first barrier, part 1
+  // after K S, part 2 after T X. With the saves every load goes in part 0 (their stores share
+  // the memory queue, and loads issued later in the step arrive late); without them K goes
+  // first, Q next and V, T, M and the gate record last (a shorter stall at each issue: the
+  // forward-only step measured 12% shorter than with every load in part 0).
+  auto issue = [&](int c, int buf, int part) {
     const int64_t t0 = sa + (int64_t)(c - c0) * C;
     const int len = (int)(sb - t0 < C ? sb - t0 : C);
     const size_t ch = ch_idx(p, c, h);
     OT* b = sbuf[buf];
-    dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
-    dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
-    dmD.issue(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
-    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
-    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
-    dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
+    if (part == 0) dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
+    if (part == (SAVE ? 0 : 1)) dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
+    if (part == (SAVE ? 0 : 2)) {
+      dmD.issue(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
+      dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
+      dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
+      dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
+    }
   };
 #pragma unroll
   for (int bf = 0; bf < 2; ++bf) {  // the blocks above the diagonal of T and M stay zero
@@ -419,12 +426,13 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     zero(S);
   }
 
-  if (c0 < c1) issue(c0, 0);
+  if (c0 < c1)
+    for (int part = 0; part < 3; ++part) issue(c0, 0, part);
   int buf = 0;
   for (int c = c0; c < c1; ++c, buf ^= 1) {
     dma_wait();
     lds_barrier();  // chunk c is in sbuf[buf]; every wave is done with sbuf[buf ^ 1] and stg
-    if (c + 1 < c1) issue(c + 1, buf ^ 1);
+    if (c + 1 < c1) issue(c + 1, buf ^ 1, 0);
     const int64_t t0 = sa + (int64_t)(c - c0) * C;
     const int len = (int)(sb - t0 < C ? sb - t0 : C);
     const size_t ch = ch_idx(p, c, h);
@@ -450,7 +458,6 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int s = 0; s < NSD; ++s) Sb[ct][s] = from_acc<OT, KSD>(S[ct], s, Ident{});
-    if constexpr (SAVE) save_rows<OT, D, CT, DT, NSD>((OT*)p.sv_S + ch * D * D, v0, S, Sb);  // S^T[v][d] at the chunk start
     // X = beta o (V - b o K S), then Delta = T X
     f32x4 X[CT][RT];
     {
@@ -469,6 +476,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
         }
       }
     }
+    if (!SAVE && c + 1 < c1) issue(c + 1, buf ^ 1, 1);
     f32x4 Dl[CT][RT];
     zero(Dl);
     wave_mm_cm<OT, C, RT, CT>(Dl, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sT, 16 * m, s); },
@@ -488,6 +496,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
 #pragma unroll
           for (int e = 0; e < 4; ++e) sDw[LD::at(16 * t + g4 + e, v0 + 16 * ct + r16)] = (OT)Dl[ct][t][e];
     }
+    if (!SAVE && c + 1 < c1) issue(c + 1, buf ^ 1, 2);
     {  // O = b o Q S + M Delta, staged as rows for the whole workgroup
       f32x4 O[RT][CT];
       zero(O);
@@ -509,6 +518,9 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
 #pragma unroll
           for (int e = 0; e < 4; ++e) stg[(16 * t + g4 + e) * CF::LSO + v0 + 16 * ct + r16] = (OT)(sc * O[t][ct][e]);
     }
+    // S^T[v][d] at the chunk start, stored late in the step (the stores then queue behind the
+    // next chunk's loads, not before them; 1% shorter step)
+    if constexpr (SAVE) save_rows<OT, D, CT, DT, NSD>((OT*)p.sv_S + ch * D * D, v0, S, Sb);
     lds_barrier();  // the chunk's output rows and Delta rows are staged
     {  // full output (and Delta) rows, 16-byte stores spread over every wave
       using V = Vec16<OT>;
