@@ -78,7 +78,8 @@ def kernel_model(name, C, D, Hk, Hv, T, n_chunks, N, es=2, S0=False, dST=True):
     saved chunk factors it reads or writes, and re-reads of q, k by the value heads that share
     a key head beyond the first). Units: ch (chunk, value head) and ck (chunk, key head)."""
     ch, ck, r = n_chunks * Hv, n_chunks * Hk, Hv // Hk
-    cd, cc, dd = C * D * es, C * C * es, D * D * es
+    cd, dd = C * D * es, D * D * es
+    cc = 128 * (C // 16) * (C // 16 + 1) * es  # T or M: the blocks on and below the diagonal
     qk, vv, gates = 2 * Hk * D * es, Hv * D * es, 2 * Hv * 4  # per token
     dqk, dgb = 2 * Hk * D * es, 2 * Hv * 4
     state = N * Hv * D * D * 4
