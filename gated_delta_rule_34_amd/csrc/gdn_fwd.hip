@@ -123,6 +123,22 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
   float* const sL = reinterpret_cast<float*>(smem);
   float* const sT = sL + C * LCF;
   OT* const sM = reinterpret_cast<OT*>(sT);
+  // Where M is staged. bf16 at C = 64: in the part of L's rows that L never uses (row tile t
+  // of L fills 16 (t + 1) of its LCF floats): M's row tiles 0 and 3 beside L's tile 0, tile 2
+  // beside tile 1, tile 1 beside tile 2. M then goes out while T is being formed, and T's
+  // store needs no barrier before the next head's L and M. Otherwise in T's tile, behind
+  // barriers.
+  constexpr bool MINL = sizeof(OT) == 2 && C == 64;
+  auto m_row = [&](int i) -> OT* {
+    if constexpr (MINL) {
+      const int t = i >> 4, r = i & 15;
+      const int lr = (t == 0 || t == 3) ? r : (t == 2 ? 16 + r : 32 + r);
+      const int lc = t == 0 ? 16 : (t == 3 ? 24 : (t == 2 ? 32 : 48));
+      return reinterpret_cast<OT*>(sL + lr * LCF + lc);
+    } else {
+      return sM + i * C;
+    }
+  };
 
   const int kh = blockIdx.x % p.Hk, c = blockIdx.x / p.Hk;
   const ChunkInfo ci = p.chunks[c];
@@ -255,21 +271,23 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
           }
           if (n < C) mv = i < n ? mv : 0.f;
           sL[i * LCF + jj] = lv;
-          sM[i * C + jj] = (OT)mv;
+          m_row(i)[jj] = (OT)mv;
         }
       }
     }
     lds_barrier();
-    {  // M in lower-block form, 16-byte stores
+    {  // M in lower-block form, 16-byte stores (beside L: by the waves that do not start T)
       using V = Vec16<OT>;
       OT* dst = (OT*)p.sv_M + ch * C * C;
-      for (int q = threadIdx.x; q < low_row_off(C) / V::N; q += NT) {
+      constexpr int Q0 = MINL ? 64 : 0;
+      for (int q = (int)threadIdx.x - Q0; q < low_row_off(C) / V::N; q += NT - Q0) {
+        if (q < 0) break;
         int i, j0;
         low_piece<C, V::N>(q, i, j0);
-        *reinterpret_cast<typename V::type*>(dst + q * V::N) = *reinterpret_cast<const typename V::type*>(sM + i * C + j0);
+        *reinterpret_cast<typename V::type*>(dst + q * V::N) = *reinterpret_cast<const typename V::type*>(m_row(i) + j0);
       }
     }
-    lds_barrier();  // M is out: its staging tile becomes T
+    if constexpr (!MINL) lds_barrier();  // M is out: its staging tile becomes T
     invert_unit_lower<C, LCF, NW>(sL, sT);
     {  // T in lower-block form, 16-byte stores
       OT* dst = (OT*)p.sv_T + ch * C * C;
@@ -287,7 +305,8 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
         }
       }
     }
-    lds_barrier();  // sL, sT, sM free for the next head
+    if constexpr (!MINL) lds_barrier();  // sL, sT, sM free for the next head (with MINL the next
+                                         // head's first barrier orders T's reads before T is rewritten)
   }
 }
 
