@@ -50,9 +50,12 @@ __global__ __launch_bounds__(DecCfg<D>::NT) void k_decode(DecArgs a) {
     sq[d] = to_f(qr[d]);
   }
   float* S = a.state + ((int64_t)slot * a.Hv + h) * D * D;
+  // The state is read once and written once per call: both through non-temporal accesses
+  // (streamed past the caches' normal allocation; 5% more bandwidth than plain ones, and
+  // either one alone is slower).
   f32x4 s[RPG];
 #pragma unroll
-  for (int i = 0; i < RPG; ++i) s[i] = *reinterpret_cast<const f32x4*>(S + (rg + RG * i) * D + c4);
+  for (int i = 0; i < RPG; ++i) s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (rg + RG * i) * D + c4));
   float gg = a.g[(int64_t)n * a.Hv + h], be = a.beta[(int64_t)n * a.Hv + h];
   if (a.a_log) {  // the gate chain from alpha and beta_raw
     gg = exp2f(chain_log2g(gg, a.a_log[h], a.dt_bias[h]));
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT) void k_decode(DecArgs a) {
 #pragma unroll
   for (int i = 0; i < RPG; ++i) {
     const int d = rg + RG * i;
-    *reinterpret_cast<f32x4*>(S + d * D + c4) = gg * s[i] + (sk[d] * rk) * delta;
+    __builtin_nontemporal_store(gg * s[i] + (sk[d] * rk) * delta, reinterpret_cast<f32x4*>(S + d * D + c4));
   }
 }
 
