@@ -124,9 +124,11 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     OT* b = sbuf[buf];
     dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
     dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
-    dmD.issue(b + CF::O_O, (const OT*)p.dO + t0 * p.dO_rs + h * D, p.dO_rs, len, w);
-    dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
-    dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
+    // dO, T and M are this workgroup's alone (non-temporal); K and Q are shared by the r value
+    // heads of the key head, which run on the same XCD
+    dmD.template issue<true>(b + CF::O_O, (const OT*)p.dO + t0 * p.dO_rs + h * D, p.dO_rs, len, w);
+    dmC.template issue<true>(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
+    dmC.template issue<true>(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
     dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
   };
 #pragma unroll
@@ -470,20 +472,20 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     const int hh = j / NBH, blk = j % NBH;
     OT* b = sB(j % CF::NBUF);
     if (part == 0) {
-      dmS.issue_rs(b + CF::O_S0, rS, D * sizeof(OT), (uint32_t)j * SBB, w);
+      dmS.template issue_rs<true>(b + CF::O_S0, rS, D * sizeof(OT), (uint32_t)j * SBB, w);
       if (blk == 0) {
         const uint32_t go = (uint32_t)(hh * kGateRows * C * 4);
-        dmG.issue_rs(sgb[hh % 3], rG, 0, go, w);  // gamma, beta
-        if constexpr (CHAIN) dmGc.issue_rs(sdl[hh % 3], rG, 0, go + 4 * C * 4, w);
+        dmG.template issue_rs<true>(sgb[hh % 3], rG, 0, go, w);  // gamma, beta
+        if constexpr (CHAIN) dmGc.template issue_rs<true>(sdl[hh % 3], rG, 0, go + 4 * C * 4, w);
       }
     } else if (part == 1) {
-      dmS.issue_rs(b + CF::O_DS, rDS, D * sizeof(OT), (uint32_t)j * SBB, w);
+      dmS.template issue_rs<true>(b + CF::O_DS, rDS, D * sizeof(OT), (uint32_t)j * SBB, w);
     } else {
       const uint64_t a = aAL + (uint64_t)j * ABB;
       const i32x4 r = {__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a),
                        __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32)),
                        (int32_t)((uint32_t)n * BV * sizeof(OT)), 0x00020000};
-      dmAL.issue_rs(b + (lo ? CF::O_A : CF::O_DL), r, BV * sizeof(OT), 0, wh);
+      dmAL.template issue_rs<true>(b + (lo ? CF::O_A : CF::O_DL), r, BV * sizeof(OT), 0, wh);
     }
   };
   auto issue_job = [&](int j) {
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
   };
   auto issue_pair = [&](int q) {
     OT* b = sP(q % CF::NPBUF);
-    dmP.issue_rs(b + (lo ? CF::O_DO : CF::O_V), rP, prsb, (uint32_t)(q * PW * sizeof(OT)), wh);
+    dmP.template issue_rs<true>(b + (lo ? CF::O_DO : CF::O_V), rP, prsb, (uint32_t)(q * PW * sizeof(OT)), wh);
   };
   // This wave's load instructions of job j, of a pair, and of the step of job j.
   auto job_loads = [&](int j) {
@@ -505,8 +507,9 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     const int q = PB == 1 ? j + 2 : j / PB + 1;
     return job_loads(j + 2) + ((j % PB == 0 && q < npairs) ? pair_loads : 0);
   };
-  dmD.issue(sK, (const OT*)p.ku + (int64_t)ci.t0 * p.ku_rs + kh * D, p.ku_rs, n, w);
-  dmD.issue(sQ, (const OT*)p.qu + (int64_t)ci.t0 * p.qu_rs + kh * D, p.qu_rs, n, w);
+  // every load of the item is non-temporal (each byte is read once per item; 8% faster)
+  dmD.template issue<true>(sK, (const OT*)p.ku + (int64_t)ci.t0 * p.ku_rs + kh * D, p.ku_rs, n, w);
+  dmD.template issue<true>(sQ, (const OT*)p.qu + (int64_t)ci.t0 * p.qu_rs + kh * D, p.qu_rs, n, w);
   issue_job(0);
   issue_pair(0);
   if (1 < njobs) {

@@ -163,8 +163,9 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
   {
     TileDma<C, D, NW, OT> dm;
     dm.init(w);
-    dm.issue(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
-    dm.issue(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
+    // non-temporal: each workgroup reads its K and Q rows once (17% faster prep)
+    dm.template issue<true>(sK, (const OT*)p.k + (int64_t)ci.t0 * p.k_rs + kh * D, p.k_rs, n, w);
+    dm.template issue<true>(sQ, (const OT*)p.q + (int64_t)ci.t0 * p.q_rs + kh * D, p.q_rs, n, w);
   }
   auto gates = [&](int hb, float gx, float bx) {
     const int hh = hb + w;
@@ -419,9 +420,11 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     if (part == 0) dmD.issue(b + CF::O_K, (const OT*)p.ku + t0 * p.ku_rs + kh * D, p.ku_rs, len, w);
     if (part == (SAVE ? 0 : 1)) dmD.issue(b + CF::O_Q, (const OT*)p.qu + t0 * p.qu_rs + kh * D, p.qu_rs, len, w);
     if (part == (SAVE ? 0 : 2)) {
-      dmD.issue(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
-      dmC.issue(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
-      dmC.issue(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
+      // V, T and M are this workgroup's alone (non-temporal); K and Q are shared by the r
+      // value heads of the key head, which run on the same XCD
+      dmD.template issue<true>(b + CF::O_V, (const OT*)p.v + t0 * p.v_rs + h * D, p.v_rs, len, w);
+      dmC.template issue<true>(b + CF::O_T, (const OT*)p.sv_T + ch * C * C, w);
+      dmC.template issue<true>(b + CF::O_M, (const OT*)p.sv_M + ch * C * C, w);
       dmG.issue(sgb[buf], p.sv_gb + ch * kGateRows * C, kSweepGateRows * C, 1, w);
     }
   };
