@@ -926,7 +926,7 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
           for (int e = 0; e < V::N; ++e)
             val[e] = (TI)(rf * ((float)val[e] - (float)X[LD::at(i, cc + e)] * dt));
         }
-        *reinterpret_cast<typename V::type*>(dst) = val;
+        store_nt(reinterpret_cast<typename V::type*>(dst), val);  // non-temporal: slightly faster
       }
     }
     if (p.r <= GRM) {  // dbeta, dg: row i, heads h0 .. h0 + r - 1

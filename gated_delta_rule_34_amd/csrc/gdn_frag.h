@@ -461,6 +461,14 @@ __device__ __forceinline__ void dma_wait_keep(int n) {
 #undef GDN_VMCNT
 }
 
+// A 16-byte store with the non-temporal cache policy (for results no later step of the same
+// kernel reads back).
+template <typename V> __device__ __forceinline__ void store_nt(V* p, V x) {
+  static_assert(sizeof(V) == 16, "16-byte stores");
+  typedef int32_t i4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(__builtin_bit_cast(i4, x), reinterpret_cast<i4*>(p));
+}
+
 // Workgroup barrier that orders LDS accesses only: it does not wait for the wave's
 // outstanding global memory operations, so loads into LDS stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

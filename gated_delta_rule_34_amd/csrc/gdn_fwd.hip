@@ -277,7 +277,8 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
       }
     }
     lds_barrier();
-    {  // M in lower-block form, 16-byte stores (beside L: by the waves that do not start T)
+    {  // M in lower-block form, 16-byte non-temporal stores (T's as well: 2% faster prep), beside
+       // L: by the waves that do not start T
       using V = Vec16<OT>;
       OT* dst = (OT*)p.sv_M + ch * C * C;
       constexpr int Q0 = MINL ? 64 : 0;
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
         if (q < 0) break;
         int i, j0;
         low_piece<C, V::N>(q, i, j0);
-        *reinterpret_cast<typename V::type*>(dst + q * V::N) = *reinterpret_cast<const typename V::type*>(m_row(i) + j0);
+        store_nt(reinterpret_cast<typename V::type*>(dst + q * V::N), *reinterpret_cast<const typename V::type*>(m_row(i) + j0));
       }
     }
     if constexpr (!MINL) lds_barrier();  // M is out: its staging tile becomes T
@@ -299,8 +300,8 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
         const f32x4 a = *reinterpret_cast<const f32x4*>(sT + i * LCF + j0);
         if constexpr (E8 == 8) {
           const f32x4 b = *reinterpret_cast<const f32x4*>(sT + i * LCF + j0 + 4);
-          *reinterpret_cast<bf16x8*>(dst + q * E8) =
-              bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3], (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+          store_nt(reinterpret_cast<bf16x8*>(dst + q * E8),
+                   bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3], (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]});
         } else {
           store4(dst + q * E8, a);
         }
