@@ -33,6 +33,19 @@ __device__ __forceinline__ float wave_scan_incl(float x) {  // sum of lanes 0..l
   x += dpp<0x143, 0xC>(x);  // row_bcast:31 -> rows 2 and 3 add the total of rows 0 and 1
   return x;
 }
+// wave_scan_incl on ints
+template <int CTRL, int ROWS = 0xF> __device__ __forceinline__ int dppi(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_scan_incl_int(int x) {
+  x += dppi<0x111>(x);
+  x += dppi<0x112>(x);
+  x += dppi<0x114>(x);
+  x += dppi<0x118>(x);
+  x += dppi<0x142, 0xA>(x);
+  x += dppi<0x143, 0xC>(x);
+  return x;
+}
 __device__ __forceinline__ float lane_value(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
@@ -80,14 +93,48 @@ __host__ __device__ constexpr int xcd_grid(int G, int r) { return (G + 7) / 8 * 
 // Sequences ranked for the sweeps' order up to this count; beyond it the order is the identity.
 constexpr int kOrderMax = 1024;
 
-// One workgroup: chunk table, per-sequence first-chunk offsets and the sweep order. The
-// sweeps give one workgroup to each (sequence, value head) and walk its chunks serially;
-// when there are more of them than CUs, the longest sequences must start first (the dispatcher
-// takes workgroups in index order), so seq_order lists the sequences by decreasing chunk count
-// (ties by index: a permutation).
-template <int C>
-__global__ __launch_bounds__(NTHREADS) void k_table(Prob p) {
-  __shared__ int cnt[kOrderMax];
+// Global chunk c as the chunk table lays it out (sequences one after the other, chunk by
+// chunk, empty ones taking none), found without the table: the per-sequence chunk counts
+// are scanned 64 sequences at a time by one wave (every lane of the wave calls it and gets
+// the same result). A slot past the last chunk gives seq = -1.
+template <int C> __device__ __forceinline__ ChunkInfo find_chunk(const Prob& p, int c) {
+  if (!p.cu) {
+    const int64_t cps = ((int64_t)p.T + C - 1) / C;  // chunks per sequence
+    const int64_t n = cps > 0 ? c / cps : p.N;
+    if (n >= p.N) return ChunkInfo{-1, 0, 0, 0};
+    const int64_t loc = c - n * cps, t = n * p.T + loc * C, rest = p.T - loc * C;
+    return ChunkInfo{(int)n, (int)t, (int)(rest < C ? rest : C), 0};
+  }
+  const int l = lane_id();
+  int64_t base = 0;  // chunks of the sequences before this group of 64
+  for (int n0 = 0; n0 < p.N; n0 += 64) {
+    const int n = n0 + l;
+    int64_t a = 0, b = 0;
+    if (n < p.N) seq_bounds(p, n, a, b);
+    const int cnt = (int)((b - a + C - 1) / C);
+    const int incl = wave_scan_incl_int(cnt);
+    const int64_t first = base + incl - cnt;  // the sequence's first chunk
+    const bool hit = n < p.N && cnt > 0 && c >= first && c < first + cnt;  // at most one lane
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int src = __builtin_ctzll(m);
+      const int64_t t = a + (c - first) * C;  // valid in lane src
+      const int64_t rest = b - t;
+      const int t32 = __builtin_amdgcn_readlane((int)t, src);
+      const int len = __builtin_amdgcn_readlane((int)(rest < C ? rest : C), src);
+      return ChunkInfo{n0 + src, t32, len, 0};
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return ChunkInfo{-1, 0, 0, 0};
+}
+
+// The chunk table's per-sequence first-chunk offsets and the sweep order, by one workgroup of
+// NT threads (cnt: scratch for kOrderMax ints). The sweeps give one workgroup to each
+// (sequence, value head) and walk its chunks serially; when there are more of them than CUs,
+// the longest sequences must start first (the dispatcher takes workgroups in index order), so
+// seq_order lists the sequences by decreasing chunk count (ties by index: a permutation).
+template <int C, int NT> __device__ __forceinline__ void seq_table(const Prob& p, int* cnt) {
   if (threadIdx.x == 0) {
     int64_t off = 0;
     for (int n = 0; n < p.N; ++n) {
@@ -99,29 +146,31 @@ __global__ __launch_bounds__(NTHREADS) void k_table(Prob p) {
     p.seq_chunk[p.N] = (int)(off < p.nc_max ? off : p.nc_max);
   }
   __syncthreads();
-  for (int n = threadIdx.x; n < p.N; n += NTHREADS) {
-    int64_t a, b;
-    seq_bounds(p, n, a, b);
-    const int c0 = p.seq_chunk[n], c1 = p.seq_chunk[n + 1];
-    for (int c = c0; c < c1; ++c) {
-      const int64_t t = a + (int64_t)(c - c0) * C;
-      const int64_t len = b - t < C ? b - t : C;
-      p.chunks[c] = ChunkInfo{n, (int)t, (int)len, 0};
-    }
-  }
-  for (int c = p.seq_chunk[p.N] + threadIdx.x; c < p.nc_max; c += NTHREADS) p.chunks[c] = ChunkInfo{-1, 0, 0, 0};
   if (p.N > kOrderMax) {
-    for (int n = threadIdx.x; n < p.N; n += NTHREADS) p.seq_order[n] = n;
+    for (int n = threadIdx.x; n < p.N; n += NT) p.seq_order[n] = n;
     return;
   }
-  for (int n = threadIdx.x; n < p.N; n += NTHREADS) cnt[n] = p.seq_chunk[n + 1] - p.seq_chunk[n];
+  for (int n = threadIdx.x; n < p.N; n += NT) cnt[n] = p.seq_chunk[n + 1] - p.seq_chunk[n];
   __syncthreads();
-  for (int n = threadIdx.x; n < p.N; n += NTHREADS) {
+  for (int n = threadIdx.x; n < p.N; n += NT) {
     const int cn = cnt[n];
     int rank = 0;
     for (int m = 0; m < p.N; ++m) rank += (cnt[m] > cn) || (cnt[m] == cn && m < n);
     p.seq_order[rank] = n;
   }
+  __syncthreads();
+}
+
+// One workgroup: the whole chunk table (the forward's prep kernel writes it itself; this
+// kernel serves a problem with sequences but no chunk slots, where prep does not run).
+template <int C>
+__global__ __launch_bounds__(NTHREADS) void k_table(Prob p) {
+  __shared__ int cnt[kOrderMax];
+  for (int c = wave_id(); c < p.nc_max; c += NTHREADS / 64) {
+    const ChunkInfo ci = find_chunk<C>(p, c);
+    if (lane_id() == 0) p.chunks[c] = ci;
+  }
+  seq_table<C, NTHREADS>(p, cnt);
 }
 
 }  // namespace gdn

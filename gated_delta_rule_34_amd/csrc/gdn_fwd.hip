@@ -115,7 +115,9 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
   constexpr int KQ_BYTES = 2 * C * D * (int)sizeof(OT);
   constexpr int INV_BYTES = 2 * C * LCF * 4;
   static_assert(C * C * (int)sizeof(OT) <= C * LCF * 4, "M staging fits in T");
-  __shared__ __align__(16) char smem[KQ_BYTES > INV_BYTES ? KQ_BYTES : INV_BYTES];
+  constexpr int SM_BYTES = KQ_BYTES > INV_BYTES ? KQ_BYTES : INV_BYTES;
+  // (workgroup 0 first uses it as the chunk table's scratch)
+  __shared__ __align__(16) char smem[SM_BYTES > kOrderMax * 4 ? SM_BYTES : kOrderMax * 4];
   constexpr int GH = NW;  // gate records formed per pass: one wave per value head
   __shared__ float sg[GH][C], sbeta[GH][C];
   OT* const sK = reinterpret_cast<OT*>(smem);
@@ -141,7 +143,12 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
   };
 
   const int kh = blockIdx.x % p.Hk, c = blockIdx.x / p.Hk;
-  const ChunkInfo ci = p.chunks[c];
+  // The chunk table: every workgroup finds its own chunk; those of key head 0 write the
+  // table's entries, and workgroup 0 the per-sequence offsets and the sweep order (in the
+  // LDS before its K and Q arrive), so no launch of its own precedes prep.
+  if (blockIdx.x == 0) seq_table<C, kPrepThreads>(p, reinterpret_cast<int*>(smem));
+  const ChunkInfo ci = find_chunk<C>(p, c);
+  if (kh == 0 && threadIdx.x == 0) p.chunks[c] = ci;
   if (ci.seq < 0) return;
   const int n = ci.len, w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, r16 = l & 15;
   // Gate records of value heads hb .. hb + GH - 1, one per wave (lane = row): gamma (log2
@@ -596,8 +603,10 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
 template <typename TI, int C, int D>
 static hipError_t fwd_seq(const Prob& p, hipStream_t s) {
   using CF = SwCfg<TI, C, D>;
-  traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
-  if (p.nc_max > 0) traced("k_prep", s, [&] { k_prep<TI, C, D><<<p.nc_max * p.Hk, kPrepThreads, 0, s>>>(p); });
+  if (p.nc_max > 0)
+    traced("k_prep", s, [&] { k_prep<TI, C, D><<<p.nc_max * p.Hk, kPrepThreads, 0, s>>>(p); });
+  else  // no chunk slots: the table still gives the sweeps their (empty) chunk ranges
+    traced("k_table", s, [&] { k_table<C><<<1, NTHREADS, 0, s>>>(p); });
   if (p.N > 0) {
     if (p.sv_S)
       traced("k_fwd_sweep", s,
