@@ -57,6 +57,10 @@ SMALL = [
     ("f32_D128_C16", [40], 1, 1, 128, "f32", 16, False),
     ("bf16_varlen_zero_len", [0, 65, 1, 128, 0, 63], 2, 4, 64, "bf16", 64, True),
     ("f32_varlen_ragged_C16", [17, 0, 33, 5], 2, 2, 32, "f32", 16, True),
+    # more value heads per key head than the kernels keep per-head state for at once (gate
+    # records are formed four heads at a time, dg and dbeta staged for up to four heads)
+    ("bf16_r8_D64", [150], 1, 8, 64, "bf16", 64, False),
+    ("f32_r5_D32_C16", [70], 1, 5, 32, "f32", 16, False),
 ]
 
 
