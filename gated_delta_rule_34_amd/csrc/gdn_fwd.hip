@@ -305,10 +305,13 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
     }
     if constexpr (!MINL) lds_barrier();  // M is out: its staging tile becomes T
     invert_unit_lower<C, LCF, NW>(sL, sT);
-    {  // T in lower-block form, 16-byte stores
+    {  // T in lower-block form, 16-byte stores. With M beside L, by waves 0 and 1 only: the
+       // others start the next head's L and M at once (waves 2 and 3 hold its most tiles).
       OT* dst = (OT*)p.sv_T + ch * C * C;
       constexpr int E8 = 16 / (int)sizeof(OT);  // elements per 16-byte store
-      for (int q = threadIdx.x; q < low_row_off(C) / E8; q += NT) {
+      constexpr int TW = MINL ? 2 : NW;           // waves that store T
+      for (int q = threadIdx.x; q < low_row_off(C) / E8; q += TW * 64) {
+        if (threadIdx.x >= TW * 64) break;
         int i, j0;
         low_piece<C, E8>(q, i, j0);
         const f32x4 a = *reinterpret_cast<const f32x4*>(sT + i * LCF + j0);
