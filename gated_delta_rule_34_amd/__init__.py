@@ -163,6 +163,8 @@ def _rs(t, width):
     contiguous heads; the ABI requires exactly that inner layout."""
     if t is None:
         return 0
+    if t.dim() in (2, 3) and t.shape[0] == 0:
+        return width  # no row to address: any layout (torch gives empty views arbitrary strides)
     if t.dim() == 3:
         if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
             raise ValueError("inner head layout must be contiguous")

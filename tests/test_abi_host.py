@@ -262,3 +262,16 @@ def test_fwd_noalloc_rejects_on_the_host(G):
     assert st(small, beta=None) == G.GDN_EINVAL
     assert st(small, q=FakeTensor(0x10002, 256, 2048, 10240)) == G.GDN_EALIGN
     assert st(prob(G, Hv=47)) == G.GDN_EINVAL
+
+
+def test_row_stride_of_empty_views(G):
+    """A view with no rows has no layout to check (torch gives empty views arbitrary strides):
+    the binding passes the row width as its stride; views with rows still need contiguous
+    heads."""
+    import torch
+
+    empty = torch.empty(4, 3, 2, 32)[:0, 1]  # zero rows, strides of the parent
+    assert G._rs(empty, 64) == 64
+    assert G._rs(torch.empty(0, 64), 64) == 64
+    with pytest.raises(ValueError):
+        G._rs(torch.empty(3, 2, 32).transpose(1, 2), 64)

@@ -13,6 +13,7 @@
 import numpy as np
 import pytest
 
+import oracle
 from synth import make_case
 from gdn_gpu import GRAD_NAMES, normwise, run_gpu
 
@@ -179,3 +180,19 @@ def test_fused_prologue_determinism_bitwise():
         outs.append(run_gpu(case, d=d, p=p))
     for name in ALL:
         assert np.array_equal(outs[0][name], outs[1][name]), name
+
+
+@pytest.mark.parametrize("lens,dtype", [([0], "f32"), ([0, 0, 0], "bf16")])
+def test_all_sequences_empty(lens, dtype):
+    """A batch whose sequences are all empty: no chunk slot at all ([0]: the chunk table then
+    comes from its own one-workgroup kernel) or only unused slots ([0, 0, 0]: prep runs and
+    writes an empty table). Nothing is read or written per token; the final state is S0 and
+    the state gradient is dS_T, bit for bit, as the oracle has them."""
+    case = make_case(7, lens, 2, 4, 32, dtype=dtype, chunk=64, gate="clamp09", with_S0=True, with_dST=True,
+                     packed=(dtype == "bf16"), varlen=True, name="all_empty")
+    gpu = run_gpu(case)
+    ref = oracle.run_case(case, backward=True)
+    assert gpu["o"].shape[0] == 0 and gpu["dq"].shape[0] == 0
+    assert np.array_equal(gpu["S_T"], ref["S_T"])
+    assert np.array_equal(gpu["dS0"], ref["dS0"])
+    assert np.array_equal(ref["S_T"], np.asarray(case.S0, dtype=np.float64))
