@@ -23,6 +23,9 @@ CASES = {
     "f32_D32_C16": dict(lens=[100], Hk=1, Hv=2, D=32, dtype="f32", chunk=16, varlen=False),
     "f32_D16_C64_two_seqs": dict(lens=[40, 40], Hk=2, Hv=4, D=16, dtype="f32", chunk=64, varlen=False),
 }
+SMALL = list(CASES)
+# the training shape (4 x 4096 tokens, 16 key heads, 48 value heads, D = 128, bf16 packed rows)
+CASES["bf16_training_shape"] = dict(lens=[4096] * 4, Hk=16, Hv=48, D=128, dtype="bf16", chunk=64, varlen=False)
 
 
 def _raw(case, seed):
@@ -68,13 +71,19 @@ def _run(name, chain):
     compare(raw, gpu, ref, OUT_NAMES + GRAD_NAMES)
 
 
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name", SMALL)
 def test_qk_l2norm_fused(name):
     _run(name, chain=False)
 
 
 def test_qk_l2norm_and_gate_chain_fused():
     _run("bf16_ragged_r3_D128", chain=True)
+
+
+def test_qk_l2norm_and_gate_chain_fused_training_shape():
+    """Both fused prologues at the shape the bench times them, every element of every output
+    and gradient against the oracle."""
+    _run("bf16_training_shape", chain=True)
 
 
 def test_qk_l2norm_decode():
