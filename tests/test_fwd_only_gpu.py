@@ -76,13 +76,15 @@ def test_fwd_only_with_fused_norm_and_gate_chain():
     assert np.array_equal(o_s, o_f) and np.array_equal(st_s, st_f)
 
 
-def test_fwd_only_config2_against_oracle():
-    """The strided v_repeat 3 workload (one sequence of 2048 tokens, Hk 16, Hv 48, D 128,
-    packed bf16 rows), every head, against the float64 oracle at the bf16 bar."""
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_fwd_only_full_shape_against_oracle(cfg):
+    """The strided v_repeat 3 workload (one sequence of 2048 tokens) and the training shape (4 x
+    4096 tokens), Hk 16, Hv 48, D 128, packed bf16 rows, every head, against the float64 oracle
+    at the bf16 bar."""
     import torch
     import gated_delta_rule_34_amd as G
 
-    case = config_case(2)
+    case = config_case(cfg)
     print(f"[fwd-only] {case.name}", flush=True)
     d = to_device(case)
     p = problem(case, d)
