@@ -27,6 +27,11 @@
 namespace gdn {
 
 constexpr int kPrepWaves = 4;
+// The lower 16 x 16 tiles (i, j) of L and M that prep's wave w forms at C = 64, dealt 3, 3,
+// 2, 2 (by row tile, 1, 2, 3, 4 per wave: the wave with four held up the barrier behind it)
+constexpr int kLmN[4] = {3, 3, 2, 2};
+constexpr int kLmI[4][3] = {{0, 1, 1}, {2, 2, 2}, {3, 3, 3}, {3, 3, 3}};
+constexpr int kLmJ[4][3] = {{0, 0, 1}, {0, 1, 2}, {0, 1, 1}, {2, 3, 3}};
 constexpr int kPrepThreads = kPrepWaves * 64;
 
 // Four accumulator values as consecutive elements of type OT (8 or 16 bytes).
@@ -308,15 +313,37 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
     }
     lds_barrier();
   }
-  // K K^T and Q K^T: wave w < C / 16 owns row tile w and every column tile, formed
-  // transposed (K_j K_w^T and K_j Q_w^T; K K^T is symmetric): lane (g, r) then holds row
-  // 16 w + r at the four adjacent columns 16 j + 4 g .. 16 j + 4 g + 3, which go into L and
-  // M as one 16-byte and one 8-byte write.
+  // The tiles (i, j) of K K^T and Q K^T below the diagonal that L and M need, formed
+  // transposed (K_j K_i^T and K_j Q_i^T; K K^T is symmetric): lane (g, r) then holds row
+  // 16 i + r at the four adjacent columns 16 j + 4 g .. 16 j + 4 g + 3, which go into L and
+  // M as one 16-byte and one 8-byte write. At C = 64 wave w takes the tiles of kLmI/kLmJ
+  // (one code path per wave, so that every tile index is a constant); otherwise wave
+  // w < C / 16 takes row tile i = w.
   const bool rw = w < RT;
-  f32x4 KK[RT][1], QK[RT][1];
+  constexpr int NTW = RT == 4 ? 3 : RT;
+  f32x4 KK[NTW][1], QK[NTW][1];
   zero(KK);
   zero(QK);
-  if (rw) {
+  auto per_wave = [&](auto&& f) {
+    if (w == 0) f(std::integral_constant<int, 0>{});
+    else if (w == 1) f(std::integral_constant<int, 1>{});
+    else if (w == 2) f(std::integral_constant<int, 2>{});
+    else f(std::integral_constant<int, 3>{});
+  };
+  if constexpr (RT == 4) {
+    per_wave([&](auto wc) {
+      constexpr int W = decltype(wc)::value;
+      using M = Mf<OT, KSD>;
+#pragma unroll
+      for (int s = 0; s < D / KSD; ++s)
+        static_for<kLmN[W]>([&](auto tc) {
+          constexpr int t = decltype(tc)::value, ti = kLmI[W][t], tj = kLmJ[W][t];
+          const typename M::frag a = ld_n<OT, KSD, STD, LD>(sK, 16 * tj, s);
+          KK[t][0] = M::run(a, ld_n<OT, KSD, STD, LD>(sK, 16 * ti, s), KK[t][0]);
+          QK[t][0] = M::run(a, ld_n<OT, KSD, STD, LD>(sQ, 16 * ti, s), QK[t][0]);
+        });
+    });
+  } else if (rw) {
     auto fa = [&](int j, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * j, s); };
     wave_mm<OT, D, RT, 1>(KK, fa, [&](int, int s) { return ld_n<OT, KSD, STD, LD>(sK, 16 * w, s); });
     wave_mm<OT, D, RT, 1>(QK, fa, [&](int, int s) { return ld_n<OT, KSD, STD, LD>(sQ, 16 * w, s); });
@@ -340,31 +367,41 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4,
     }
     const float* sgh = sg[hh % GH];
     const float* sbh = sbeta[hh % GH];
-    if (rw) {  // wave w: row tile w of L and M. Above the diagonal neither is stored (M and T
-               // go out in lower-block form, and L is never read there); below it no element
-               // mask is needed.
-      const int i = 16 * w + r16;  // this lane's row
+    // Tile (ti, tj) of L and M from the wave's Gram tiles. Above the diagonal neither is
+    // stored (M and T go out in lower-block form, and L is never read there); below it no
+    // element mask is needed.
+    auto lm_tile = [&](int ti, int tj, const f32x4& kk, const f32x4& qk) {
+      const int i = 16 * ti + r16;  // this lane's row
       const float gi = sgh[i], bi = sbh[i];
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(sgh + 16 * tj + g4);
+      f32x4 lv4, mv4;
 #pragma unroll
-      for (int j = 0; j < RT; ++j) {
-        if (j > w) continue;
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(sgh + 16 * j + g4);
-        f32x4 lv4, mv4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {  // column 16 j + g4 + e
-          const float gd = __builtin_amdgcn_exp2f(gi - gj[e]);
-          float lv = bi * gd * KK[j][0][e], mv = gd * QK[j][0][e];
-          if (j == w) {
-            lv = r16 > g4 + e ? lv : 0.f;
-            mv = r16 >= g4 + e ? mv : 0.f;
-          }
-          if (n < C) mv = i < n ? mv : 0.f;
-          lv4[e] = lv;
-          mv4[e] = mv;
+      for (int e = 0; e < 4; ++e) {  // column 16 tj + g4 + e
+        const float gd = __builtin_amdgcn_exp2f(gi - gj[e]);
+        float lv = bi * gd * kk[e], mv = gd * qk[e];
+        if (ti == tj) {
+          lv = r16 > g4 + e ? lv : 0.f;
+          mv = r16 >= g4 + e ? mv : 0.f;
         }
-        *reinterpret_cast<f32x4*>(sL + i * LCF + 16 * j + g4) = lv4;
-        store4(m_row(i) + 16 * j + g4, mv4);
+        if (n < C) mv = i < n ? mv : 0.f;
+        lv4[e] = lv;
+        mv4[e] = mv;
       }
+      *reinterpret_cast<f32x4*>(sL + i * LCF + 16 * tj + g4) = lv4;
+      store4(m_row(i) + 16 * tj + g4, mv4);
+    };
+    if constexpr (RT == 4) {
+      per_wave([&](auto wc) {
+        constexpr int W = decltype(wc)::value;
+        static_for<kLmN[W]>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          lm_tile(kLmI[W][t], kLmJ[W][t], KK[t][0], QK[t][0]);
+        });
+      });
+    } else if (rw) {
+#pragma unroll
+      for (int j = 0; j < RT; ++j)
+        if (j <= w) lm_tile(w, j, KK[j][0], QK[j][0]);
     }
     lds_barrier();
     {  // M in lower-block form, 16-byte non-temporal stores (T's as well: 2% faster prep), beside
