@@ -897,18 +897,31 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
     using V = Vec16<TI>;
     constexpr int VPR = D / V::N;
     const bool l2 = p.sv_qn != nullptr;
-    if (l2) {  // x_hat . dx_hat per row (wave w takes rows w, w + NW, ... of dq, then of dk)
-      for (int rr = w; rr < 2 * C; rr += NW) {
-        const int i = rr % C;
-        const OT* X = rr < C ? sQ : sK;  // the normalised rows
+    if (l2) {  // x_hat . dx_hat per row of dq, then of dk: PPR lanes per row, one 16-byte
+               // piece each, RPW rows per wave and pass
+      // The rows' norm factors, one load per row (thread rr: row rr % C of q, then of k), in
+      // flight during the dots and written after them (loaded one at a time by one lane, the
+      // loads' latencies had added a quarter to the kernel's time)
+      float rfv = 0.f;
+      const int fr = threadIdx.x;
+      if (fr < 2 * C && fr % C < n) rfv = p.sv_r[((int64_t)(ci.t0 + fr % C) * p.Hk + kh) * 2 + (fr < C ? 0 : 1)];
+      constexpr int PPR = D / V::N, RPW = 64 / PPR;
+      const int sub = lane % PPR;
+      for (int r0 = w * RPW; r0 < 2 * C; r0 += NW * RPW) {
+        const int rr = r0 + lane / PPR;
+        const bool okr = rr < 2 * C;  // (every lane takes part in the group sum)
+        const int rc = okr ? rr : 0, i = rc % C;
+        const OT* X = rc < C ? sQ : sK;  // the normalised rows
+        const typename V::type xv = *reinterpret_cast<const typename V::type*>(X + LD::at(i, sub * V::N));
+        const typename V::type dv = *reinterpret_cast<const typename V::type*>(st + LS::at(rc, sub * V::N));
         float x = 0.f;
-        for (int c = lane; c < D; c += 64) x += (float)X[LD::at(i, c)] * (float)st[LS::at(rr, c)];
-        x = wave_sum(x);
-        if (lane == 0) {
-          sdot[rr] = x;
-          srf[rr] = i < n ? p.sv_r[((int64_t)(ci.t0 + i) * p.Hk + kh) * 2 + (rr < C ? 0 : 1)] : 0.f;
-        }
+#pragma unroll
+        for (int e = 0; e < V::N; ++e) x += (float)xv[e] * (float)dv[e];
+#pragma unroll
+        for (int o = 1; o < PPR; o <<= 1) x += __shfl_xor(x, o);
+        if (okr && sub == 0) sdot[rr] = x;
       }
+      if (fr < 2 * C) srf[fr] = rfv;
       lds_barrier();
     }
     TI* dq = (TI*)p.dq + (int64_t)ci.t0 * p.dq_rs + kh * D;
@@ -921,10 +934,10 @@ __global__ __launch_bounds__(kThreadsG) void k_bwd_grad(Prob p) {
         typename V::type val = *reinterpret_cast<const typename V::type*>(st + LS::at(r, cc));
         if (l2) {  // dx = r (dx_hat - x_hat (x_hat . dx_hat)), the gradient of the raw row
           const OT* X = r < C ? sQ : sK;
+          const typename V::type xv = *reinterpret_cast<const typename V::type*>(X + LD::at(i, cc));
           const float dt = sdot[r], rf = srf[r];
 #pragma unroll
-          for (int e = 0; e < V::N; ++e)
-            val[e] = (TI)(rf * ((float)val[e] - (float)X[LD::at(i, cc + e)] * dt));
+          for (int e = 0; e < V::N; ++e) val[e] = (TI)(rf * ((float)val[e] - (float)xv[e] * dt));
         }
         store_nt(reinterpret_cast<typename V::type*>(dst), val);  // non-temporal: slightly faster
       }
