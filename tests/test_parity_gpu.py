@@ -61,6 +61,9 @@ SMALL = [
     # records are formed four heads at a time, dg and dbeta staged for up to four heads)
     ("bf16_r8_D64", [150], 1, 8, 64, "bf16", 64, False),
     ("f32_r5_D32_C16", [70], 1, 5, 32, "f32", 16, False),
+    # bf16 chunk 64 at the small head sizes (one and two MFMA steps over d in prep's Gram)
+    ("bf16_D16_C64_ragged", [90, 90], 2, 2, 16, "bf16", 64, False),
+    ("bf16_D32_C64", [128, 128], 1, 3, 32, "bf16", 64, False),
 ]
 
 
