@@ -49,24 +49,6 @@ template <typename TI, int C, int D> struct BwCfg {
   static constexpr int O_K = 0, O_Q = C * D, O_O = 2 * C * D, O_T = 3 * C * D, O_M = O_T + C * C, BUF = O_M + C * C;
 };
 
-template <typename OT, int K, int MT, int NT, class FA, class FB>
-__device__ __forceinline__ void wave_mm_cm(f32x4 (&acc)[NT][MT], FA&& fa, FB&& fb) {
-  constexpr int KS = ks_of<OT, K>();
-  using M = Mf<OT, KS>;
-#pragma unroll
-  for (int s = 0; s < K / KS; ++s) {
-    typename M::frag b[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) b[n] = fb(n, s);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const typename M::frag a = fa(m, s);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n][m] = M::run(a, b[n], acc[n][m]);
-    }
-  }
-}
-
 // Saved rows X^T[v][j] of a wave's accumulator tiles, in RowOrd<OT, LEN> order (the same
 // writer as the forward's: fragment order stores each lane's 16-byte fragment at once).
 template <typename OT, int LEN, int CT, int NT, int NS>
@@ -197,7 +179,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
       zero(MdO);
       wave_mm<OT, D, RT, CT>(KdS, [&](int m, int s) { return ld_n<OT, KSD, ACC, LD>(sK, 16 * m, s); },
                              [&](int j, int s) { return dSb[j][s]; });
-      wave_mm<OT, C, RT, CT>(MdO, [&](int m, int s) { return ld_t<OT, KSC, STD, LC>(sM, 16 * m, s); },
+      wave_mm<OT, C, RT, CT, TRI_UP>(MdO, [&](int m, int s) { return ld_t<OT, KSC, STD, LC>(sM, 16 * m, s); },
                              [&](int j, int s) { return ld_t<OT, KSC, STD, LD>(sO, v0 + 16 * j, s); });
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -215,7 +197,7 @@ __global__ __launch_bounds__((BwCfg<TI, C, D>::NW * 64)) void k_bwd_sweep(Prob p
     // of BV value columns) and dV = diag(beta) A from them
     f32x4 Z[CT][RT];
     zero(Z);
-    wave_mm_cm<OT, C, RT, CT>(Z, [&](int m, int s) { return ld_t<OT, KSC, ACC, LC>(sT, 16 * m, s); },
+    wave_mm_cm<OT, C, RT, CT, TRI_UP>(Z, [&](int m, int s) { return ld_t<OT, KSC, ACC, LC>(sT, 16 * m, s); },
                               [&](int j, int s) { return dDb[j][s]; });
 #pragma unroll
     for (int t = 0; t < RT; ++t)

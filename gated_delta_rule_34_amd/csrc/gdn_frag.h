@@ -251,10 +251,23 @@ template <> struct Vec16<__bf16> {
   typedef __bf16 type __attribute__((ext_vector_type(8)));
 };
 
+// A product whose A operand is triangular by 16 x 16 tiles (row tile m = rows 16 m ..
+// 16 m + 15): TRI_LOW, zero where k >= 16 (m + 1); TRI_UP, zero where k < 16 m. A
+// contraction step whose indices all lie there adds nothing and is skipped, with its
+// fragment reads. The indices of step s lie in [lo, lo + w): KS s and KS wide for KS = 32 or
+// 16 in either order; one tile of 16 for KS = 4 (STD takes four of them, ACC spreads its
+// four over the tile).
+enum { TRI_NONE = 0, TRI_LOW = 1, TRI_UP = 2 };
+template <int TRI, int KS> __device__ __forceinline__ constexpr bool tri_skip(int s, int m) {
+  const int lo = KS == 4 ? 16 * (s >> 2) : KS * s, wd = KS == 4 ? 16 : KS;
+  return TRI == TRI_LOW ? lo >= 16 * (m + 1) : (TRI == TRI_UP ? lo + wd <= 16 * m : false);
+}
+
 // acc[m][n] += sum_k A(m, k) B(k, n) over a contraction of length K for a wave's
 // MT x NT block of 16 x 16 tiles. fa(m, s) and fb(n, s) return the step-s fragments;
 // the NT B fragments of a step are loaded once and reused across the MT A fragments.
-template <typename OT, int K, int MT, int NT, class FA, class FB>
+// With TRI, m must be the absolute row tile of A.
+template <typename OT, int K, int MT, int NT, int TRI = TRI_NONE, class FA, class FB>
 __device__ __forceinline__ void wave_mm(f32x4 (&acc)[MT][NT], FA&& fa, FB&& fb) {
   constexpr int KS = ks_of<OT, K>();
   using M = Mf<OT, KS>;
@@ -266,9 +279,31 @@ __device__ __forceinline__ void wave_mm(f32x4 (&acc)[MT][NT], FA&& fa, FB&& fb) 
     for (int n = 0; n < NT; ++n) b[n] = fb(n, s);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
+      if (tri_skip<TRI, KS>(s, m)) continue;
       const typename M::frag a = fa(m, s);
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[m][n] = M::run(a, b[n], acc[m][n]);
+    }
+  }
+}
+
+// acc[n][m] += sum_k A(m, k) B(k, n): wave_mm with the accumulator tiles stored
+// column-tile major (the layout from_acc reads when the result feeds a later product).
+template <typename OT, int K, int MT, int NT, int TRI = TRI_NONE, class FA, class FB>
+__device__ __forceinline__ void wave_mm_cm(f32x4 (&acc)[NT][MT], FA&& fa, FB&& fb) {
+  constexpr int KS = ks_of<OT, K>();
+  using M = Mf<OT, KS>;
+#pragma unroll
+  for (int s = 0; s < K / KS; ++s) {
+    typename M::frag b[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) b[n] = fb(n, s);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (tri_skip<TRI, KS>(s, m)) continue;
+      const typename M::frag a = fa(m, s);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n][m] = M::run(a, b[n], acc[n][m]);
     }
   }
 }

@@ -465,26 +465,6 @@ template <typename TI, int C, int D> struct SwCfg {
   static constexpr int O_K = 0, O_Q = SD, O_V = 2 * SD, O_T = 3 * SD, O_M = O_T + SC, BUF = O_M + SC;
 };
 
-// acc[n][m] += sum_k A(m, k) B(k, n): wave_mm with the accumulator tiles stored
-// column-tile major (the layout from_acc reads when the result feeds a later product).
-template <typename OT, int K, int MT, int NT, class FA, class FB>
-__device__ __forceinline__ void wave_mm_cm(f32x4 (&acc)[NT][MT], FA&& fa, FB&& fb) {
-  constexpr int KS = ks_of<OT, K>();
-  using M = Mf<OT, KS>;
-#pragma unroll
-  for (int s = 0; s < K / KS; ++s) {
-    typename M::frag b[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) b[n] = fb(n, s);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const typename M::frag a = fa(m, s);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n][m] = M::run(a, b[n], acc[n][m]);
-    }
-  }
-}
-
 // One saved row segment per lane and column tile: the transposed tile X^T[v][j] of a
 // wave's accumulators Xc[ct][t] (rows j = 16 t + g4 + e of column v = v0 + 16 ct + r16),
 // into rows of LEN elements in RowOrd<OT, LEN> order. In fragment order every lane stores
@@ -637,7 +617,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
     if (!SAVE && c + 1 < c1) issue(c + 1, buf ^ 1, 1);
     f32x4 Dl[CT][RT];
     zero(Dl);
-    wave_mm_cm<OT, C, RT, CT>(Dl, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sT, 16 * m, s); },
+    wave_mm_cm<OT, C, RT, CT, TRI_LOW>(Dl, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sT, 16 * m, s); },
                               [&](int j, int s) { return from_acc<OT, KSC>(X[j], s, Ident{}); });
     FragC Db[CT][NSC];  // Delta's fragments: B operand of M Delta
 #pragma unroll
@@ -666,7 +646,7 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
           for (int e = 0; e < 4; ++e) O[t][ct][e] *= bx[t][e];
-      wave_mm<OT, C, RT, CT>(O, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sM, 16 * m, s); },
+      wave_mm<OT, C, RT, CT, TRI_LOW>(O, [&](int m, int s) { return ld_n<OT, KSC, ACC, LC>(sM, 16 * m, s); },
                              [&](int j, int s) { return Db[j][s]; });
       const float sc = p.scale;
 #pragma unroll
