@@ -671,8 +671,13 @@ __global__ __launch_bounds__((SwCfg<TI, C, D>::NW * 64)) void k_fwd_sweep(Prob p
       for (int idx = threadIdx.x; idx < C * VPR; idx += NW * 64) {
         const int i = idx / VPR, q = idx % VPR;
         if (i < len) {
-          *reinterpret_cast<typename V::type*>(o + (int64_t)i * p.o_rs + q * CE) =
-              *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
+          // (non-temporal without the saves: 0.3% shorter forward-only call; with them the
+          // temporal store measured faster)
+          const typename V::type ov = *reinterpret_cast<const typename V::type*>(stg + i * CF::LSO + q * CE);
+          if constexpr (SAVE)
+            *reinterpret_cast<typename V::type*>(o + (int64_t)i * p.o_rs + q * CE) = ov;
+          else
+            store_nt(reinterpret_cast<typename V::type*>(o + (int64_t)i * p.o_rs + q * CE), ov);
           if constexpr (SAVE)
             *reinterpret_cast<typename V::type*>(dl + (q * CE / BV) * C * BV + i * BV + (q * CE) % BV) =
                 *reinterpret_cast<const typename V::type*>(sD + LD::at(i, q * CE));
