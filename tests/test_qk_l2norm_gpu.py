@@ -22,6 +22,10 @@ CASES = {
     "bf16_ragged_r3_D128": dict(lens=[130, 67], Hk=2, Hv=6, D=128, dtype="bf16", chunk=64, varlen=True),
     "f32_D32_C16": dict(lens=[100], Hk=1, Hv=2, D=32, dtype="f32", chunk=16, varlen=False),
     "f32_D16_C64_two_seqs": dict(lens=[40, 40], Hk=2, Hv=4, D=16, dtype="f32", chunk=64, varlen=False),
+    # bf16 at the small head sizes: two and eight lanes per row in the row dots of the norm's
+    # backward
+    "bf16_D16_C64": dict(lens=[90], Hk=2, Hv=4, D=16, dtype="bf16", chunk=64, varlen=False),
+    "bf16_D64_C16_varlen": dict(lens=[33, 0, 70], Hk=1, Hv=3, D=64, dtype="bf16", chunk=16, varlen=True),
 }
 SMALL = list(CASES)
 # the training shape (4 x 4096 tokens, 16 key heads, 48 value heads, D = 128, bf16 packed rows)
