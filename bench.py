@@ -498,7 +498,7 @@ def main():
     print(f"[bench] eager: {eager_t['median_ms']:.4f} ms/step (median of {args.steps})", file=sys.stderr, flush=True)
     if args.profile_step:
         return
-    # The headline: the same step (the same five kernels on the same buffers) captured once in
+    # The headline: the same step (the same four kernels on the same buffers) captured once in
     # a HIP graph and replayed, so the launch gaps between the kernels shrink.
     step_graph = capture(torch, wl["step"])
     main_t = timer.run(step_graph, args.steps, 3)
