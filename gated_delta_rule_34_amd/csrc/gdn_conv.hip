@@ -130,7 +130,10 @@ template <typename TI> __device__ __forceinline__ F8 cvt(const Raw8<TI>& x) {
   return r;
 }
 
-__device__ __forceinline__ float sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }
+// The reciprocal is the hardware's v_rcp_f32 (about 1 ulp; 0 for an infinite argument,
+// NaN for NaN): an IEEE division here took about ten VALU instructions per element
+// (measured: the backward 3% faster, the forward faster in every run).
+__device__ __forceinline__ float sigmoid(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 // Grid (rows / kConvRun, channel groups / kConvThreads).
 template <typename TI, int K>
