@@ -170,6 +170,10 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_fwd(ConvArgs a) {
 #pragma unroll
   for (int u = 0; u < kConvPF; ++u)
     if (t0 + u < t1) buf[u] = ldraw(x + (t0 + u) * a.x_rs);
+  // Unrolled by the window length, so that the window's K - 1 rows rename registers
+  // instead of moving down one slot per row (forward 1-5% faster; the same unrolling of the
+  // backward was 2% slower)
+#pragma unroll (K > 1 ? K - 1 : 1)
   for (int64_t base = t0; base < t1; base += kConvPF) {
 #pragma unroll
     for (int u = 0; u < kConvPF; ++u) {
